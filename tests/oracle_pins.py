@@ -1,0 +1,296 @@
+"""Pins that tie the fp64 oracle to mathematics rather than to itself.
+
+Each ``pin_*`` function takes the oracle module (or a copy with a planted
+mistake) and raises AssertionError when it disagrees with an independent
+statement of what RoPE computes:
+
+* brute-force position counting over tiny packed batches;
+* 50-digit mpmath values of the frequencies, cos and sin at the exact angle;
+* the D = 2 closed form (the unit vectors rotate to (cos p, sin p) and
+  (-sin p, cos p));
+* RoFormer's block-diagonal rotary matrix, which pairs *adjacent* elements,
+  written out entry by entry in mpmath and conjugated by the permutation that
+  maps the rotate_half layout (i, i + D/2) onto adjacent pairs;
+* complex multiplication (x_i + j x_{i+D/2}) * exp(j * direction * angle);
+* invariants: identity at position 0, per-pair norm, backward after forward,
+  dependence of q.k on the position difference only, packed = unpacked.
+
+The pages print no formula and no worked numbers, so every value here comes
+from mathematics; see the module docstring of the oracle for the reading.
+"""
+
+from __future__ import annotations
+
+import math
+
+import mpmath
+import numpy as np
+
+mpmath.mp.dps = 50
+
+F64_EPS = 2.0 ** -52
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------
+# positions
+# ---------------------------------------------------------------------------
+
+POSITION_CASES = [
+    ([0, 7, 40, 104, 256], 256),
+    ([0, 1, 2, 3], 5),  # length-1 sequences, two trailing tokens outside
+    ([0, 0, 0, 4, 4, 9], 9),  # empty segments
+    ([3, 5, 5, 8], 12),  # tokens before cu[0] and after cu[nseq]
+    ([0], 4),  # nseq = 0: nothing is inside
+    ([0, 16], 16),
+]
+
+
+def brute_positions(cu, T):
+    """Walk the tokens one by one, counting up inside each sequence."""
+    pos = [-1] * T
+    for s in range(len(cu) - 1):
+        n = 0
+        for t in range(cu[s], cu[s + 1]):
+            pos[t] = n
+            n += 1
+    return pos
+
+
+def pin_positions(O):
+    for cu, T in POSITION_CASES:
+        got = O.segment_positions(np.array(cu, dtype=np.int32), T)
+        assert list(got) == brute_positions(cu, T), (cu, list(got))
+
+
+# ---------------------------------------------------------------------------
+# frequencies, cos, sin
+# ---------------------------------------------------------------------------
+
+def pin_inv_freq(O):
+    for theta in (1e4, 5e5, 1e6):
+        for D in (2, 8, 64, 80, 128):
+            got = O.inv_freq(theta, D)
+            assert got.shape == (D // 2,)
+            for i in range(D // 2):
+                exact = mpmath.power(mpmath.mpf(theta), -mpmath.mpf(2 * i) / D)
+                err = abs(mpmath.mpf(float(got[i])) - exact) / exact
+                # one rounding of pow, plus the float64 rounding of the exponent 2i/D
+                # (exact when D is a power of two) magnified by ln(theta)
+                tol = F64_EPS + math.log(theta) * (2 * i / D) * 2.0 ** -53
+                assert err <= tol, (theta, D, i, float(err))
+
+
+def _exact_angle(p, theta, D, i):
+    return mpmath.mpf(p) * mpmath.power(mpmath.mpf(theta), -mpmath.mpf(2 * i) / D)
+
+
+def pin_cos_sin(O):
+    """cos/sin at 50 digits; the only slack is the float64 rounding of the angle.
+
+    |angle_f64 - angle| <= 1.5 ulp(angle) (one rounding in inv_freq scaled by
+    p, one in the product), and cos/sin are 1-Lipschitz, plus one ulp of 1
+    for the libm evaluation.
+    """
+    cases = [(0, 1e6, 64), (1, 1e6, 64), (151, 1e6, 64), (16383, 1e6, 64),
+             (65535, 1e6, 128), (524287, 5e5, 128), (524287, 1e6, 128), (300000, 5e5, 128)]
+    for p, theta, D in cases:
+        for direction in (1, -1):
+            c, s = O.cos_sin(np.array([p]), theta, D, direction)
+            for i in range(0, D // 2, 3):
+                a = _exact_angle(p, theta, D, i)
+                tol = 1.5 * math.ulp(float(a)) + 2 * F64_EPS if p else 0.0
+                ec = abs(mpmath.mpf(float(c[0, i])) - mpmath.cos(a))
+                es = abs(mpmath.mpf(float(s[0, i])) - direction * mpmath.sin(a))
+                assert ec <= tol and es <= tol, (p, theta, D, i, direction, float(ec), float(es))
+
+
+# ---------------------------------------------------------------------------
+# the rotation itself
+# ---------------------------------------------------------------------------
+
+def pin_closed_form_d2(O):
+    """D = 2: inv_freq = [1], so (1,0) -> (cos p, sin p) and (0,1) -> (-sin p, cos p)."""
+    ps = [0, 1, 2, 7, 100, 12345, 524287]
+    T = len(ps)
+    for theta in (1e4, 5e5):
+        for direction in (1, -1):
+            e1 = np.zeros((T, 1, 2))
+            e1[:, 0, 0] = 1.0
+            e2 = np.zeros((T, 1, 2))
+            e2[:, 0, 1] = 1.0
+            pos = np.array(ps)
+            y1 = O.rotate(e1, pos, theta, direction)
+            y2 = O.rotate(e2, pos, theta, direction)
+            for r, p in enumerate(ps):
+                c = mpmath.cos(p)
+                s = direction * mpmath.sin(p)
+                tol = 2 * F64_EPS
+                assert abs(y1[r, 0, 0] - c) <= tol and abs(y1[r, 0, 1] - s) <= tol, (p, direction, y1[r])
+                assert abs(y2[r, 0, 0] + s) <= tol and abs(y2[r, 0, 1] - c) <= tol, (p, direction, y2[r])
+
+
+def _roformer_matrix(p, theta, D, direction):
+    """RoFormer's rotary matrix for position p: 2x2 rotations on adjacent pairs
+    (2i, 2i+1) by angle p * theta^(-2i/D), written out entry by entry."""
+    R = [[mpmath.mpf(0)] * D for _ in range(D)]
+    for i in range(D // 2):
+        a = direction * _exact_angle(p, theta, D, i)
+        c, s = mpmath.cos(a), mpmath.sin(a)
+        R[2 * i][2 * i] = c
+        R[2 * i][2 * i + 1] = -s
+        R[2 * i + 1][2 * i] = s
+        R[2 * i + 1][2 * i + 1] = c
+    return R
+
+
+def pin_roformer_matrix(O):
+    """rotate_half RoPE == P^T R_adjacent P, where P interleaves (i, i+D/2) -> (2i, 2i+1)."""
+    rng = _rng(11)
+    for D, theta in ((8, 1e4), (12, 1e6), (16, 5e5)):
+        ps = [0, 1, 5, 333, 90001]
+        H = 2
+        x = rng.standard_normal((len(ps), H, D))
+        for direction in (1, -1):
+            y = O.rotate(x, np.array(ps), theta, direction)
+            for r, p in enumerate(ps):
+                R = _roformer_matrix(p, theta, D, direction)
+                for h in range(H):
+                    z = [None] * D  # interleaved copy of the head
+                    for i in range(D // 2):
+                        z[2 * i] = mpmath.mpf(float(x[r, h, i]))
+                        z[2 * i + 1] = mpmath.mpf(float(x[r, h, i + D // 2]))
+                    w = [mpmath.fsum(R[a][b] * z[b] for b in range(D)) for a in range(D)]
+                    norm = math.sqrt(sum(float(v) ** 2 for v in z))
+                    tol = (8 * F64_EPS + 2 * math.ulp(float(_exact_angle(p, theta, D, 0)))) * max(norm, 1.0)
+                    for i in range(D // 2):
+                        assert abs(y[r, h, i] - w[2 * i]) <= tol, (D, p, h, i, direction)
+                        assert abs(y[r, h, i + D // 2] - w[2 * i + 1]) <= tol, (D, p, h, i, direction)
+
+
+def pin_complex_form(O):
+    """(x_i + j x_{i+D/2}) * exp(j * direction * angle) in complex128."""
+    rng = _rng(12)
+    T, H, D, theta = 300, 3, 64, 1e6
+    x = rng.standard_normal((T, H, D))
+    pos = rng.integers(0, 524288, size=T)
+    for direction in (1, -1):
+        y = O.rotate(x, pos, theta, direction)
+        i = np.arange(D // 2)
+        # angles from mpmath-exact frequencies, rounded once to float64
+        f = np.array([float(mpmath.power(mpmath.mpf(theta), -mpmath.mpf(2 * int(k)) / D)) for k in i])
+        ang = pos[:, None].astype(np.float64) * f[None, :]
+        rot = np.exp(1j * direction * ang)[:, None, :]
+        z = (x[:, :, : D // 2] + 1j * x[:, :, D // 2:]) * rot
+        scale = np.abs(x[:, :, : D // 2] + 1j * x[:, :, D // 2:])
+        tol = 8 * F64_EPS * scale + 4 * F64_EPS * 524288 * scale  # angle rounding at positions up to 2^19
+        assert np.all(np.abs(y[:, :, : D // 2] - z.real) <= tol)
+        assert np.all(np.abs(y[:, :, D // 2:] - z.imag) <= tol)
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+
+def pin_identity_at_zero(O):
+    rng = _rng(13)
+    cu = np.array([0, 7, 40, 104, 256], dtype=np.int32)
+    x = rng.standard_normal((256, 4, 64)).astype(np.float32).astype(np.float64)
+    for direction in (1, -1):
+        y = O.rope(x, cu, 1e6, direction)
+        starts = cu[:-1]
+        assert np.array_equal(y[starts], x[starts])
+
+
+def pin_untouched_outside(O):
+    rng = _rng(14)
+    cu = np.array([3, 5, 5, 8], dtype=np.int32)
+    x = rng.standard_normal((12, 2, 8))
+    y = O.rope(x, cu, 1e4, 1)
+    assert np.array_equal(y[:3], x[:3]) and np.array_equal(y[8:], x[8:])
+    assert not np.array_equal(y[4], x[4])
+
+
+def pin_pair_norm(O):
+    rng = _rng(15)
+    x = rng.standard_normal((500, 3, 128))
+    pos = rng.integers(0, 524288, size=500)
+    for direction in (1, -1):
+        y = O.rotate(x, pos, 5e5, direction)
+        n_in = x[:, :, :64] ** 2 + x[:, :, 64:] ** 2
+        n_out = y[:, :, :64] ** 2 + y[:, :, 64:] ** 2
+        assert np.all(np.abs(n_out - n_in) <= 1e-14 * np.maximum(n_in, 1e-300))
+
+
+def pin_bwd_after_fwd(O):
+    rng = _rng(16)
+    cu = np.array([0, 100, 101, 1000, 4096], dtype=np.int32)
+    x = rng.standard_normal((4096, 2, 64))
+    y = O.rope(O.rope(x, cu, 1e6, 1), cu, 1e6, -1)
+    assert np.max(np.abs(y - x)) <= 1e-14 * max(1.0, np.max(np.abs(x)))
+    # and the other order
+    y = O.rope(O.rope(x, cu, 1e6, -1), cu, 1e6, 1)
+    assert np.max(np.abs(y - x)) <= 1e-14 * max(1.0, np.max(np.abs(x)))
+
+
+def pin_relative_position(O):
+    """<f(q, m), f(k, n)> depends on m - n only."""
+    rng = _rng(17)
+    D, theta = 64, 1e4
+    q = rng.standard_normal((1, 1, D))
+    k = rng.standard_normal((1, 1, D))
+    scale = np.linalg.norm(q) * np.linalg.norm(k)
+    for m, n in ((5, 2), (100, 100), (3, 900), (1000, 10)):
+        ref = np.sum(O.rotate(q, np.array([m]), theta, 1) * O.rotate(k, np.array([n]), theta, 1))
+        for delta in (1, 17, 999, 9000):
+            got = np.sum(O.rotate(q, np.array([m + delta]), theta, 1) * O.rotate(k, np.array([n + delta]), theta, 1))
+            tol = 1e-12 * scale * max(1.0, (m + n + 2 * delta) / 1e4)
+            assert abs(got - ref) <= tol, (m, n, delta, got, ref)
+    # and it does depend on the difference
+    a = np.sum(O.rotate(q, np.array([10]), theta, 1) * O.rotate(k, np.array([0]), theta, 1))
+    b = np.sum(O.rotate(q, np.array([0]), theta, 1) * O.rotate(k, np.array([10]), theta, 1))
+    assert abs(a - b) > 1e-6 * scale
+
+
+def pin_packed_equals_unpacked(O):
+    rng = _rng(18)
+    lengths = [7, 1, 33, 0, 64, 151]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    T = int(cu[-1])
+    x = rng.standard_normal((T, 3, 64))
+    for direction in (1, -1):
+        packed = O.rope(x, cu, 1e6, direction)
+        for s, L in enumerate(lengths):
+            a, b = int(cu[s]), int(cu[s + 1])
+            alone = O.rope(x[a:b], np.array([0, L], dtype=np.int32), 1e6, direction)
+            assert np.array_equal(packed[a:b], alone)
+
+
+def pin_qk_share_angles(O):
+    """q and k rotated by one call see the same positions and angles."""
+    rng = _rng(19)
+    cu = np.array([0, 10, 30], dtype=np.int32)
+    q = rng.standard_normal((30, 4, 16))
+    k = q[:, :2, :].copy()
+    yq, yk = O.rope_qk(q, k, cu, 1e4, 1)
+    assert np.array_equal(yq[:, :2, :], yk)
+
+
+ALL_PINS = [
+    pin_positions,
+    pin_inv_freq,
+    pin_cos_sin,
+    pin_closed_form_d2,
+    pin_roformer_matrix,
+    pin_complex_form,
+    pin_identity_at_zero,
+    pin_untouched_outside,
+    pin_pair_norm,
+    pin_bwd_after_fwd,
+    pin_relative_position,
+    pin_packed_equals_unpacked,
+    pin_qk_share_angles,
+]
