@@ -1,0 +1,328 @@
+"""Benchmark: fused QK-RoPE forward + backward over a packed variable-length batch.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+
+One step = the whole hot path over one packed batch: rope_qk_fwd on (q, k)
+then rope_qk_bwd on (dq, dk), each one kernel launch through the C ABI.
+Inputs are resident in HBM before timing starts; consecutive steps rotate
+over enough independent batches (>= 1 GiB in total) that every launch reads
+cold HBM rather than the 256 MB Infinity Cache.
+
+Prints ONE JSON line on stdout (progress goes to stderr) with:
+  value        tokens/s of the whole step (fwd + bwd), wall clock over K steps
+  roofline     the rotation kernel's achieved HBM bandwidth: algorithmic bytes
+               per launch (read + write of q and k) / mean launch duration,
+               from HIP events recorded around every launch on its stream,
+               against MI355X's 8 TB/s; `traffic` is the measured HBM bytes per
+               launch from committed rocprofv3 counters when they were taken
+               on the current kernel source, else null
+  cpu_baseline the fp64 numpy oracle on a bounded sample of the same
+               workload, on the host cores
+  parity       a fresh batch checked against the oracle in the same run
+Workloads: 1 tiny fp32, 2 Qwen2.5-0.5B-shaped (default), 3 Qwen3-8B-shaped,
+4 Qwen3-32B-shaped, 5 Llama-3.1-8B-shaped 524,288-token context.
+"""
+
+from __future__ import annotations
+
+import argparse
+import concurrent.futures as cf
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused QK-RoPE fwd+bwd tokens/s and achieved HBM GB/s (% of MI355X peak)"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "packed_varlen_rotary_amd", "csrc", "rope_qk.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rope_qk_kernel_traffic.md")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload_name: str):
+    """HBM bytes per launch from the committed counter summary, if it matches this kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    if not m or m.group(1) != kernel_sha():
+        return None
+    for line in text.splitlines():
+        mm = re.match(r"\|\s*(.+?)\s*\|\s*hbm_bytes_per_launch\s*\|\s*(\d+)\s*\|", line)
+        if mm and mm.group(1) == workload_name:
+            return int(mm.group(2))
+    return None
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle as it stands, on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(w, budget_s: float = 12.0, chunk: int = 1024):
+    import numpy as np
+
+    import oracle
+
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    pos_all = oracle.segment_positions(w.cu_seqlens, w.T)
+    rng = np.random.default_rng(0)
+    starts = list(range(0, w.T, chunk))
+
+    def one_chunk(s):
+        e = min(s + chunk, w.T)
+        n = e - s
+        pos = pos_all[s:e]
+        for H in (w.Hq, w.Hkv):
+            for direction in (1, -1):
+                x = rng.standard_normal((n, H, w.D))
+                if w.dtype == "bf16":
+                    x = oracle.bf16_rne(x)
+                y = oracle.rotate(x, pos, w.theta, direction)
+                if w.dtype == "bf16":
+                    oracle.bf16_bits(oracle.bf16_rne(y))
+                else:
+                    y.astype(np.float32)
+        return n
+
+    t0 = time.perf_counter()
+    tokens = 0
+    with cf.ThreadPoolExecutor(max_workers=cores) as ex:
+        i = 0
+        while time.perf_counter() - t0 < budget_s and i < 100000:
+            batch = [starts[(i + j) % len(starts)] for j in range(cores)]
+            tokens += sum(ex.map(one_chunk, batch))
+            i += cores
+    dt = time.perf_counter() - t0
+    return {
+        "value": tokens / dt,
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{tokens} tokens of the workload ({chunk}-token chunks, q and k, fwd and bwd, "
+                  f"positions+fp64 rotation+bf16 rounding) in {dt:.1f} s on {cores} threads",
+    }
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+
+def run_gpu(args):
+    import numpy as np
+    import torch
+
+    import packed_varlen_rotary_amd as P
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    w = W.make_workload(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cu = torch.as_tensor(w.cu_seqlens, device=dev)
+    set_bytes = w.bytes_per_pass  # q, k, dq, dk of one batch: (Hq+Hkv)*D*s*T bytes each pair
+    nsets = max(1, min(64, -(-(1 << 30) // set_bytes)))
+    log(f"[bench] {w.name}: {nsets} resident batches of {set_bytes / 2**20:.1f} MiB")
+    sets = [W.make_tensors(w, ("q", "k", "dq", "dk"), device=dev, salt=s) for s in range(nsets)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        b = sets[i % nsets]
+        if ev is not None:
+            ev[0].record(stream)
+        P.rope_qk_fwd(b["q"], b["k"], cu, w.theta)
+        if ev is not None:
+            ev[1].record(stream)
+            ev[2].record(stream)
+        P.rope_qk_bwd(b["dq"], b["dk"], cu, w.theta)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, HIP events around every launch on the launch stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    bwd_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    region_ms = t_start.elapsed_time(t_end)
+
+    # parity of a fresh batch in the same run
+    parity = check_parity(w, cu, dev)
+
+    launch_ms = float(np.mean(np.concatenate([fwd_ms, bwd_ms])))
+    ms_per_step = wall * 1e3 / args.steps
+    gbs = w.bytes_per_pass / (launch_ms * 1e-3) / 1e9
+    traffic = measured_traffic(w.name)
+    return w, {
+        "ms_per_step": ms_per_step,
+        "tokens_per_s": w.T / (ms_per_step * 1e-3),
+        "event_region_ms_per_step": region_ms / args.steps,
+        "launch_ms": launch_ms,
+        "fwd_ms_median": float(np.median(fwd_ms)),
+        "bwd_ms_median": float(np.median(bwd_ms)),
+        "fwd_gbs": w.bytes_per_pass / (float(np.median(fwd_ms)) * 1e-3) / 1e9,
+        "bwd_gbs": w.bytes_per_pass / (float(np.median(bwd_ms)) * 1e-3) / 1e9,
+        "gbs": gbs,
+        "traffic": traffic,
+        "parity": parity,
+        "resident_batches": nsets,
+        "device": torch.cuda.get_device_name(dev),
+    }
+
+
+def check_parity(w, cu, dev):
+    import numpy as np
+    import torch
+
+    import oracle
+    import packed_varlen_rotary_amd as P
+    import workloads as W
+
+    t = W.make_tensors(w, ("q", "k", "dq", "dk"), device=dev, salt=999)
+    if w.T * (w.Hq + w.Hkv) * w.D <= 40_000_000:
+        idx = np.arange(w.T)
+    else:
+        rng = np.random.default_rng(1)
+        idx = np.unique(np.concatenate([[0, w.T - 1], w.cu_seqlens[:-1], rng.integers(0, w.T, 512)]))
+    idx_d = torch.as_tensor(idx, device=dev)
+    x = {n: t[n].index_select(0, idx_d).float().cpu().numpy().astype(np.float64) for n in t}
+    P.rope_qk_fwd(t["q"], t["k"], cu, w.theta)
+    P.rope_qk_bwd(t["dq"], t["dk"], cu, w.theta)
+    torch.cuda.synchronize()
+    pos = oracle.segment_positions(w.cu_seqlens, w.T)[idx]
+    worst = {"max_ulp": 0, "max_abs": 0.0, "exact_fraction": 1.0, "tokens_checked": int(len(idx))}
+    exact_n, total_n = 0, 0
+    for n, d in (("q", 1), ("k", 1), ("dq", -1), ("dk", -1)):
+        ref = oracle.rotate(x[n], pos, w.theta, d)
+        out = t[n].index_select(0, idx_d)
+        if w.dtype == "fp32":
+            worst["max_abs"] = max(worst["max_abs"], float(np.abs(out.cpu().numpy().astype(np.float64) - ref).max()))
+        else:
+            want = oracle.bf16_bits(oracle.bf16_rne(ref))
+            got = out.cpu().view(torch.int16).numpy().view(np.uint16)
+            dist = oracle.ulp_distance_bf16(got, want)
+            worst["max_ulp"] = max(worst["max_ulp"], int(dist.max()))
+            exact_n += int((dist == 0).sum())
+            total_n += dist.size
+    if total_n:
+        worst["exact_fraction"] = exact_n / total_n
+    worst["ok"] = bool(worst["max_ulp"] <= 1 and worst["max_abs"] <= 1e-5)
+    return worst
+
+
+def run_copy_calibration(args):
+    """A plain device-to-device copy of a known size, for scaling HBM counters."""
+    import torch
+
+    n = args.copy_bytes // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copied {n * 2} bytes x {args.steps}")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain copy of --copy-bytes (for HBM counter scaling)")
+    ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the rotation is per token and needs no "
+              "exchange, so more GPUs would each run this same one-GPU workload on their own shard.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        run_copy_calibration(args)
+        return
+
+    w, r = run_gpu(args)
+    log(f"[bench] gpu done: {r['ms_per_step']:.4f} ms/step, launch {r['launch_ms'] * 1e3:.2f} us, "
+        f"{r['gbs']:.0f} GB/s, parity {r['parity']}")
+    cpu = None
+    if args.workload and not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        log(f"[bench] cpu oracle: {cpu['value']:.0f} tokens/s on {cpu['cores']} threads")
+
+    achieved = r["gbs"]
+    line = {
+        "metric": METRIC,
+        "value": r["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "theta": w.theta,
+            "io_dtype": w.dtype, "nseq": w.nseq,
+            "step": "rope_qk_fwd(q,k) + rope_qk_bwd(dq,dk), in place",
+            "resident_batches": r["resident_batches"],
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": r["traffic"],
+        },
+        "cpu_baseline": cpu,
+        "kernel": {
+            "name": "rope_qk_kernel",
+            "algorithmic_bytes_per_launch": w.bytes_per_pass,
+            "mean_launch_us": r["launch_ms"] * 1e3,
+            "fwd_median_us": r["fwd_ms_median"] * 1e3,
+            "bwd_median_us": r["bwd_ms_median"] * 1e3,
+            "fwd_gbs": r["fwd_gbs"],
+            "bwd_gbs": r["bwd_gbs"],
+            "event_region_ms_per_step": r["event_region_ms_per_step"],
+        },
+        "parity": r["parity"],
+        "device": r["device"],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

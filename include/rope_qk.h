@@ -1,0 +1,134 @@
+/*
+ * rope_qk.h -- fused, in-place rotary position embedding of the query and key
+ * tensors of a packed variable-length batch, forward and backward, on AMD
+ * Instinct MI355X (gfx950).  C ABI: plain pointers and sizes, no framework
+ * types.
+ *
+ * What the operation is
+ * ---------------------
+ * "Unsloth prétend accélérer 5 fois l'entraînement des LLM avec de nouveaux
+ * noyaux Triton et un auto-packing" (seventnews.com), paragraph on the fused
+ * QK RoPE kernel: one kernel rotates both q and k (instead of one kernel each),
+ * accepts variable-length input, and works fully in place without clones or
+ * contiguous transposes.  The same article's auto-packing paragraph: short
+ * sequences are concatenated along one token axis and only their length
+ * metadata is kept, so that nothing leaks between samples.  "Chronicals: A
+ * High-Performance Framework for LLM Fine-Tuning with 3.51x Speedup over
+ * Unsloth", abstract, optimisation (1): QK-RoPE is one of the fused kernels
+ * that remove memory traffic.  The article's LONG_INDEXING paragraph: 500K-token
+ * contexts overflowed 32-bit indexing; here every offset is 64-bit in the one
+ * build.
+ *
+ * The pages print no formula.  The reading implemented is the standard rotary
+ * embedding (RoFormer, Su et al. 2021) in the rotate_half layout: for every
+ * token t inside a packed sequence, every head of q and of k, and i < D/2,
+ *
+ *   inv_freq[i] = theta^(-2i/D)            (float64, computed on the host)
+ *   a           = pos(t) * inv_freq[i]      (float64)
+ *   x1 = x[t,h,i], x2 = x[t,h,i+D/2]
+ *   forward:   x1' = x1 cos a - x2 sin a,   x2' = x2 cos a + x1 sin a
+ *   backward:  the same with sin a -> -sin a (the transpose), applied to dq, dk
+ *
+ * pos(t) = t - cu_seqlens[s], where s is the last index with cu_seqlens[s] <= t,
+ * so positions restart at 0 at every sequence boundary.  Tokens t < cu_seqlens[0]
+ * and t >= cu_seqlens[nseq] are not read and not written.  The rotation is
+ * evaluated in float64 and rounded once to the storage type (round to nearest,
+ * ties to even): bf16 results are the correctly rounded bf16 of the float64
+ * rotation, fp32 results the correctly rounded fp32.
+ *
+ * Memory, ownership, ordering
+ * ---------------------------
+ * All tensor pointers are device memory owned by the caller; the library keeps
+ * no state and allocates nothing.  q is [T, Hq, D] and k is [T, Hkv, D] with
+ * element strides (stride_t, stride_h) and a unit stride along D; the two
+ * tensors must not overlap each other and each must not overlap itself
+ * (checked from the strides; q/k views into one fused QKV buffer are fine).
+ * Calls are asynchronous on `stream` (a hipStream_t; NULL = the legacy default
+ * stream of the current device) and never synchronise with the host:
+ * cu_seqlens is read only on the device.  cu_seqlens must be int32, with
+ * 0 <= cu[0] <= cu[1] <= ... <= cu[nseq] <= T; this is NOT validated (that
+ * would need a device read).  Whatever cu_seqlens holds, the kernel only
+ * touches tokens t < T and heads < H, so bad metadata changes positions but
+ * never causes an out-of-bounds access.  Calls are reentrant.
+ *
+ * Errors are returned, never thrown or aborted; a launch error is reported as
+ * ROPE_QK_ERR_LAUNCH, and a device-side fault surfaces, as usual with HIP, at
+ * the caller's next synchronisation.
+ */
+#ifndef ROPE_QK_H
+#define ROPE_QK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* storage types of q and k (both tensors share one type) */
+#define ROPE_QK_FP32 0
+#define ROPE_QK_BF16 1
+
+/* status codes */
+#define ROPE_QK_OK 0
+#define ROPE_QK_ERR_NULL -1      /* a required pointer is NULL */
+#define ROPE_QK_ERR_SHAPE -2     /* negative size, D odd or < 2 or > 512, T >= 2^31, too many heads */
+#define ROPE_QK_ERR_DTYPE -3     /* dtype not ROPE_QK_FP32 / ROPE_QK_BF16 */
+#define ROPE_QK_ERR_ALIGN -4     /* base, stride*elem or (D/2)*elem not a multiple of 16 bytes */
+#define ROPE_QK_ERR_THETA -5     /* theta not finite or <= 0 */
+#define ROPE_QK_ERR_LAUNCH -6    /* the HIP launch itself failed */
+#define ROPE_QK_ERR_LAYOUT -7    /* negative strides, or a tensor whose rows overlap */
+
+/*
+ * Forward rotation, in place, of q and k in ONE kernel launch.
+ *
+ *   q            device pointer to q[T, Hq, D] (may be NULL only if Hq == 0)
+ *   k            device pointer to k[T, Hkv, D] (may be NULL only if Hkv == 0)
+ *   cu_seqlens   device pointer to int32[nseq + 1], cumulative sequence offsets
+ *   nseq         number of packed sequences (0: nothing is rotated)
+ *   T            number of tokens along the first axis of q and k, < 2^31
+ *   Hq, Hkv      heads of q and of k (grouped-query attention: Hkv <= Hq is usual)
+ *   D            head dimension, even, 2 <= D <= 512
+ *   q_stride_t, q_stride_h, k_stride_t, k_stride_h
+ *                element strides of the token and head axes (contiguous:
+ *                (Hq*D, D) and (Hkv*D, D)); must be >= 0
+ *   theta        rotary base (e.g. 1e6 for Qwen2.5/Qwen3, 5e5 for Llama-3.1)
+ *   dtype        ROPE_QK_FP32 or ROPE_QK_BF16
+ *   stream       hipStream_t to launch on
+ *
+ * Alignment (16-byte vector path): q, k, every stride * elem_size and
+ * (D/2) * elem_size must be multiples of 16 bytes.
+ * Returns ROPE_QK_OK or a negative status; T == 0, nseq == 0 or no heads is a
+ * no-op that launches nothing.
+ */
+int rope_qk_fwd(void* q, void* k, const int32_t* cu_seqlens, int64_t nseq, int64_t T,
+                int64_t Hq, int64_t Hkv, int64_t D, int64_t q_stride_t, int64_t q_stride_h,
+                int64_t k_stride_t, int64_t k_stride_h, double theta, int dtype, void* stream);
+
+/*
+ * Backward rotation, in place, of the incoming gradients dq and dk: the
+ * transpose of the forward map, i.e. rotation by the negated angle.  Same
+ * arguments, layout, ownership and errors as rope_qk_fwd.
+ */
+int rope_qk_bwd(void* dq, void* dk, const int32_t* cu_seqlens, int64_t nseq, int64_t T,
+                int64_t Hq, int64_t Hkv, int64_t D, int64_t q_stride_t, int64_t q_stride_h,
+                int64_t k_stride_t, int64_t k_stride_h, double theta, int dtype, void* stream);
+
+/*
+ * The positions the rotation kernels use, for inspection: writes, for every
+ * t < T, pos(t) as defined above, or -1 for tokens outside
+ * [cu_seqlens[0], cu_seqlens[nseq]).  Runs the same device function as the
+ * rotation kernels.  pos_out: device int32[T], caller-owned.  Asynchronous on
+ * `stream`.  Returns ROPE_QK_OK, ROPE_QK_ERR_NULL, ROPE_QK_ERR_SHAPE or
+ * ROPE_QK_ERR_LAUNCH.
+ */
+int rope_qk_positions(const int32_t* cu_seqlens, int64_t nseq, int64_t T, int32_t* pos_out,
+                      void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* rope_qk_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROPE_QK_H */

@@ -1,0 +1,33 @@
+"""Fused in-place QK rotary position embedding over packed variable-length
+batches, for AMD Instinct MI355X (gfx950).
+
+The work runs in the HIP kernels of ``librope_qk.so`` (C ABI in
+``include/rope_qk.h``); this package is a thin ctypes binding with the same
+entry-point names.  PyTorch is used only for device memory and streams.
+"""
+
+from ._lib import (  # noqa: F401
+    EXPORTS,
+    LIB_PATH,
+    ROPE_QK_BF16,
+    ROPE_QK_FP32,
+    RopeQKError,
+    load,
+    rope_qk_bwd,
+    rope_qk_fwd,
+    rope_qk_positions,
+    rope_qk_strerror,
+)
+
+__all__ = [
+    "rope_qk_fwd",
+    "rope_qk_bwd",
+    "rope_qk_positions",
+    "rope_qk_strerror",
+    "RopeQKError",
+    "load",
+    "LIB_PATH",
+    "EXPORTS",
+    "ROPE_QK_FP32",
+    "ROPE_QK_BF16",
+]

@@ -1,0 +1,154 @@
+"""ctypes binding to librope_qk.so: argument marshalling only.
+
+Every step of the rotation runs in the HIP kernels of the library; this module
+turns torch tensors into pointers, element strides, a dtype code and the
+current HIP stream, and raises on a non-zero status.  There is no fallback:
+if the library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librope_qk.so")
+
+ROPE_QK_FP32 = 0
+ROPE_QK_BF16 = 1
+
+# names exported by include/rope_qk.h
+EXPORTS = ("rope_qk_fwd", "rope_qk_bwd", "rope_qk_positions", "rope_qk_strerror")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class RopeQKError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"rope_qk status {status}: {msg}")
+        self.status = status
+
+
+def load():
+    """Load the shared library (once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        # torch wheels bundle their own libamdhip64.so.7; importing torch first makes
+        # the library bind to that same HIP runtime instance (streams and device
+        # pointers from torch are only valid there) instead of /opt/rocm's copy.
+        import torch  # noqa: F401
+
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m packed_varlen_rotary_amd.build` "
+                "(or __graft_entry__.build()); there is no fallback path"
+            )
+        lib = ctypes.CDLL(LIB_PATH)
+        i64, vp = ctypes.c_int64, ctypes.c_void_p
+        rot = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, i64, i64, ctypes.c_double, ctypes.c_int, vp]
+        for name in ("rope_qk_fwd", "rope_qk_bwd"):
+            fn = getattr(lib, name)
+            fn.argtypes = rot
+            fn.restype = ctypes.c_int
+        lib.rope_qk_positions.argtypes = [vp, i64, i64, vp, vp]
+        lib.rope_qk_positions.restype = ctypes.c_int
+        lib.rope_qk_strerror.argtypes = [ctypes.c_int]
+        lib.rope_qk_strerror.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def rope_qk_strerror(status: int) -> str:
+    return load().rope_qk_strerror(int(status)).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise RopeQKError(status, rope_qk_strerror(status))
+
+
+def _stream_ptr(device, stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return ROPE_QK_BF16
+    if t.dtype == torch.float32:
+        return ROPE_QK_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}: expected torch.float32 or torch.bfloat16")
+
+
+def _rotate(entry: str, q, k, cu_seqlens, theta: float, stream=None):
+    import torch
+
+    lib = load()
+    for name, t in (("q", q), ("k", k)):
+        if t.dim() != 3:
+            raise ValueError(f"{name} must be [T, H, D], got shape {tuple(t.shape)}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.shape[2] > 1 and t.stride(2) != 1:
+            raise ValueError(f"{name} must be unit-stride along D")
+    if q.shape[0] != k.shape[0] or q.shape[2] != k.shape[2]:
+        raise ValueError("q and k must share T and D")
+    if q.dtype != k.dtype:
+        raise TypeError("q and k must share one dtype")
+    if q.device != k.device or cu_seqlens.device != q.device:
+        raise ValueError("q, k and cu_seqlens must be on one device")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor")
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    with torch.cuda.device(q.device):
+        status = getattr(lib, entry)(
+            ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+            ctypes.c_void_p(cu_seqlens.data_ptr()), cu_seqlens.numel() - 1, T, Hq, Hkv, D,
+            q.stride(0), q.stride(1), k.stride(0), k.stride(1),
+            float(theta), _dtype_code(q), _stream_ptr(q.device, stream),
+        )
+    _check(status)
+
+
+def rope_qk_fwd(q, k, cu_seqlens, theta: float, stream=None):
+    """Rotate q [T, Hq, D] and k [T, Hkv, D] in place (one kernel launch).
+
+    cu_seqlens: int32 [nseq + 1] device tensor of packed-sequence offsets.
+    stream: a torch.cuda.Stream (default: the current stream of q's device).
+    """
+    _rotate("rope_qk_fwd", q, k, cu_seqlens, theta, stream)
+
+
+def rope_qk_bwd(dq, dk, cu_seqlens, theta: float, stream=None):
+    """Backward of rope_qk_fwd, in place on the incoming gradients dq and dk."""
+    _rotate("rope_qk_bwd", dq, dk, cu_seqlens, theta, stream)
+
+
+def rope_qk_positions(cu_seqlens, T: int, out=None, stream=None):
+    """Per-token positions the kernels use (int32 [T], -1 outside every sequence)."""
+    import torch
+
+    lib = load()
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor")
+    if out is None:
+        out = torch.empty(T, dtype=torch.int32, device=cu_seqlens.device)
+    if out.dtype != torch.int32 or out.numel() != T or not out.is_contiguous():
+        raise ValueError("out must be a contiguous int32 tensor of T elements")
+    with torch.cuda.device(cu_seqlens.device):
+        status = lib.rope_qk_positions(
+            ctypes.c_void_p(cu_seqlens.data_ptr()), cu_seqlens.numel() - 1, int(T),
+            ctypes.c_void_p(out.data_ptr()), _stream_ptr(cu_seqlens.device, stream),
+        )
+    _check(status)
+    return out

@@ -1,0 +1,383 @@
+// Fused in-place QK rotary position embedding over packed variable-length
+// batches, forward and backward, for AMD Instinct MI355X (CDNA4, gfx950).
+//
+// The operation, its arguments and its contract are documented in
+// include/rope_qk.h.  Sources on the pages: the fused QK RoPE kernel paragraph
+// of "Unsloth prétend accélérer 5 fois l'entraînement des LLM avec de nouveaux
+// noyaux Triton et un auto-packing" (seventnews.com: q and k in one kernel,
+// variable length, fully in place), its auto-packing paragraph (length
+// metadata keeps samples apart), its LONG_INDEXING paragraph (500K-token
+// contexts need wide offsets) and its kernel-history paragraph (blocks launched
+// for groups of heads share the rotary factors); "Chronicals: A
+// High-Performance Framework for LLM Fine-Tuning with 3.51x Speedup over
+// Unsloth", abstract, optimisation (1) (QK-RoPE fusion removes memory traffic).
+//
+// Design (one launch per call, HBM-bound: every element of q and k is read
+// once and written once, ~0.75 flop per byte, so there is no MFMA here):
+//
+//  * A workgroup owns a tile of consecutive tokens.  The work of a tile is a
+//    flat list of "tasks"; a task is one 16-byte chunk of the first half of a
+//    head together with the matching 16-byte chunk of its second half (the
+//    rotate_half partner i + D/2), over the heads of q followed by those of k.
+//    Consecutive lanes take consecutive chunks of a head, so each load/store
+//    instruction of a wave covers whole 64-128 byte runs.
+//  * The global loads of a pass are issued first.  While they are in flight
+//    the workgroup finds each token's position (binary search over cu_seqlens,
+//    which stays on the device) and evaluates cos/sin once per (token, pair)
+//    in float64 into LDS, where all heads of q and k read them.
+//  * The rotation is done in float64 and rounded once: fp32 output is the
+//    correctly rounded fp32; bf16 output is the correctly rounded bf16 (fast
+//    float64->fp32->bf16 path, and an exact re-rounding for the rare values
+//    whose fp32 rounding lands exactly on a bf16 midpoint).
+//  * All offsets are 64-bit; one build covers every tensor size.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include "rope_qk.h"
+
+namespace {
+
+constexpr int kThreads = 256;          // 4 wave64s per workgroup
+constexpr int kMaxHalf = 256;          // D <= 512
+constexpr int kMaxTileTokens = 64;
+constexpr int kMaxLdsBytes = 32768;    // cos/sin table per workgroup
+constexpr uint32_t kMaxTasksPerToken = 65535;
+constexpr int64_t kMaxGrid = int64_t(1) << 20;
+
+#ifndef ROPE_QK_TASKS_PER_THREAD
+#define ROPE_QK_TASKS_PER_THREAD 4
+#endif
+constexpr int kTPT = ROPE_QK_TASKS_PER_THREAD;  // 16-byte chunk pairs in flight per lane
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct RopeParams {
+  char* q;                 // base of q (bytes)
+  char* k;                 // base of k (bytes)
+  const int32_t* cu;       // cu_seqlens[nseq + 1]
+  int64_t T;
+  int64_t q_st, q_sh;      // byte strides of q along tokens / heads
+  int64_t k_st, k_sh;      // byte strides of k along tokens / heads
+  int64_t ntiles;          // ceil(T / tile_tokens)
+  uint64_t magic_task;     // ceil(2^32 / tasks_per_tok)
+  uint64_t magic_chunk;    // ceil(2^32 / chunks)
+  int32_t nseq;
+  int32_t Hq;
+  int32_t tasks_per_tok;   // (Hq + Hkv) * chunks
+  int32_t chunks;          // 16-byte chunks per half head
+  int32_t half;            // D / 2
+  int32_t half_bytes;      // (D / 2) * element size
+  int32_t tile_tokens;
+  double sign;             // +1 forward, -1 backward
+  double inv_freq[kMaxHalf];
+};
+
+// n / d for n, d < 2^16 with m = ceil(2^32 / d): exact because n * (m d - 2^32) < 2^32.
+__device__ __forceinline__ uint32_t div_small(uint32_t n, uint64_t m) {
+  return static_cast<uint32_t>((static_cast<uint64_t>(n) * m) >> 32);
+}
+
+// Position of token t inside its packed sequence, or -1 when t lies outside
+// [cu[0], cu[nseq]).  s is the last index with cu[s] <= t, so empty segments
+// (repeated offsets) resolve to the sequence that actually holds t and the
+// counter restarts at every boundary.  Indices stay inside [0, nseq] whatever
+// cu holds.
+__device__ __forceinline__ int32_t token_position(const int32_t* __restrict__ cu, int32_t nseq,
+                                                  int64_t t) {
+  const int64_t first = cu[0];
+  const int64_t last = cu[nseq];
+  if (t < first || t >= last) return -1;
+  int32_t lo = 0, hi = nseq;  // cu[lo] <= t < cu[hi] for non-decreasing cu
+  while (hi - lo > 1) {
+    const int32_t mid = lo + ((hi - lo) >> 1);
+    if (static_cast<int64_t>(cu[mid]) <= t) lo = mid; else hi = mid;
+  }
+  const int64_t p = t - static_cast<int64_t>(cu[lo]);
+  return (p >= 0 && p <= INT32_MAX) ? static_cast<int32_t>(p) : -1;
+}
+
+// LDS slot of pair i of tile token tt.  Pairs are stored chunk-minor:
+// i = c * vec + j -> (tt * vec + j) * chunks + c, so lanes working on
+// different chunks of one token read adjacent 16-byte slots (no bank
+// conflicts) and lanes on the same chunk read the same slot (broadcast).
+__device__ __forceinline__ int cs_slot(int tt, int i, int vec, int chunks) {
+  const int c = i / vec;
+  const int j = i - c * vec;
+  return (tt * vec + j) * chunks + c;
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+
+// Fast rounding of two float64 values to a packed bf16 pair: round each to
+// fp32, then the pair to bf16 (both round to nearest even; one packed
+// conversion).  The result equals the single correctly rounded bf16 unless
+// an fp32 value is exactly a bf16 midpoint, which sets `tie`.
+__device__ __forceinline__ uint32_t pack_bf16_fast(double lo, double hi, bool& tie) {
+  const f32x2 f = {static_cast<float>(lo), static_cast<float>(hi)};
+  tie |= (__float_as_uint(f.x) & 0xFFFFu) == 0x8000u;
+  tie |= (__float_as_uint(f.y) & 0xFFFFu) == 0x8000u;
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+// Exact: one rounding from float64 to bf16 (the compiler's float64->bf16
+// conversion rounds to odd at fp32 precision, then to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16_exact(double lo, double hi) {
+  const f64x2 d = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(d, bf16x2));
+}
+
+__device__ __forceinline__ double bf16_lo(uint32_t w) { return static_cast<double>(__uint_as_float(w << 16)); }
+__device__ __forceinline__ double bf16_hi(uint32_t w) { return static_cast<double>(__uint_as_float(w & 0xFFFF0000u)); }
+
+// Rotate one task of bf16 data: a holds x[i .. i+7], b holds x[i+D/2 .. i+D/2+7].
+template <bool kExact>
+__device__ __forceinline__ bool rotate_bf16(const u32x4& a, const u32x4& b, const double2* __restrict__ cs,
+                                            int chunks, u32x4& oa, u32x4& ob) {
+  bool tie = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const double2 c0 = cs[(2 * j) * chunks];
+    const double2 c1 = cs[(2 * j + 1) * chunks];
+    const double x1l = bf16_lo(a[j]), x1h = bf16_hi(a[j]);
+    const double x2l = bf16_lo(b[j]), x2h = bf16_hi(b[j]);
+    const double y1l = fma(x1l, c0.x, -(x2l * c0.y));
+    const double y2l = fma(x2l, c0.x, x1l * c0.y);
+    const double y1h = fma(x1h, c1.x, -(x2h * c1.y));
+    const double y2h = fma(x2h, c1.x, x1h * c1.y);
+    if (kExact) {
+      oa[j] = pack_bf16_exact(y1l, y1h);
+      ob[j] = pack_bf16_exact(y2l, y2h);
+    } else {
+      oa[j] = pack_bf16_fast(y1l, y1h, tie);
+      ob[j] = pack_bf16_fast(y2l, y2h, tie);
+    }
+  }
+  return tie;
+}
+
+// Rotate one task of fp32 data: a holds x[i .. i+3], b holds x[i+D/2 .. i+D/2+3].
+__device__ __forceinline__ void rotate_f32(const u32x4& a, const u32x4& b, const double2* __restrict__ cs,
+                                           int chunks, u32x4& oa, u32x4& ob) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const double2 c = cs[j * chunks];
+    const double x1 = static_cast<double>(__uint_as_float(a[j]));
+    const double x2 = static_cast<double>(__uint_as_float(b[j]));
+    oa[j] = __float_as_uint(static_cast<float>(fma(x1, c.x, -(x2 * c.y))));
+    ob[j] = __float_as_uint(static_cast<float>(fma(x2, c.x, x1 * c.y)));
+  }
+}
+
+template <int kDtype>
+__global__ __launch_bounds__(kThreads) void rope_qk_kernel(const RopeParams p) {
+  constexpr int kVec = (kDtype == ROPE_QK_BF16) ? 8 : 4;  // elements per 16 bytes
+  extern __shared__ double2 s_cs[];                        // [tile_tokens * half]
+  __shared__ int32_t s_pos[kMaxTileTokens];
+  const int tid = threadIdx.x;
+
+  for (int64_t tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
+    const int64_t t0 = tile * p.tile_tokens;
+    const int ntok = static_cast<int>(min(static_cast<int64_t>(p.tile_tokens), p.T - t0));
+    const uint32_t ntasks = static_cast<uint32_t>(ntok) * static_cast<uint32_t>(p.tasks_per_tok);
+
+    for (uint32_t base = 0; base < ntasks; base += kThreads * kTPT) {
+      u32x4 a[kTPT], b[kTPT];
+      char* ptr[kTPT];
+      int tt_of[kTPT], c_of[kTPT];
+      bool act[kTPT];
+
+      // 1. issue every load of this pass
+#pragma unroll
+      for (int u = 0; u < kTPT; ++u) {
+        const uint32_t n = base + static_cast<uint32_t>(tid + u * kThreads);
+        act[u] = n < ntasks;
+        const uint32_t tt = div_small(n, p.magic_task);
+        const uint32_t r = n - tt * static_cast<uint32_t>(p.tasks_per_tok);
+        const uint32_t h = div_small(r, p.magic_chunk);
+        const uint32_t c = r - h * static_cast<uint32_t>(p.chunks);
+        const int64_t t = t0 + tt;
+        const bool is_q = static_cast<int32_t>(h) < p.Hq;
+        char* row = is_q ? p.q + t * p.q_st + static_cast<int64_t>(h) * p.q_sh
+                         : p.k + t * p.k_st + static_cast<int64_t>(h - p.Hq) * p.k_sh;
+        ptr[u] = row + static_cast<int64_t>(c) * 16;
+        tt_of[u] = static_cast<int>(tt);
+        c_of[u] = static_cast<int>(c);
+        if (act[u]) {
+          a[u] = *reinterpret_cast<const u32x4*>(ptr[u]);
+          b[u] = *reinterpret_cast<const u32x4*>(ptr[u] + p.half_bytes);
+        }
+      }
+
+      // 2. positions and the cos/sin table, while the loads are in flight
+      if (base == 0) {
+        if (tid < ntok) s_pos[tid] = token_position(p.cu, p.nseq, t0 + tid);
+        __syncthreads();
+        const int nent = ntok * p.half;
+        for (int e = tid; e < nent; e += kThreads) {
+          const int tt = e / p.half;
+          const int i = e - tt * p.half;
+          const int32_t pos = s_pos[tt];
+          if (pos >= 0) {
+            double sn, cs;
+            sincos(static_cast<double>(pos) * p.inv_freq[i], &sn, &cs);
+            s_cs[cs_slot(tt, i, kVec, p.chunks)] = make_double2(cs, p.sign * sn);
+          }
+        }
+        __syncthreads();
+      }
+
+      // 3. rotate and store; tokens outside every sequence are left untouched
+#pragma unroll
+      for (int u = 0; u < kTPT; ++u) {
+        if (!act[u] || s_pos[tt_of[u]] < 0) continue;
+        const double2* cs = s_cs + tt_of[u] * kVec * p.chunks + c_of[u];
+        u32x4 oa, ob;
+        if constexpr (kDtype == ROPE_QK_BF16) {
+          if (rotate_bf16<false>(a[u], b[u], cs, p.chunks, oa, ob))
+            rotate_bf16<true>(a[u], b[u], cs, p.chunks, oa, ob);
+        } else {
+          rotate_f32(a[u], b[u], cs, p.chunks, oa, ob);
+        }
+        *reinterpret_cast<u32x4*>(ptr[u]) = oa;
+        *reinterpret_cast<u32x4*>(ptr[u] + p.half_bytes) = ob;
+      }
+    }
+    __syncthreads();  // the next tile of this workgroup rewrites s_pos and s_cs
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void rope_positions_kernel(const int32_t* __restrict__ cu, int32_t nseq,
+                                                                  int64_t T, int32_t* __restrict__ out) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; t < T; t += stride)
+    out[t] = token_position(cu, nseq, t);
+}
+
+// Rows of D elements at t * st + h * sh (t < T, h < H), all strides >= 0: do any two overlap?
+bool rows_overlap(int64_t T, int64_t H, int64_t D, int64_t st, int64_t sh) {
+  if (T <= 1 && H <= 1) return false;
+  if (T <= 1) return sh < D;
+  if (H <= 1) return st < D;
+  const int64_t s_small = st < sh ? st : sh, n_small = st < sh ? T : H;
+  const int64_t s_big = st < sh ? sh : st;
+  if (s_small < D) return true;
+  return s_big / s_small < n_small;  // s_big < n_small * s_small, without overflow
+}
+
+int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, int64_t Hq, int64_t Hkv, int64_t D,
+                int64_t q_st, int64_t q_sh, int64_t k_st, int64_t k_sh, double theta, int dtype, void* stream,
+                double sign) {
+  if (dtype != ROPE_QK_FP32 && dtype != ROPE_QK_BF16) return ROPE_QK_ERR_DTYPE;
+  if (nseq < 0 || T < 0 || Hq < 0 || Hkv < 0 || D < 2 || (D & 1) || D > 2 * kMaxHalf || T > INT32_MAX ||
+      nseq >= INT32_MAX || Hq + Hkv > INT32_MAX)
+    return ROPE_QK_ERR_SHAPE;
+  if (!(theta > 0.0) || !isfinite(theta)) return ROPE_QK_ERR_THETA;
+  if (T == 0 || nseq == 0 || Hq + Hkv == 0) return ROPE_QK_OK;
+  if (cu == nullptr || (Hq > 0 && q == nullptr) || (Hkv > 0 && k == nullptr)) return ROPE_QK_ERR_NULL;
+  if ((Hq > 0 && (q_st < 0 || q_sh < 0 || rows_overlap(T, Hq, D, q_st, q_sh))) ||
+      (Hkv > 0 && (k_st < 0 || k_sh < 0 || rows_overlap(T, Hkv, D, k_st, k_sh))))
+    return ROPE_QK_ERR_LAYOUT;
+
+  const int64_t esz = dtype == ROPE_QK_BF16 ? 2 : 4;
+  const int64_t half = D / 2;
+  if ((half * esz) % 16) return ROPE_QK_ERR_ALIGN;
+  if (Hq > 0 && ((reinterpret_cast<uintptr_t>(q) % 16) || (q_st * esz) % 16 || (q_sh * esz) % 16))
+    return ROPE_QK_ERR_ALIGN;
+  if (Hkv > 0 && ((reinterpret_cast<uintptr_t>(k) % 16) || (k_st * esz) % 16 || (k_sh * esz) % 16))
+    return ROPE_QK_ERR_ALIGN;
+
+  const int64_t chunks = half * esz / 16;
+  const int64_t tasks_per_tok = (Hq + Hkv) * chunks;
+  if (tasks_per_tok > kMaxTasksPerToken) return ROPE_QK_ERR_SHAPE;
+
+  int64_t tile = static_cast<int64_t>(kThreads) * kTPT / tasks_per_tok;
+  const int64_t lds_cap = kMaxLdsBytes / (half * 16);
+  if (tile > kMaxTileTokens) tile = kMaxTileTokens;
+  if (tile > lds_cap) tile = lds_cap;
+  if (tile < 1) tile = 1;
+
+  RopeParams p;
+  p.q = static_cast<char*>(q);
+  p.k = static_cast<char*>(k);
+  p.cu = cu;
+  p.T = T;
+  p.q_st = q_st * esz;
+  p.q_sh = q_sh * esz;
+  p.k_st = k_st * esz;
+  p.k_sh = k_sh * esz;
+  p.ntiles = (T + tile - 1) / tile;
+  p.magic_task = ((uint64_t(1) << 32) + tasks_per_tok - 1) / tasks_per_tok;
+  p.magic_chunk = ((uint64_t(1) << 32) + chunks - 1) / chunks;
+  p.nseq = static_cast<int32_t>(nseq);
+  p.Hq = static_cast<int32_t>(Hq);
+  p.tasks_per_tok = static_cast<int32_t>(tasks_per_tok);
+  p.chunks = static_cast<int32_t>(chunks);
+  p.half = static_cast<int32_t>(half);
+  p.half_bytes = static_cast<int32_t>(half * esz);
+  p.tile_tokens = static_cast<int32_t>(tile);
+  p.sign = sign;
+  for (int64_t i = 0; i < kMaxHalf; ++i)
+    p.inv_freq[i] = i < half ? pow(theta, -static_cast<double>(2 * i) / static_cast<double>(D)) : 0.0;
+
+  const int64_t grid = p.ntiles < kMaxGrid ? p.ntiles : kMaxGrid;
+  const size_t lds = static_cast<size_t>(tile * half) * sizeof(double2);
+  void* args[] = {&p};
+  const void* fn = dtype == ROPE_QK_BF16 ? reinterpret_cast<const void*>(&rope_qk_kernel<ROPE_QK_BF16>)
+                                         : reinterpret_cast<const void*>(&rope_qk_kernel<ROPE_QK_FP32>);
+  const hipError_t err = hipLaunchKernel(fn, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), args, lds,
+                                         static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? ROPE_QK_OK : ROPE_QK_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rope_qk_fwd(void* q, void* k, const int32_t* cu_seqlens, int64_t nseq, int64_t T, int64_t Hq, int64_t Hkv,
+                int64_t D, int64_t q_stride_t, int64_t q_stride_h, int64_t k_stride_t, int64_t k_stride_h,
+                double theta, int dtype, void* stream) {
+  return launch_rope(q, k, cu_seqlens, nseq, T, Hq, Hkv, D, q_stride_t, q_stride_h, k_stride_t, k_stride_h, theta,
+                     dtype, stream, 1.0);
+}
+
+int rope_qk_bwd(void* dq, void* dk, const int32_t* cu_seqlens, int64_t nseq, int64_t T, int64_t Hq, int64_t Hkv,
+                int64_t D, int64_t q_stride_t, int64_t q_stride_h, int64_t k_stride_t, int64_t k_stride_h,
+                double theta, int dtype, void* stream) {
+  return launch_rope(dq, dk, cu_seqlens, nseq, T, Hq, Hkv, D, q_stride_t, q_stride_h, k_stride_t, k_stride_h,
+                     theta, dtype, stream, -1.0);
+}
+
+int rope_qk_positions(const int32_t* cu_seqlens, int64_t nseq, int64_t T, int32_t* pos_out, void* stream) {
+  if (nseq < 0 || T < 0 || T > INT32_MAX || nseq >= INT32_MAX) return ROPE_QK_ERR_SHAPE;
+  if (T == 0) return ROPE_QK_OK;
+  if (cu_seqlens == nullptr || pos_out == nullptr) return ROPE_QK_ERR_NULL;
+  const int64_t blocks = (T + kThreads - 1) / kThreads;
+  const int64_t grid = blocks < kMaxGrid ? blocks : kMaxGrid;
+  int32_t n = static_cast<int32_t>(nseq);
+  void* args[] = {&cu_seqlens, &n, &T, &pos_out};
+  const hipError_t err =
+      hipLaunchKernel(reinterpret_cast<const void*>(&rope_positions_kernel), dim3(static_cast<uint32_t>(grid)),
+                      dim3(kThreads), args, 0, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? ROPE_QK_OK : ROPE_QK_ERR_LAUNCH;
+}
+
+const char* rope_qk_strerror(int status) {
+  switch (status) {
+    case ROPE_QK_OK: return "ok";
+    case ROPE_QK_ERR_NULL: return "a required pointer is NULL";
+    case ROPE_QK_ERR_SHAPE: return "unsupported shape (negative size, D odd/<2/>512, T >= 2^31, too many heads)";
+    case ROPE_QK_ERR_DTYPE: return "unsupported dtype (expected ROPE_QK_FP32 or ROPE_QK_BF16)";
+    case ROPE_QK_ERR_ALIGN: return "misaligned: pointers, strides and D/2 must be multiples of 16 bytes";
+    case ROPE_QK_ERR_THETA: return "theta must be finite and > 0";
+    case ROPE_QK_ERR_LAUNCH: return "HIP kernel launch failed";
+    case ROPE_QK_ERR_LAYOUT: return "negative strides or overlapping rows";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"
