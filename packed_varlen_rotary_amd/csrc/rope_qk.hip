@@ -15,16 +15,21 @@
 // Design (one launch per call, HBM-bound: every element of q and k is read
 // once and written once, ~0.75 flop per byte, so there is no MFMA here):
 //
-//  * A workgroup owns a tile of consecutive tokens.  The work of a tile is a
-//    flat list of "tasks"; a task is one 16-byte chunk of the first half of a
-//    head together with the matching 16-byte chunk of its second half (the
-//    rotate_half partner i + D/2), over the heads of q followed by those of k.
-//    Consecutive lanes take consecutive chunks of a head, so each load/store
-//    instruction of a wave covers whole 64-128 byte runs.
-//  * The global loads of a pass are issued first.  While they are in flight
-//    the workgroup finds each token's position (binary search over cu_seqlens,
-//    which stays on the device) and evaluates cos/sin once per (token, pair)
-//    in float64 into LDS, where all heads of q and k read them.
+//  * A workgroup owns a tile of consecutive tokens (one tile per workgroup;
+//    measured on MI355X, a one-shot grid streams better than a persistent
+//    one).  The work of a tile is a flat list of "tasks"; a task is one
+//    16-byte chunk of the first half of a head together with the matching
+//    16-byte chunk of its second half (the rotate_half partner i + D/2), over
+//    the heads of q followed by those of k.  Consecutive lanes take
+//    consecutive chunks of a head, so each load/store instruction of a wave
+//    covers whole 64-128 byte runs.  Each lane keeps 4 tasks (128 bytes of
+//    loads) in flight.
+//  * First the workgroup finds each token's position -- a wave-uniform
+//    binary search over cu_seqlens through the scalar cache, then a uniform
+//    scan of the boundaries inside the tile -- and evaluates cos/sin once per
+//    (token, pair) in float64 into LDS, where all heads of q and k read them.
+//    Then it streams its q/k chunks with non-temporal loads and stores; the
+//    other workgroups resident on the CU overlap each other's phases.
 //  * The rotation is done in float64 and rounded once: fp32 output is the
 //    correctly rounded fp32; bf16 output is the correctly rounded bf16 (fast
 //    float64->fp32->bf16 path, and an exact re-rounding for the rare values
@@ -37,22 +42,33 @@
 #include <stdint.h>
 
 #include "rope_qk.h"
+#include "rope_sincos.h"
 
 namespace {
 
 constexpr int kThreads = 256;          // 4 wave64s per workgroup
 constexpr int kMaxHalf = 256;          // D <= 512
 constexpr int kMaxTileTokens = 64;
-constexpr int kMaxLdsBytes = 32768;    // cos/sin table per workgroup
+constexpr int kMaxTableBytes = 16384;  // cos/sin table per workgroup
 constexpr uint32_t kMaxTasksPerToken = 65535;
-constexpr int64_t kMaxGrid = int64_t(1) << 20;
+constexpr int64_t kMaxGrid = int64_t(1) << 20;  // grid * 256 work-items stays below 2^32
 
 #ifndef ROPE_QK_TASKS_PER_THREAD
 #define ROPE_QK_TASKS_PER_THREAD 4
 #endif
+#ifndef ROPE_QK_WAVES_PER_SIMD
+#define ROPE_QK_WAVES_PER_SIMD 3
+#endif
 constexpr int kTPT = ROPE_QK_TASKS_PER_THREAD;  // 16-byte chunk pairs in flight per lane
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+// cu_seqlens is only read, with wave-uniform indices: through the constant
+// address space these become scalar loads, which the vector-memory counter
+// does not order behind the tile's in-flight HBM loads.
+typedef const __attribute__((address_space(4))) int32_t* cu_ptr;
 
 struct RopeParams {
   char* q;                 // base of q (bytes)
@@ -80,23 +96,27 @@ __device__ __forceinline__ uint32_t div_small(uint32_t n, uint64_t m) {
   return static_cast<uint32_t>((static_cast<uint64_t>(n) * m) >> 32);
 }
 
-// Position of token t inside its packed sequence, or -1 when t lies outside
-// [cu[0], cu[nseq]).  s is the last index with cu[s] <= t, so empty segments
-// (repeated offsets) resolve to the sequence that actually holds t and the
-// counter restarts at every boundary.  Indices stay inside [0, nseq] whatever
-// cu holds.
-__device__ __forceinline__ int32_t token_position(const int32_t* __restrict__ cu, int32_t nseq,
-                                                  int64_t t) {
-  const int64_t first = cu[0];
-  const int64_t last = cu[nseq];
-  if (t < first || t >= last) return -1;
-  int32_t lo = 0, hi = nseq;  // cu[lo] <= t < cu[hi] for non-decreasing cu
+// Last index s in [0, nseq] with cu[s] <= t, or -1 if cu[0] > t.  Every index
+// probed lies in [0, nseq] whatever cu holds.
+__device__ __forceinline__ int32_t last_start_at_or_before(cu_ptr cu, int32_t nseq, int64_t t) {
+  int32_t lo = -1, hi = nseq + 1;  // cu[lo] <= t < cu[hi], with virtual -inf / +inf ends
   while (hi - lo > 1) {
     const int32_t mid = lo + ((hi - lo) >> 1);
     if (static_cast<int64_t>(cu[mid]) <= t) lo = mid; else hi = mid;
   }
-  const int64_t p = t - static_cast<int64_t>(cu[lo]);
-  return (p >= 0 && p <= INT32_MAX) ? static_cast<int32_t>(p) : -1;
+  return lo;
+}
+
+// Position of token t inside its packed sequence, or -1 when t lies outside
+// [cu[0], cu[nseq]): t minus the last sequence start at or before t, so empty
+// segments (repeated offsets) resolve to the sequence that holds t and the
+// counter restarts at every boundary.
+__device__ __forceinline__ int32_t token_position(cu_ptr cu, int32_t nseq, int64_t t) {
+  if (t >= static_cast<int64_t>(cu[nseq])) return -1;
+  const int32_t s = last_start_at_or_before(cu, nseq, t);
+  if (s < 0) return -1;
+  const int64_t p = t - static_cast<int64_t>(cu[s]);
+  return p <= INT32_MAX ? static_cast<int32_t>(p) : -1;
 }
 
 // LDS slot of pair i of tile token tt.  Pairs are stored chunk-minor:
@@ -108,10 +128,6 @@ __device__ __forceinline__ int cs_slot(int tt, int i, int vec, int chunks) {
   const int j = i - c * vec;
   return (tt * vec + j) * chunks + c;
 }
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 // Fast rounding of two float64 values to a packed bf16 pair: round each to
 // fp32, then the pair to bf16 (both round to nearest even; one packed
@@ -173,17 +189,27 @@ __device__ __forceinline__ void rotate_f32(const u32x4& a, const u32x4& b, const
   }
 }
 
+// One tile of consecutive tokens per workgroup (a grid-stride loop covers
+// launches with more tiles than the grid).
 template <int kDtype>
-__global__ __launch_bounds__(kThreads) void rope_qk_kernel(const RopeParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ROPE_QK_WAVES_PER_SIMD)))
+void rope_qk_kernel(const RopeParams p) {
   constexpr int kVec = (kDtype == ROPE_QK_BF16) ? 8 : 4;  // elements per 16 bytes
-  extern __shared__ double2 s_cs[];                        // [tile_tokens * half]
-  __shared__ int32_t s_pos[kMaxTileTokens];
+  __shared__ int32_t s_pos[kMaxTileTokens];                 // positions of the tile's tokens
+  extern __shared__ double2 s_cs[];                         // [tile_tokens * half] {cos, sign*sin}
   const int tid = threadIdx.x;
+  const cu_ptr cu = (cu_ptr)p.cu;  // address-space cast (C-style: reinterpret_cast cannot change it)
+  const int32_t nseq = p.nseq;
+  const int64_t cu_last = cu[nseq];
 
   for (int64_t tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
     const int64_t t0 = tile * p.tile_tokens;
     const int ntok = static_cast<int>(min(static_cast<int64_t>(p.tile_tokens), p.T - t0));
+    const int64_t t_end = t0 + ntok;  // one past the tile's last token
     const uint32_t ntasks = static_cast<uint32_t>(ntok) * static_cast<uint32_t>(p.tasks_per_tok);
+    const int nent = ntok * p.half;
+
+    const int32_t s0 = last_start_at_or_before(cu, nseq, t0);  // scalar loads
 
     for (uint32_t base = 0; base < ntasks; base += kThreads * kTPT) {
       u32x4 a[kTPT], b[kTPT];
@@ -191,11 +217,44 @@ __global__ __launch_bounds__(kThreads) void rope_qk_kernel(const RopeParams p) {
       int tt_of[kTPT], c_of[kTPT];
       bool act[kTPT];
 
-      // 1. issue every load of this pass
+      // 1. positions and the cos/sin table (first pass of the tile only)
+      if (base == 0) {
+#pragma unroll 1
+        for (int e0 = 0; e0 < nent; e0 += kThreads) {
+          const int e = e0 + tid;
+          const bool on = e < nent;
+          const int tt = on ? e / p.half : 0;
+          const int i = e - tt * p.half;
+          const int64_t t = t0 + tt;
+          // last sequence start at or before t: the tile's first start, then
+          // any boundaries inside the tile (wave-uniform scan)
+          int64_t start = s0 >= 0 ? static_cast<int64_t>(cu[s0]) : INT64_MIN;
+          for (int32_t j = s0 + 1; j <= nseq; ++j) {
+            const int64_t v = cu[j];
+            if (v >= t_end) break;
+            start = v <= t ? v : start;
+          }
+          const int64_t pos64 = t - start;
+          const int32_t pos =
+              (start != INT64_MIN && t < cu_last && pos64 <= INT32_MAX) ? static_cast<int32_t>(pos64) : -1;
+          if (on) {
+            if (i == 0) s_pos[tt] = pos;
+            if (pos >= 0) {
+              double sn, cs;
+              rope_sincos(static_cast<double>(pos) * p.inv_freq[i], &sn, &cs);
+              s_cs[cs_slot(tt, i, kVec, p.chunks)] = make_double2(cs, p.sign * sn);
+            }
+          }
+        }
+        __syncthreads();
+      }
+
+      // 2. issue every load of this pass (lanes without a task re-read task 0)
 #pragma unroll
       for (int u = 0; u < kTPT; ++u) {
-        const uint32_t n = base + static_cast<uint32_t>(tid + u * kThreads);
-        act[u] = n < ntasks;
+        const uint32_t n_raw = base + static_cast<uint32_t>(tid + u * kThreads);
+        act[u] = n_raw < ntasks;
+        const uint32_t n = act[u] ? n_raw : 0u;
         const uint32_t tt = div_small(n, p.magic_task);
         const uint32_t r = n - tt * static_cast<uint32_t>(p.tasks_per_tok);
         const uint32_t h = div_small(r, p.magic_chunk);
@@ -207,28 +266,9 @@ __global__ __launch_bounds__(kThreads) void rope_qk_kernel(const RopeParams p) {
         ptr[u] = row + static_cast<int64_t>(c) * 16;
         tt_of[u] = static_cast<int>(tt);
         c_of[u] = static_cast<int>(c);
-        if (act[u]) {
-          a[u] = *reinterpret_cast<const u32x4*>(ptr[u]);
-          b[u] = *reinterpret_cast<const u32x4*>(ptr[u] + p.half_bytes);
-        }
-      }
-
-      // 2. positions and the cos/sin table, while the loads are in flight
-      if (base == 0) {
-        if (tid < ntok) s_pos[tid] = token_position(p.cu, p.nseq, t0 + tid);
-        __syncthreads();
-        const int nent = ntok * p.half;
-        for (int e = tid; e < nent; e += kThreads) {
-          const int tt = e / p.half;
-          const int i = e - tt * p.half;
-          const int32_t pos = s_pos[tt];
-          if (pos >= 0) {
-            double sn, cs;
-            sincos(static_cast<double>(pos) * p.inv_freq[i], &sn, &cs);
-            s_cs[cs_slot(tt, i, kVec, p.chunks)] = make_double2(cs, p.sign * sn);
-          }
-        }
-        __syncthreads();
+        // streamed once: non-temporal, so they do not displace other data in the caches
+        a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr[u]));
+        b[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr[u] + p.half_bytes));
       }
 
       // 3. rotate and store; tokens outside every sequence are left untouched
@@ -243,16 +283,18 @@ __global__ __launch_bounds__(kThreads) void rope_qk_kernel(const RopeParams p) {
         } else {
           rotate_f32(a[u], b[u], cs, p.chunks, oa, ob);
         }
-        *reinterpret_cast<u32x4*>(ptr[u]) = oa;
-        *reinterpret_cast<u32x4*>(ptr[u] + p.half_bytes) = ob;
+        __builtin_nontemporal_store(oa, reinterpret_cast<u32x4*>(ptr[u]));
+        __builtin_nontemporal_store(ob, reinterpret_cast<u32x4*>(ptr[u] + p.half_bytes));
       }
     }
-    __syncthreads();  // the next tile of this workgroup rewrites s_pos and s_cs
+    __syncthreads();  // a further tile of this workgroup rewrites s_pos and s_cs
   }
 }
 
-__global__ __launch_bounds__(kThreads) void rope_positions_kernel(const int32_t* __restrict__ cu, int32_t nseq,
-                                                                  int64_t T, int32_t* __restrict__ out) {
+__global__ __launch_bounds__(kThreads) void rope_positions_kernel(const int32_t* __restrict__ cu_seqlens,
+                                                                  int32_t nseq, int64_t T,
+                                                                  int32_t* __restrict__ out) {
+  const cu_ptr cu = (cu_ptr)cu_seqlens;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
   for (int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; t < T; t += stride)
     out[t] = token_position(cu, nseq, t);
@@ -296,7 +338,7 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
   if (tasks_per_tok > kMaxTasksPerToken) return ROPE_QK_ERR_SHAPE;
 
   int64_t tile = static_cast<int64_t>(kThreads) * kTPT / tasks_per_tok;
-  const int64_t lds_cap = kMaxLdsBytes / (half * 16);
+  const int64_t lds_cap = kMaxTableBytes / (half * 16);
   if (tile > kMaxTileTokens) tile = kMaxTileTokens;
   if (tile > lds_cap) tile = lds_cap;
   if (tile < 1) tile = 1;
@@ -357,7 +399,7 @@ int rope_qk_positions(const int32_t* cu_seqlens, int64_t nseq, int64_t T, int32_
   if (T == 0) return ROPE_QK_OK;
   if (cu_seqlens == nullptr || pos_out == nullptr) return ROPE_QK_ERR_NULL;
   const int64_t blocks = (T + kThreads - 1) / kThreads;
-  const int64_t grid = blocks < kMaxGrid ? blocks : kMaxGrid;
+  const int64_t grid = blocks < 65536 ? blocks : 65536;
   int32_t n = static_cast<int32_t>(nseq);
   void* args[] = {&cu_seqlens, &n, &T, &pos_out};
   const hipError_t err =

@@ -1,0 +1,75 @@
+// float64 sine and cosine of a rotary angle, for 0 <= x < 2^31.
+//
+// The rotary angle is position * inv_freq with position < 2^31 and
+// inv_freq <= 1, so a three-part Cody-Waite reduction by pi/2 is exact
+// enough over the whole range (W. J. Cody and W. Waite, "Software Manual for
+// the Elementary Functions", 1980: subtract k*(P1 + P2 + P3) with the leading
+// parts short enough that k*P1 and k*P2 are exact products).  Here
+// P1 and P2 carry 21 significant bits of pi/2 each (k < 2^31 has at most 31
+// bits, so k*P1 and k*P2 fit in 52 bits), P3 the next 53 bits; what is left
+// of pi/2 after them is below 1e-31, i.e. below 2^-71 after multiplying by k.
+// The reduced argument r lies in [-pi/4, pi/4] (up to rounding of k) and is
+// accurate to a few units of 2^-54 in absolute terms.  sin r and cos r are
+// the Taylor series through r^19 and r^20 (first omitted terms below 1e-21
+// on |r| <= 0.8), evaluated by Horner's rule with fused multiply-adds; the
+// coefficients are 1/n! rounded to float64.  The constants were derived from
+// pi and n! directly (mpmath at 400 bits).
+//
+// Exact at x = 0: sin 0 = 0 and cos 0 = 1, so position 0 is the identity.
+// Usable from device code and from a host C or C++ compiler (for CPU checks).
+
+#ifndef ROPE_SINCOS_H
+#define ROPE_SINCOS_H
+
+#include <math.h>
+
+#if defined(__HIPCC__)
+#define ROPE_HD __host__ __device__ __forceinline__
+#else
+#define ROPE_HD static inline
+#endif
+
+ROPE_HD void rope_sincos(double x, double* s_out, double* c_out) {
+  const double kTwoOverPi = 0x1.45f306dc9c883p-1;
+  const double kP1 = 0x1.921fb00000000p+0;   // pi/2, leading 21 bits
+  const double kP2 = 0x1.5110b00000000p-22;  // next 21 bits
+  const double kP3 = 0x1.18469898cc517p-44;  // next 53 bits
+  const double k = rint(x * kTwoOverPi);
+  double r = fma(-k, kP1, x);  // exact
+  r = fma(-k, kP2, r);         // exact product, one rounding
+  r = fma(-k, kP3, r);
+  const double z = r * r;
+  // sin r = r (1 - z/3! + z^2/5! - ... - z^9/19!)
+  double ps = -0x1.2f49b46814157p-57;             // -1/19!
+  ps = fma(ps, z, 0x1.952c77030ad4ap-49);         // +1/17!
+  ps = fma(ps, z, -0x1.ae7f3e733b81fp-41);        // -1/15!
+  ps = fma(ps, z, 0x1.6124613a86d09p-33);         // +1/13!
+  ps = fma(ps, z, -0x1.ae64567f544e4p-26);        // -1/11!
+  ps = fma(ps, z, 0x1.71de3a556c734p-19);         // +1/9!
+  ps = fma(ps, z, -0x1.a01a01a01a01ap-13);        // -1/7!
+  ps = fma(ps, z, 0x1.1111111111111p-7);          // +1/5!
+  ps = fma(ps, z, -0x1.5555555555555p-3);         // -1/3!
+  const double sr = fma(ps * z, r, r);
+  // cos r = 1 - z/2! + z^2/4! - ... + z^10/20!
+  double pc = 0x1.e542ba4020225p-62;              // +1/20!
+  pc = fma(pc, z, -0x1.6827863b97d97p-53);        // -1/18!
+  pc = fma(pc, z, 0x1.ae7f3e733b81fp-45);         // +1/16!
+  pc = fma(pc, z, -0x1.93974a8c07c9dp-37);        // -1/14!
+  pc = fma(pc, z, 0x1.1eed8eff8d898p-29);         // +1/12!
+  pc = fma(pc, z, -0x1.27e4fb7789f5cp-22);        // -1/10!
+  pc = fma(pc, z, 0x1.a01a01a01a01ap-16);         // +1/8!
+  pc = fma(pc, z, -0x1.6c16c16c16c17p-10);        // -1/6!
+  pc = fma(pc, z, 0x1.5555555555555p-5);          // +1/4!
+  pc = fma(pc, z, -0.5);                          // -1/2!
+  const double cr = fma(pc, z, 1.0);
+  // x = k pi/2 + r: rotate (cos r, sin r) by the quadrant k mod 4
+  const int q = (int)((long long)k & 3);
+  const double s = (q & 1) ? cr : sr;
+  const double c = (q & 1) ? sr : cr;
+  *s_out = (q & 2) ? -s : s;
+  *c_out = ((q + 1) & 2) ? -c : c;
+}
+
+#undef ROPE_HD
+
+#endif  // ROPE_SINCOS_H
