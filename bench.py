@@ -10,9 +10,11 @@ cold HBM rather than the 256 MB Infinity Cache.
 
 Prints ONE JSON line on stdout (progress goes to stderr) with:
   value        tokens/s of the whole step (fwd + bwd), wall clock over K steps
+               (replayed as one HIP graph unless --no-graph)
   roofline     the rotation kernel's achieved HBM bandwidth: algorithmic bytes
                per launch (read + write of q and k) / mean launch duration,
-               from HIP events recorded around every launch on its stream,
+               from HIP events bracketing the K steps (2 launches each) on the
+               launch stream,
                against MI355X's 8 TB/s; `traffic` is the measured HBM bytes per
                launch from committed rocprofv3 counters when they were taken
                on the current kernel source, else null
@@ -121,7 +123,6 @@ def cpu_baseline(w, budget_s: float = 12.0, chunk: int = 1024):
 # ---------------------------------------------------------------------------
 
 def run_gpu(args):
-    import numpy as np
     import torch
 
     import packed_varlen_rotary_amd as P
@@ -133,62 +134,65 @@ def run_gpu(args):
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     cu = torch.as_tensor(w.cu_seqlens, device=dev)
-    set_bytes = w.bytes_per_pass  # q, k, dq, dk of one batch: (Hq+Hkv)*D*s*T bytes each pair
+    set_bytes = w.bytes_per_pass  # q, k, dq, dk of one batch: (Hq+Hkv)*D*s*T bytes per pair
     nsets = max(1, min(64, -(-(1 << 30) // set_bytes)))
     log(f"[bench] {w.name}: {nsets} resident batches of {set_bytes / 2**20:.1f} MiB")
     sets = [W.make_tensors(w, ("q", "k", "dq", "dk"), device=dev, salt=s) for s in range(nsets)]
-    stream = torch.cuda.current_stream(dev)
 
-    def step(i, ev=None):
+    def step(i):
         b = sets[i % nsets]
-        if ev is not None:
-            ev[0].record(stream)
         P.rope_qk_fwd(b["q"], b["k"], cu, w.theta)
-        if ev is not None:
-            ev[1].record(stream)
-            ev[2].record(stream)
         P.rope_qk_bwd(b["dq"], b["dk"], cu, w.theta)
-        if ev is not None:
-            ev[3].record(stream)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: K steps, HIP events around every launch on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    graph = None
+    if args.graph:
+        # the K timed steps as one HIP graph (the entry points make no host
+        # syncs and allocate nothing, so they capture as plain kernel nodes)
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            step(0)
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                step(i)
+        graph.replay()  # upload and first replay: untimed
+        torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     t_start.record(stream)
-    for i in range(args.steps):
-        step(i, evs[i])
+    if graph is not None:
+        graph.replay()
+    else:
+        for i in range(args.steps):
+            step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    bwd_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
     region_ms = t_start.elapsed_time(t_end)
 
     # parity of a fresh batch in the same run
     parity = check_parity(w, cu, dev)
 
-    launch_ms = float(np.mean(np.concatenate([fwd_ms, bwd_ms])))
+    launch_ms = region_ms / (2 * args.steps)  # HIP events around the K steps, on the launch stream
     ms_per_step = wall * 1e3 / args.steps
-    gbs = w.bytes_per_pass / (launch_ms * 1e-3) / 1e9
-    traffic = measured_traffic(w.name)
     return w, {
         "ms_per_step": ms_per_step,
         "tokens_per_s": w.T / (ms_per_step * 1e-3),
-        "event_region_ms_per_step": region_ms / args.steps,
+        "event_ms_per_step": region_ms / args.steps,
         "launch_ms": launch_ms,
-        "fwd_ms_median": float(np.median(fwd_ms)),
-        "bwd_ms_median": float(np.median(bwd_ms)),
-        "fwd_gbs": w.bytes_per_pass / (float(np.median(fwd_ms)) * 1e-3) / 1e9,
-        "bwd_gbs": w.bytes_per_pass / (float(np.median(bwd_ms)) * 1e-3) / 1e9,
-        "gbs": gbs,
-        "traffic": traffic,
+        "gbs": w.bytes_per_pass / (launch_ms * 1e-3) / 1e9,
+        "traffic": measured_traffic(w.name),
         "parity": parity,
         "resident_batches": nsets,
         "device": torch.cuda.get_device_name(dev),
@@ -255,6 +259,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="launch the timed steps one by one on the stream instead of replaying a HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of --copy-bytes (for HBM counter scaling)")
@@ -271,7 +277,7 @@ def main():
         return
 
     w, r = run_gpu(args)
-    log(f"[bench] gpu done: {r['ms_per_step']:.4f} ms/step, launch {r['launch_ms'] * 1e3:.2f} us, "
+    log(f"[bench] gpu done: {r['ms_per_step']:.4f} ms/step, mean launch {r['launch_ms'] * 1e3:.2f} us, "
         f"{r['gbs']:.0f} GB/s, parity {r['parity']}")
     cpu = None
     if args.workload and not args.no_cpu_baseline:
@@ -310,13 +316,11 @@ def main():
         "cpu_baseline": cpu,
         "kernel": {
             "name": "rope_qk_kernel",
+            "launches_per_step": 2,
             "algorithmic_bytes_per_launch": w.bytes_per_pass,
             "mean_launch_us": r["launch_ms"] * 1e3,
-            "fwd_median_us": r["fwd_ms_median"] * 1e3,
-            "bwd_median_us": r["bwd_ms_median"] * 1e3,
-            "fwd_gbs": r["fwd_gbs"],
-            "bwd_gbs": r["bwd_gbs"],
-            "event_region_ms_per_step": r["event_region_ms_per_step"],
+            "event_ms_per_step": r["event_ms_per_step"],
+            "launch": "hip graph of the K steps" if args.graph else "stream launches",
         },
         "parity": r["parity"],
         "device": r["device"],
