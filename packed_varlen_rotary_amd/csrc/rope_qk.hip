@@ -53,13 +53,14 @@ constexpr int kMaxTableBytes = 16384;  // cos/sin table per workgroup
 constexpr uint32_t kMaxTasksPerToken = 65535;
 constexpr int64_t kMaxGrid = int64_t(1) << 20;  // grid * 256 work-items stays below 2^32
 
-#ifndef ROPE_QK_TASKS_PER_THREAD
-#define ROPE_QK_TASKS_PER_THREAD 4
-#endif
-#ifndef ROPE_QK_WAVES_PER_SIMD
-#define ROPE_QK_WAVES_PER_SIMD 3
-#endif
-constexpr int kTPT = ROPE_QK_TASKS_PER_THREAD;  // 16-byte chunk pairs in flight per lane
+// Two instances of the rotation kernel, by the number of 16-byte chunk pairs
+// each lane keeps in flight: 2 (occupancy 4 waves/SIMD) or 4 (occupancy 3).
+// Tiles hold whole tokens, so a tile of 256 * tpt tasks is only partly used
+// when a token's task count does not divide it.  Measured on MI355X, the
+// 2-task instance is faster whenever its tiles are at least ~90% full
+// (e.g. 16 heads x D 64: +5-11% at every batch size), otherwise the 4-task
+// instance is (e.g. 40 heads x D 128: 62.5% full tiles, 4-task +10-18%).
+constexpr double kMinTileFill = 0.9;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -191,8 +192,8 @@ __device__ __forceinline__ void rotate_f32(const u32x4& a, const u32x4& b, const
 
 // One tile of consecutive tokens per workgroup (a grid-stride loop covers
 // launches with more tiles than the grid).
-template <int kDtype>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ROPE_QK_WAVES_PER_SIMD)))
+template <int kDtype, int kTPT, int kWavesPerSimd>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd)))
 void rope_qk_kernel(const RopeParams p) {
   constexpr int kVec = (kDtype == ROPE_QK_BF16) ? 8 : 4;  // elements per 16 bytes
   __shared__ int32_t s_pos[kMaxTileTokens];                 // positions of the tile's tokens
@@ -337,11 +338,19 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
   const int64_t tasks_per_tok = (Hq + Hkv) * chunks;
   if (tasks_per_tok > kMaxTasksPerToken) return ROPE_QK_ERR_SHAPE;
 
-  int64_t tile = static_cast<int64_t>(kThreads) * kTPT / tasks_per_tok;
-  const int64_t lds_cap = kMaxTableBytes / (half * 16);
-  if (tile > kMaxTileTokens) tile = kMaxTileTokens;
-  if (tile > lds_cap) tile = lds_cap;
-  if (tile < 1) tile = 1;
+  // tokens per tile for an instance keeping tpt tasks per lane: as many whole
+  // tokens as fill 256 * tpt task slots, within the LDS table and position caps
+  const auto tile_tokens_for = [&](int64_t tpt) {
+    int64_t tt = static_cast<int64_t>(kThreads) * tpt / tasks_per_tok;
+    const int64_t lds_cap = kMaxTableBytes / (half * 16);
+    if (tt > kMaxTileTokens) tt = kMaxTileTokens;
+    if (tt > lds_cap) tt = lds_cap;
+    return tt < 1 ? int64_t(1) : tt;
+  };
+  const int64_t tile2 = tile_tokens_for(2);
+  const bool two_per_lane =
+      tile2 * tasks_per_tok <= 2 * kThreads && tile2 * tasks_per_tok >= kMinTileFill * 2 * kThreads;
+  const int64_t tile = two_per_lane ? tile2 : tile_tokens_for(4);
 
   RopeParams p;
   p.q = static_cast<char*>(q);
@@ -369,8 +378,13 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
   const int64_t grid = p.ntiles < kMaxGrid ? p.ntiles : kMaxGrid;
   const size_t lds = static_cast<size_t>(tile * half) * sizeof(double2);
   void* args[] = {&p};
-  const void* fn = dtype == ROPE_QK_BF16 ? reinterpret_cast<const void*>(&rope_qk_kernel<ROPE_QK_BF16>)
-                                         : reinterpret_cast<const void*>(&rope_qk_kernel<ROPE_QK_FP32>);
+  const void* fn;
+  if (dtype == ROPE_QK_BF16)
+    fn = two_per_lane ? reinterpret_cast<const void*>(&rope_qk_kernel<ROPE_QK_BF16, 2, 4>)
+                     : reinterpret_cast<const void*>(&rope_qk_kernel<ROPE_QK_BF16, 4, 3>);
+  else
+    fn = two_per_lane ? reinterpret_cast<const void*>(&rope_qk_kernel<ROPE_QK_FP32, 2, 4>)
+                     : reinterpret_cast<const void*>(&rope_qk_kernel<ROPE_QK_FP32, 4, 3>);
   const hipError_t err = hipLaunchKernel(fn, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), args, lds,
                                          static_cast<hipStream_t>(stream));
   return err == hipSuccess ? ROPE_QK_OK : ROPE_QK_ERR_LAUNCH;
