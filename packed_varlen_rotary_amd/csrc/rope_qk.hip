@@ -15,21 +15,31 @@
 // Design (one launch per call, HBM-bound: every element of q and k is read
 // once and written once, ~0.75 flop per byte, so there is no MFMA here):
 //
-//  * A workgroup owns a tile of consecutive tokens (one tile per workgroup;
-//    measured on MI355X, a one-shot grid streams better than a persistent
-//    one).  The work of a tile is a flat list of "tasks"; a task is one
-//    16-byte chunk of the first half of a head together with the matching
-//    16-byte chunk of its second half (the rotate_half partner i + D/2), over
-//    the heads of q followed by those of k.  Consecutive lanes take
-//    consecutive chunks of a head, so each load/store instruction of a wave
-//    covers whole 64-128 byte runs.  Each lane keeps 4 tasks (128 bytes of
-//    loads) in flight.
-//  * First the workgroup finds each token's position -- a wave-uniform
-//    binary search over cu_seqlens through the scalar cache, then a uniform
-//    scan of the boundaries inside the tile -- and evaluates cos/sin once per
-//    (token, pair) in float64 into LDS, where all heads of q and k read them.
-//    Then it streams its q/k chunks with non-temporal loads and stores; the
-//    other workgroups resident on the CU overlap each other's phases.
+//  * The work is a flat list of tasks in (token, head of q then k, chunk)
+//    order.  Half rows of 128 bytes or more: a task is a 16-byte chunk of the
+//    first half of a head together with the chunk D/2 further on (the
+//    rotate_half partner), and one lane holds both.  Shorter half rows (1, 2
+//    or 4 chunks): a task is a single 16-byte chunk and consecutive lanes
+//    cover whole rows, so every wave-wide load and store covers whole 128-byte
+//    lines (partner halves loaded by separate instructions cost ~13% of HBM
+//    throughput on MI355X at D = 64); the partner chunk comes from the lane
+//    kG away through a DPP move.
+//  * A workgroup owns one tile of consecutive tasks (256 lanes x 2 pairs or
+//    x 4 chunks), which may begin and end inside a token, so every tile but
+//    the last is full whatever the head count.  The grid is two-dimensional
+//    rather than a grid-stride loop: a loop's second copy of the body would
+//    set the register count (and so the occupancy) of every launch.
+//  * Each lane first issues the load of its table entry's inv_freq and then
+//    all its data loads (non-temporal), and only then finds the tile's token
+//    positions -- a wave-uniform binary search of cu_seqlens through the
+//    scalar cache, whose loads are not ordered behind the data -- and
+//    evaluates cos/sin once per (token, pair) in float64 into LDS, where all
+//    heads of q and k read them.  The memory counter completes in order, so
+//    waiting for inv_freq does not wait for the data: the table is built
+//    while the tile's data is in flight.
+//  * Every task is rotated before any store is issued: a store's registers
+//    cannot be reused until it completes, so an early store would make the
+//    next task wait for a write acknowledgement.
 //  * The rotation is done in float64 and rounded once: fp32 output is the
 //    correctly rounded fp32; bf16 output is the correctly rounded bf16 (fast
 //    float64->fp32->bf16 path, and an exact re-rounding for the rare values
@@ -46,21 +56,25 @@
 
 namespace {
 
-constexpr int kThreads = 256;          // 4 wave64s per workgroup
-constexpr int kMaxHalf = 256;          // D <= 512
-constexpr int kMaxTileTokens = 64;
-constexpr int kMaxTableBytes = 16384;  // cos/sin table per workgroup
+constexpr int kThreads = 256;                         // 4 wave64s per workgroup
+constexpr int kMaxHalf = 256;                         // D <= 512
+constexpr int kMaxTileTokens = 64;                    // tokens a tile may touch
+constexpr int kMaxTableBytes = 16384;                 // cos/sin table per workgroup
+constexpr int kEnt = kMaxTableBytes / 16 / kThreads;  // table entries per thread, at most
 constexpr uint32_t kMaxTasksPerToken = 65535;
-constexpr int64_t kMaxGrid = int64_t(1) << 20;  // grid * 256 work-items stays below 2^32
+constexpr int kPairTasks = 2;                         // chunk pairs per lane (pair tiles)
+constexpr int kUnitTasks = 4;                         // chunks per lane (unit tiles)
+constexpr int64_t kGridX = 65536;                     // tiles per grid row
+constexpr int64_t kLdsPerCu = 163840;                 // MI355X: 160 KiB of LDS per compute unit
 
-// Two instances of the rotation kernel, by the number of 16-byte chunk pairs
-// each lane keeps in flight: 2 (occupancy 4 waves/SIMD) or 4 (occupancy 3).
-// Tiles hold whole tokens, so a tile of 256 * tpt tasks is only partly used
-// when a token's task count does not divide it.  Measured on MI355X, the
-// 2-task instance is faster whenever its tiles are at least ~90% full
-// (e.g. 16 heads x D 64: +5-11% at every batch size), otherwise the 4-task
-// instance is (e.g. 40 heads x D 128: 62.5% full tiles, 4-task +10-18%).
-constexpr double kMinTileFill = 0.9;
+// Resident workgroups per compute unit for pair tiles, measured on MI355X
+// (bf16, D = 128, 0.5-10 GB per launch): with 256 or more tasks per token
+// (e.g. 40 or 72 heads) 3 resident tiles stream 2-5% faster than 4-6, with
+// fewer (e.g. 16 heads) 4 are best.  Unit tiles run uncapped (5 per CU at
+// their register count); any cap costs them 2-17%.
+constexpr int kPairCapWide = 3;
+constexpr int kPairCapNarrow = 4;
+constexpr int64_t kWideTasksPerToken = 256;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -78,16 +92,18 @@ struct RopeParams {
   int64_t T;
   int64_t q_st, q_sh;      // byte strides of q along tokens / heads
   int64_t k_st, k_sh;      // byte strides of k along tokens / heads
-  int64_t ntiles;          // ceil(T / tile_tokens)
-  uint64_t magic_task;     // ceil(2^32 / tasks_per_tok)
+  uint64_t magic_tok;      // ceil(2^40 / tasks_per_tok): exact n / tasks_per_tok for n < 2^24
   uint64_t magic_chunk;    // ceil(2^32 / chunks)
+  uint64_t magic_half;     // ceil(2^32 / half)
+  double rcp_tok;          // 1 / tasks_per_tok, rounded
+  uint32_t ntiles;         // ceil(T * tasks_per_tok / tile_tasks) < 2^31
+  int32_t tile_tasks;      // consecutive tasks per tile
   int32_t nseq;
   int32_t Hq;
-  int32_t tasks_per_tok;   // (Hq + Hkv) * chunks
-  int32_t chunks;          // 16-byte chunks per half head
+  int32_t tasks_per_tok;   // (Hq + Hkv) * chunks per row for unit tiles, per half row for pair tiles
+  int32_t chunks;          // 16-byte chunks per half row
   int32_t half;            // D / 2
   int32_t half_bytes;      // (D / 2) * element size
-  int32_t tile_tokens;
   double sign;             // +1 forward, -1 backward
   double inv_freq[kMaxHalf];
 };
@@ -190,106 +206,217 @@ __device__ __forceinline__ void rotate_f32(const u32x4& a, const u32x4& b, const
   }
 }
 
-// One tile of consecutive tokens per workgroup (a grid-stride loop covers
-// launches with more tiles than the grid).
-template <int kDtype, int kTPT, int kWavesPerSimd>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd)))
-void rope_qk_kernel(const RopeParams p) {
+// Partner exchange for unit tiles: lane l receives the dword lane l ^ kG
+// holds (the 16-byte chunk D/2 further on, or back, in the same row; a row's
+// 2*kG chunks sit on 2*kG consecutive lanes).
+template <int kG>
+__device__ __forceinline__ uint32_t partner_dword(uint32_t x) {
+  if constexpr (kG == 1) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+  } else if constexpr (kG == 2) {
+    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+  } else {
+    static_assert(kG == 4, "unit tiles need a half row of 1, 2 or 4 chunks");
+    // lanes 0-3 and 8-11 of each 16-lane row take lane + 4 (row_shl:4 on banks 0, 2);
+    // lanes 4-7 and 12-15 take lane - 4 (row_shr:4 on banks 1, 3)
+    const int t = __builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x), 0x104, 0xF, 0x5, false);
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(t, static_cast<int>(x), 0x114, 0xF, 0xA, false));
+  }
+}
+
+// Rotate one 16-byte chunk of bf16 data in place of its row: own holds
+// x[m .. m+7], par the partner elements D/2 away, negated when own lies in
+// the first half, so every output is own * cos + par * sin (the same
+// float64 operations as the paired form).
+template <bool kExact>
+__device__ __forceinline__ bool rotate_unit_bf16(const u32x4& own, const u32x4& par, const double2* __restrict__ cs,
+                                                 int chunks, u32x4& out) {
+  bool tie = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const double2 c0 = cs[(2 * j) * chunks];
+    const double2 c1 = cs[(2 * j + 1) * chunks];
+    const double yl = fma(bf16_lo(own[j]), c0.x, bf16_lo(par[j]) * c0.y);
+    const double yh = fma(bf16_hi(own[j]), c1.x, bf16_hi(par[j]) * c1.y);
+    out[j] = kExact ? pack_bf16_exact(yl, yh) : pack_bf16_fast(yl, yh, tie);
+  }
+  return tie;
+}
+
+__device__ __forceinline__ void rotate_unit_f32(const u32x4& own, const u32x4& par, const double2* __restrict__ cs,
+                                                int chunks, u32x4& out) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const double2 c = cs[j * chunks];
+    const double x = static_cast<double>(__uint_as_float(own[j]));
+    const double y = static_cast<double>(__uint_as_float(par[j]));
+    out[j] = __float_as_uint(static_cast<float>(fma(x, c.x, y * c.y)));
+  }
+}
+
+// n / tasks_per_tok for n < 2^24 (m = ceil(2^40 / d), d < 2^16).
+__device__ __forceinline__ uint32_t div_tok(uint32_t n, uint64_t m) {
+  return static_cast<uint32_t>((static_cast<uint64_t>(n) * m) >> 40);
+}
+
+// One tile: tile_tasks consecutive tasks of the flat (token, head, chunk)
+// order, which may start and end inside a token.
+// kG = 0: a task is a pair of 16-byte chunks D/2 apart (one lane holds both).
+// kG = 1, 2, 4 (half rows of fewer than 128 bytes): a task is one 16-byte
+// chunk; consecutive lanes cover whole rows, so every load and store of a
+// wave covers whole cache lines, and the partner chunk comes from the lane
+// kG away.
+template <int kDtype, int kG, int kTPT>
+__device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, int32_t* s_pos, double2* s_cs) {
   constexpr int kVec = (kDtype == ROPE_QK_BF16) ? 8 : 4;  // elements per 16 bytes
-  __shared__ int32_t s_pos[kMaxTileTokens];                 // positions of the tile's tokens
-  extern __shared__ double2 s_cs[];                         // [tile_tokens * half] {cos, sign*sin}
   const int tid = threadIdx.x;
   const cu_ptr cu = (cu_ptr)p.cu;  // address-space cast (C-style: reinterpret_cast cannot change it)
   const int32_t nseq = p.nseq;
-  const int64_t cu_last = cu[nseq];
-
-  for (int64_t tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
-    const int64_t t0 = tile * p.tile_tokens;
-    const int ntok = static_cast<int>(min(static_cast<int64_t>(p.tile_tokens), p.T - t0));
+  const int32_t tpt = p.tasks_per_tok;
+  {
+    // first task n0 = t0 * tasks_per_tok + r0 (n0 < 2^42 is exact in float64;
+    // the rounded quotient is off by at most one)
+    const int64_t n0 = static_cast<int64_t>(tile) * p.tile_tasks;
+    int32_t t0i = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(static_cast<double>(n0) * p.rcp_tok));
+    int64_t r0l = n0 - static_cast<int64_t>(t0i) * tpt;
+    if (r0l < 0) { t0i -= 1; r0l += tpt; }
+    if (r0l >= tpt) { t0i += 1; r0l -= tpt; }
+    const int64_t t0 = t0i;
+    const uint32_t r0 = static_cast<uint32_t>(r0l);
+    const int64_t n_end = min(n0 + p.tile_tasks, p.T * tpt);          // one past the tile's last task
+    const int ntok = static_cast<int>(div_tok(static_cast<uint32_t>(n_end - n0) + r0 - 1, p.magic_tok)) + 1;
     const int64_t t_end = t0 + ntok;  // one past the tile's last token
-    const uint32_t ntasks = static_cast<uint32_t>(ntok) * static_cast<uint32_t>(p.tasks_per_tok);
     const int nent = ntok * p.half;
 
-    const int32_t s0 = last_start_at_or_before(cu, nseq, t0);  // scalar loads
-
-    for (uint32_t base = 0; base < ntasks; base += kThreads * kTPT) {
-      u32x4 a[kTPT], b[kTPT];
-      char* ptr[kTPT];
-      int tt_of[kTPT], c_of[kTPT];
-      bool act[kTPT];
-
-      // 1. positions and the cos/sin table (first pass of the tile only)
-      if (base == 0) {
-#pragma unroll 1
-        for (int e0 = 0; e0 < nent; e0 += kThreads) {
-          const int e = e0 + tid;
-          const bool on = e < nent;
-          const int tt = on ? e / p.half : 0;
-          const int i = e - tt * p.half;
-          const int64_t t = t0 + tt;
-          // last sequence start at or before t: the tile's first start, then
-          // any boundaries inside the tile (wave-uniform scan)
-          int64_t start = s0 >= 0 ? static_cast<int64_t>(cu[s0]) : INT64_MIN;
-          for (int32_t j = s0 + 1; j <= nseq; ++j) {
-            const int64_t v = cu[j];
-            if (v >= t_end) break;
-            start = v <= t ? v : start;
-          }
-          const int64_t pos64 = t - start;
-          const int32_t pos =
-              (start != INT64_MIN && t < cu_last && pos64 <= INT32_MAX) ? static_cast<int32_t>(pos64) : -1;
-          if (on) {
-            if (i == 0) s_pos[tt] = pos;
-            if (pos >= 0) {
-              double sn, cs;
-              rope_sincos(static_cast<double>(pos) * p.inv_freq[i], &sn, &cs);
-              s_cs[cs_slot(tt, i, kVec, p.chunks)] = make_double2(cs, p.sign * sn);
-            }
-          }
-        }
-        __syncthreads();
-      }
-
-      // 2. issue every load of this pass (lanes without a task re-read task 0)
+    // 1. inv_freq of this thread's table entries.  Issued before the tile's
+    //    data: the memory counter completes in order, so the table can be
+    //    built while the data loads are still in flight.
+    double f[kEnt];
+    int tt_e[kEnt], i_e[kEnt];
 #pragma unroll
-      for (int u = 0; u < kTPT; ++u) {
-        const uint32_t n_raw = base + static_cast<uint32_t>(tid + u * kThreads);
-        act[u] = n_raw < ntasks;
-        const uint32_t n = act[u] ? n_raw : 0u;
-        const uint32_t tt = div_small(n, p.magic_task);
-        const uint32_t r = n - tt * static_cast<uint32_t>(p.tasks_per_tok);
-        const uint32_t h = div_small(r, p.magic_chunk);
-        const uint32_t c = r - h * static_cast<uint32_t>(p.chunks);
-        const int64_t t = t0 + tt;
-        const bool is_q = static_cast<int32_t>(h) < p.Hq;
-        char* row = is_q ? p.q + t * p.q_st + static_cast<int64_t>(h) * p.q_sh
-                         : p.k + t * p.k_st + static_cast<int64_t>(h - p.Hq) * p.k_sh;
-        ptr[u] = row + static_cast<int64_t>(c) * 16;
-        tt_of[u] = static_cast<int>(tt);
-        c_of[u] = static_cast<int>(c);
-        // streamed once: non-temporal, so they do not displace other data in the caches
-        a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr[u]));
-        b[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr[u] + p.half_bytes));
-      }
+    for (int v = 0; v < kEnt; ++v) {
+      const int e = tid + v * kThreads;
+      const int tt = e < nent ? static_cast<int>(div_small(static_cast<uint32_t>(e), p.magic_half)) : 0;
+      tt_e[v] = tt;
+      i_e[v] = e < nent ? e - tt * p.half : 0;
+      f[v] = (v == 0 || v * kThreads < nent) ? p.inv_freq[i_e[v]] : 0.0;
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
-      // 3. rotate and store; tokens outside every sequence are left untouched
+    // 2. every load of the tile (lanes past the last token re-read the tile's first task)
+    u32x4 a[kTPT], b[kTPT];
+    char* ptr[kTPT];
+    int tt_of[kTPT], c_of[kTPT];
+    bool act[kTPT], first[kTPT];
 #pragma unroll
-      for (int u = 0; u < kTPT; ++u) {
-        if (!act[u] || s_pos[tt_of[u]] < 0) continue;
-        const double2* cs = s_cs + tt_of[u] * kVec * p.chunks + c_of[u];
-        u32x4 oa, ob;
-        if constexpr (kDtype == ROPE_QK_BF16) {
-          if (rotate_bf16<false>(a[u], b[u], cs, p.chunks, oa, ob))
-            rotate_bf16<true>(a[u], b[u], cs, p.chunks, oa, ob);
-        } else {
-          rotate_f32(a[u], b[u], cs, p.chunks, oa, ob);
+    for (int u = 0; u < kTPT; ++u) {
+      const uint32_t l_raw = r0 + static_cast<uint32_t>(tid + u * kThreads);  // task index from the tile's first token
+      act[u] = n0 + static_cast<int64_t>(tid + u * kThreads) < n_end;
+      const uint32_t l = act[u] ? l_raw : r0;
+      const uint32_t tt = div_tok(l, p.magic_tok);
+      const uint32_t r = l - tt * static_cast<uint32_t>(tpt);
+      uint32_t h, c, cc;  // head, chunk within the row, chunk within the half row
+      if constexpr (kG == 0) {
+        h = div_small(r, p.magic_chunk);
+        c = r - h * static_cast<uint32_t>(p.chunks);
+        cc = c;
+      } else {
+        h = r / (2 * kG);
+        c = r % (2 * kG);
+        cc = c % kG;
+      }
+      const int64_t t = t0 + tt;
+      const bool is_q = static_cast<int32_t>(h) < p.Hq;
+      char* row = is_q ? p.q + t * p.q_st + static_cast<int64_t>(h) * p.q_sh
+                       : p.k + t * p.k_st + static_cast<int64_t>(h - p.Hq) * p.k_sh;
+      ptr[u] = row + static_cast<int64_t>(c) * 16;
+      tt_of[u] = static_cast<int>(tt);
+      c_of[u] = static_cast<int>(cc);
+      first[u] = c < static_cast<uint32_t>(kG);
+      // streamed once: non-temporal, so they do not displace other data in the caches
+      a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr[u]));
+      if constexpr (kG == 0) b[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr[u] + p.half_bytes));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3. positions (scalar loads, not ordered behind the data) and the table
+    const int32_t s0 = last_start_at_or_before(cu, nseq, t0);
+    const int64_t cu_last = cu[nseq];
+    int64_t start[kEnt];
+#pragma unroll
+    for (int v = 0; v < kEnt; ++v) start[v] = s0 >= 0 ? static_cast<int64_t>(cu[s0]) : INT64_MIN;
+    for (int32_t j = s0 + 1; j <= nseq; ++j) {  // boundaries inside the tile (wave-uniform)
+      const int64_t cv = cu[j];
+      if (cv >= t_end) break;
+#pragma unroll
+      for (int v = 0; v < kEnt; ++v) start[v] = cv <= t0 + tt_e[v] ? cv : start[v];
+    }
+#pragma unroll
+    for (int v = 0; v < kEnt; ++v) {
+      if (v > 0 && v * kThreads >= nent) break;
+      const int e = tid + v * kThreads;
+      const int64_t t = t0 + tt_e[v];
+      const int64_t pos64 = t - start[v];
+      const int32_t pos =
+          (start[v] != INT64_MIN && t < cu_last && pos64 <= INT32_MAX) ? static_cast<int32_t>(pos64) : -1;
+      if (e < nent) {
+        if (i_e[v] == 0) s_pos[tt_e[v]] = pos;
+        if (pos >= 0) {
+          double sn, cs;
+          rope_sincos(static_cast<double>(pos) * f[v], &sn, &cs);
+          s_cs[cs_slot(tt_e[v], i_e[v], kVec, p.chunks)] = make_double2(cs, p.sign * sn);
         }
-        __builtin_nontemporal_store(oa, reinterpret_cast<u32x4*>(ptr[u]));
-        __builtin_nontemporal_store(ob, reinterpret_cast<u32x4*>(ptr[u] + p.half_bytes));
       }
     }
-    __syncthreads();  // a further tile of this workgroup rewrites s_pos and s_cs
+    __syncthreads();
+
+    // 4. rotate every task, then store them all; tokens outside every
+    //    sequence are left untouched
+    bool st[kTPT];
+    u32x4 oa[kTPT], ob[kTPT];
+#pragma unroll
+    for (int u = 0; u < kTPT; ++u) {
+      st[u] = act[u] && s_pos[tt_of[u]] >= 0;
+      const int chunks = kG == 0 ? p.chunks : kG;
+      const double2* cs = s_cs + tt_of[u] * kVec * chunks + c_of[u];
+      if constexpr (kG == 0) {
+        if constexpr (kDtype == ROPE_QK_BF16) {
+          if (rotate_bf16<false>(a[u], b[u], cs, chunks, oa[u], ob[u]))
+            rotate_bf16<true>(a[u], b[u], cs, chunks, oa[u], ob[u]);
+        } else {
+          rotate_f32(a[u], b[u], cs, chunks, oa[u], ob[u]);
+        }
+      } else {
+        // partner chunk from the lane kG away; negated when this chunk is in the first half
+        const uint32_t neg = first[u] ? (kDtype == ROPE_QK_BF16 ? 0x80008000u : 0x80000000u) : 0u;
+        u32x4 par;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) par[d] = partner_dword<kG>(a[u][d]) ^ neg;
+        if constexpr (kDtype == ROPE_QK_BF16) {
+          if (rotate_unit_bf16<false>(a[u], par, cs, chunks, oa[u]))
+            rotate_unit_bf16<true>(a[u], par, cs, chunks, oa[u]);
+        } else {
+          rotate_unit_f32(a[u], par, cs, chunks, oa[u]);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kTPT; ++u) {
+      if (!st[u]) continue;
+      __builtin_nontemporal_store(oa[u], reinterpret_cast<u32x4*>(ptr[u]));
+      if constexpr (kG == 0) __builtin_nontemporal_store(ob[u], reinterpret_cast<u32x4*>(ptr[u] + p.half_bytes));
+    }
   }
+}
+
+// One tile per workgroup; the grid's rows cover launches of more than kGridX tiles.
+template <int kDtype, int kG, int kTPT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void rope_qk_kernel(const RopeParams p) {
+  __shared__ int32_t s_pos[kMaxTileTokens];  // positions of the tile's tokens
+  extern __shared__ double2 s_cs[];          // [tokens touched * half] {cos, sign*sin}
+  const uint32_t tile = blockIdx.y * gridDim.x + blockIdx.x;
+  if (tile < p.ntiles) rope_tile<kDtype, kG, kTPT>(p, tile, s_pos, s_cs);
 }
 
 __global__ __launch_bounds__(kThreads) void rope_positions_kernel(const int32_t* __restrict__ cu_seqlens,
@@ -335,22 +462,21 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
     return ROPE_QK_ERR_ALIGN;
 
   const int64_t chunks = half * esz / 16;
-  const int64_t tasks_per_tok = (Hq + Hkv) * chunks;
+  // half rows of 1, 2 or 4 chunks: unit tiles (one chunk per task, partner by lane exchange)
+  const int unit_g = (chunks == 1 || chunks == 2 || chunks == 4) ? static_cast<int>(chunks) : 0;
+  const int64_t tasks_per_tok = (Hq + Hkv) * (unit_g ? 2 * chunks : chunks);
   if (tasks_per_tok > kMaxTasksPerToken) return ROPE_QK_ERR_SHAPE;
 
-  // tokens per tile for an instance keeping tpt tasks per lane: as many whole
-  // tokens as fill 256 * tpt task slots, within the LDS table and position caps
-  const auto tile_tokens_for = [&](int64_t tpt) {
-    int64_t tt = static_cast<int64_t>(kThreads) * tpt / tasks_per_tok;
-    const int64_t lds_cap = kMaxTableBytes / (half * 16);
-    if (tt > kMaxTileTokens) tt = kMaxTileTokens;
-    if (tt > lds_cap) tt = lds_cap;
-    return tt < 1 ? int64_t(1) : tt;
-  };
-  const int64_t tile2 = tile_tokens_for(2);
-  const bool two_per_lane =
-      tile2 * tasks_per_tok <= 2 * kThreads && tile2 * tasks_per_tok >= kMinTileFill * 2 * kThreads;
-  const int64_t tile = two_per_lane ? tile2 : tile_tokens_for(4);
+  // a tile touches at most cap_tokens tokens, so its table and positions fit in LDS
+  int64_t cap_tokens = kMaxTableBytes / (half * 16);
+  if (cap_tokens > kMaxTileTokens) cap_tokens = kMaxTileTokens;
+  int64_t tile_tasks = int64_t(kThreads) * (unit_g ? kUnitTasks : kPairTasks);
+  if (tile_tasks > (cap_tokens - 1) * tasks_per_tok) tile_tasks = (cap_tokens - 1) * tasks_per_tok;
+  // tokens one tile touches: exactly tile_tasks / tasks_per_tok when every tile starts on a token
+  const int64_t span = tile_tasks % tasks_per_tok == 0 ? tile_tasks / tasks_per_tok
+                                                      : (tasks_per_tok + tile_tasks - 2) / tasks_per_tok + 1;
+  const int64_t ntiles = (T * tasks_per_tok + tile_tasks - 1) / tile_tasks;
+  if (ntiles > INT32_MAX) return ROPE_QK_ERR_SHAPE;
 
   RopeParams p;
   p.q = static_cast<char*>(q);
@@ -361,32 +487,49 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
   p.q_sh = q_sh * esz;
   p.k_st = k_st * esz;
   p.k_sh = k_sh * esz;
-  p.ntiles = (T + tile - 1) / tile;
-  p.magic_task = ((uint64_t(1) << 32) + tasks_per_tok - 1) / tasks_per_tok;
+  p.magic_tok = ((uint64_t(1) << 40) + tasks_per_tok - 1) / tasks_per_tok;
   p.magic_chunk = ((uint64_t(1) << 32) + chunks - 1) / chunks;
+  p.magic_half = ((uint64_t(1) << 32) + half - 1) / half;
+  p.rcp_tok = 1.0 / static_cast<double>(tasks_per_tok);
+  p.ntiles = static_cast<uint32_t>(ntiles);
+  p.tile_tasks = static_cast<int32_t>(tile_tasks);
   p.nseq = static_cast<int32_t>(nseq);
   p.Hq = static_cast<int32_t>(Hq);
   p.tasks_per_tok = static_cast<int32_t>(tasks_per_tok);
   p.chunks = static_cast<int32_t>(chunks);
   p.half = static_cast<int32_t>(half);
   p.half_bytes = static_cast<int32_t>(half * esz);
-  p.tile_tokens = static_cast<int32_t>(tile);
   p.sign = sign;
   for (int64_t i = 0; i < kMaxHalf; ++i)
     p.inv_freq[i] = i < half ? pow(theta, -static_cast<double>(2 * i) / static_cast<double>(D)) : 0.0;
 
-  const int64_t grid = p.ntiles < kMaxGrid ? p.ntiles : kMaxGrid;
-  const size_t lds = static_cast<size_t>(tile * half) * sizeof(double2);
-  void* args[] = {&p};
+  // LDS: the table of the tokens one tile touches; for pair tiles, padded so
+  // that at most the measured best number of workgroups share a compute unit
+  size_t lds = static_cast<size_t>(span * half) * sizeof(double2);
+  if (!unit_g) {
+    const int64_t cap = tasks_per_tok >= kWideTasksPerToken ? kPairCapWide : kPairCapNarrow;
+    const size_t pad = static_cast<size_t>(kLdsPerCu / (cap + 1) + 1024 - kMaxTileTokens * sizeof(int32_t));
+    if (lds < pad) lds = pad;
+  }
+  const int64_t gx = ntiles < kGridX ? ntiles : kGridX;
+  const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>((ntiles + gx - 1) / gx));
+
   const void* fn;
-  if (dtype == ROPE_QK_BF16)
-    fn = two_per_lane ? reinterpret_cast<const void*>(&rope_qk_kernel<ROPE_QK_BF16, 2, 4>)
-                     : reinterpret_cast<const void*>(&rope_qk_kernel<ROPE_QK_BF16, 4, 3>);
-  else
-    fn = two_per_lane ? reinterpret_cast<const void*>(&rope_qk_kernel<ROPE_QK_FP32, 2, 4>)
-                     : reinterpret_cast<const void*>(&rope_qk_kernel<ROPE_QK_FP32, 4, 3>);
-  const hipError_t err = hipLaunchKernel(fn, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), args, lds,
-                                         static_cast<hipStream_t>(stream));
+#define ROPE_FN(DT, G, TPT) reinterpret_cast<const void*>(&rope_qk_kernel<DT, G, TPT>)
+  if (dtype == ROPE_QK_BF16) {
+    fn = unit_g == 1   ? ROPE_FN(ROPE_QK_BF16, 1, kUnitTasks)
+         : unit_g == 2 ? ROPE_FN(ROPE_QK_BF16, 2, kUnitTasks)
+         : unit_g == 4 ? ROPE_FN(ROPE_QK_BF16, 4, kUnitTasks)
+                       : ROPE_FN(ROPE_QK_BF16, 0, kPairTasks);
+  } else {
+    fn = unit_g == 1   ? ROPE_FN(ROPE_QK_FP32, 1, kUnitTasks)
+         : unit_g == 2 ? ROPE_FN(ROPE_QK_FP32, 2, kUnitTasks)
+         : unit_g == 4 ? ROPE_FN(ROPE_QK_FP32, 4, kUnitTasks)
+                       : ROPE_FN(ROPE_QK_FP32, 0, kPairTasks);
+  }
+#undef ROPE_FN
+  void* args[] = {&p};
+  const hipError_t err = hipLaunchKernel(fn, grid, dim3(kThreads), args, lds, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? ROPE_QK_OK : ROPE_QK_ERR_LAUNCH;
 }
 

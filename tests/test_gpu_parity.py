@@ -130,6 +130,10 @@ SHAPES = [
     (64, 2, 2, 256, "bf16", [0, 10, 64]),
     (33, 4, 2, 512, "bf16", [0, 33]),
     (130, 128, 16, 128, "bf16", [0, 60, 130]),  # more than one pass of tasks per token
+    (513, 7, 1, 32, "bf16", [0, 100, 513]),  # half row of 2 chunks: chunk tasks, partner 2 lanes away
+    (129, 2, 2, 48, "bf16", [0, 64, 129]),  # 3 chunks per half row: chunk-pair tasks
+    (300, 5, 3, 32, "fp32", [0, 17, 300]),  # fp32 half row of 4 chunks
+    (77, 3, 2, 16, "fp32", [0, 77]),  # fp32 half row of 2 chunks
     (1000, 6, 2, 8, "fp32", [0, 999, 1000]),
     (511, 9, 1, 136, "fp32", [3, 200, 480]),
     (40, 1, 1, 2 * 4, "fp32", [0, 40]),
@@ -174,6 +178,22 @@ def test_head_major_view_in_place():
     torch.cuda.synchronize()
     check_against(q, oracle.rope(xq, cu, 1e6, 1), "q head-major")
     check_against(k, oracle.rope(xk, cu, 1e6, 1), "k head-major")
+
+
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+def test_rows_off_cache_line(D):
+    """Rows that start 16 bytes past a 128-byte line (a fused buffer with an odd offset)."""
+    T, Hq, Hkv = 203, 5, 3
+    raw = W.randn((T * (Hq + Hkv) * D + 8,), "bf16", seed=D, device=DEV)
+    qk = raw[8:].view(T, Hq + Hkv, D)
+    q, k = qk[:, :Hq], qk[:, Hq:]
+    assert q.data_ptr() % 128 == 16
+    xq, xk = f64(q), f64(k)
+    cu = [0, 1, 90, 203]
+    run(1, q, k, cu, 1e4)
+    torch.cuda.synchronize()
+    check_against(q, oracle.rope(xq, cu, 1e4, 1), f"q D{D}")
+    check_against(k, oracle.rope(xk, cu, 1e4, 1), f"k D{D}")
 
 
 def test_no_kv_heads():
