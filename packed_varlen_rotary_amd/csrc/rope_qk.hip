@@ -84,6 +84,10 @@ typedef double f64x2 __attribute__((ext_vector_type(2)));
 // address space these become scalar loads, which the vector-memory counter
 // does not order behind the tile's in-flight HBM loads.
 typedef const __attribute__((address_space(4))) int32_t* cu_ptr;
+// q and k rows: explicitly global, so every load and store is a global_* (not
+// flat) instruction, which the scalar-memory counter does not track.
+typedef __attribute__((address_space(1))) char gchar;
+typedef __attribute__((address_space(1))) u32x4 gu32x4;
 
 struct RopeParams {
   char* q;                 // base of q (bytes)
@@ -97,6 +101,7 @@ struct RopeParams {
   uint64_t magic_half;     // ceil(2^32 / half)
   double rcp_tok;          // 1 / tasks_per_tok, rounded
   uint32_t ntiles;         // ceil(T * tasks_per_tok / tile_tasks) < 2^31
+  uint32_t tok_step;       // unit tiles: 256 / tasks_per_tok when that is exact, else 0
   int32_t tile_tasks;      // consecutive tasks per tile
   int32_t nseq;
   int32_t Hq;
@@ -208,20 +213,14 @@ __device__ __forceinline__ void rotate_f32(const u32x4& a, const u32x4& b, const
 
 // Partner exchange for unit tiles: lane l receives the dword lane l ^ kG
 // holds (the 16-byte chunk D/2 further on, or back, in the same row; a row's
-// 2*kG chunks sit on 2*kG consecutive lanes).
+// 2*kG chunks sit on 2*kG consecutive lanes).  ds_swizzle in bit-mask mode
+// (and-mask 31, xor-mask kG, within each 32-lane half) moves it through the
+// LDS crossbar, leaving the vector ALU to the rotation.
 template <int kG>
 __device__ __forceinline__ uint32_t partner_dword(uint32_t x) {
-  if constexpr (kG == 1) {
-    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
-  } else if constexpr (kG == 2) {
-    return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(x), 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
-  } else {
-    static_assert(kG == 4, "unit tiles need a half row of 1, 2 or 4 chunks");
-    // lanes 0-3 and 8-11 of each 16-lane row take lane + 4 (row_shl:4 on banks 0, 2);
-    // lanes 4-7 and 12-15 take lane - 4 (row_shr:4 on banks 1, 3)
-    const int t = __builtin_amdgcn_update_dpp(static_cast<int>(x), static_cast<int>(x), 0x104, 0xF, 0x5, false);
-    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(t, static_cast<int>(x), 0x114, 0xF, 0xA, false));
-  }
+  static_assert(kG == 1 || kG == 2 || kG == 4, "unit tiles need a half row of 1, 2 or 4 chunks");
+  constexpr int kPattern = (kG << 10) | 0x1F;
+  return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(x), kPattern));
 }
 
 // Rotate one 16-byte chunk of bf16 data in place of its row: own holds
@@ -305,37 +304,51 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
 
     // 2. every load of the tile (lanes past the last token re-read the tile's first task)
     u32x4 a[kTPT], b[kTPT];
-    char* ptr[kTPT];
+    gchar* ptr[kTPT];
     int tt_of[kTPT], c_of[kTPT];
     bool act[kTPT], first[kTPT];
+    // Unit tiles whose token task count divides 256 (e.g. 16 heads at D = 64):
+    // a lane's tasks are tok_step tokens apart at the same head and chunk, so
+    // only the first address needs the general computation.
+    const bool stepped = kG != 0 && p.tok_step != 0;  // wave-uniform
+    bool is_q0 = false;
 #pragma unroll
     for (int u = 0; u < kTPT; ++u) {
-      const uint32_t l_raw = r0 + static_cast<uint32_t>(tid + u * kThreads);  // task index from the tile's first token
       act[u] = n0 + static_cast<int64_t>(tid + u * kThreads) < n_end;
-      const uint32_t l = act[u] ? l_raw : r0;
-      const uint32_t tt = div_tok(l, p.magic_tok);
-      const uint32_t r = l - tt * static_cast<uint32_t>(tpt);
-      uint32_t h, c, cc;  // head, chunk within the row, chunk within the half row
-      if constexpr (kG == 0) {
-        h = div_small(r, p.magic_chunk);
-        c = r - h * static_cast<uint32_t>(p.chunks);
-        cc = c;
+      if (stepped && u > 0) {
+        const int64_t step = static_cast<int64_t>(u * p.tok_step) * (is_q0 ? p.q_st : p.k_st);
+        ptr[u] = ptr[0] + (act[u] ? step : int64_t(0));  // offset select keeps the global address space
+        tt_of[u] = act[u] ? tt_of[0] + u * static_cast<int>(p.tok_step) : tt_of[0];
+        c_of[u] = c_of[0];
+        first[u] = first[0];
       } else {
-        h = r / (2 * kG);
-        c = r % (2 * kG);
-        cc = c % kG;
+        const uint32_t l_raw = r0 + static_cast<uint32_t>(tid + u * kThreads);  // task index from the tile's first token
+        const uint32_t l = act[u] ? l_raw : r0;
+        const uint32_t tt = div_tok(l, p.magic_tok);
+        const uint32_t r = l - tt * static_cast<uint32_t>(tpt);
+        uint32_t h, c, cc;  // head, chunk within the row, chunk within the half row
+        if constexpr (kG == 0) {
+          h = div_small(r, p.magic_chunk);
+          c = r - h * static_cast<uint32_t>(p.chunks);
+          cc = c;
+        } else {
+          h = r / (2 * kG);
+          c = r % (2 * kG);
+          cc = c % kG;
+        }
+        const int64_t t = t0 + tt;
+        const bool is_q = static_cast<int32_t>(h) < p.Hq;
+        if (u == 0) is_q0 = is_q;
+        gchar* row = is_q ? (gchar*)p.q + t * p.q_st + static_cast<int64_t>(h) * p.q_sh
+                          : (gchar*)p.k + t * p.k_st + static_cast<int64_t>(h - p.Hq) * p.k_sh;
+        ptr[u] = row + static_cast<int64_t>(c) * 16;
+        tt_of[u] = static_cast<int>(tt);
+        c_of[u] = static_cast<int>(cc);
+        first[u] = c < static_cast<uint32_t>(kG);
       }
-      const int64_t t = t0 + tt;
-      const bool is_q = static_cast<int32_t>(h) < p.Hq;
-      char* row = is_q ? p.q + t * p.q_st + static_cast<int64_t>(h) * p.q_sh
-                       : p.k + t * p.k_st + static_cast<int64_t>(h - p.Hq) * p.k_sh;
-      ptr[u] = row + static_cast<int64_t>(c) * 16;
-      tt_of[u] = static_cast<int>(tt);
-      c_of[u] = static_cast<int>(cc);
-      first[u] = c < static_cast<uint32_t>(kG);
       // streamed once: non-temporal, so they do not displace other data in the caches
-      a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr[u]));
-      if constexpr (kG == 0) b[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr[u] + p.half_bytes));
+      a[u] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4*>(ptr[u]));
+      if constexpr (kG == 0) b[u] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4*>(ptr[u] + p.half_bytes));
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -403,8 +416,8 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
 #pragma unroll
     for (int u = 0; u < kTPT; ++u) {
       if (!st[u]) continue;
-      __builtin_nontemporal_store(oa[u], reinterpret_cast<u32x4*>(ptr[u]));
-      if constexpr (kG == 0) __builtin_nontemporal_store(ob[u], reinterpret_cast<u32x4*>(ptr[u] + p.half_bytes));
+      __builtin_nontemporal_store(oa[u], reinterpret_cast<gu32x4*>(ptr[u]));
+      if constexpr (kG == 0) __builtin_nontemporal_store(ob[u], reinterpret_cast<gu32x4*>(ptr[u] + p.half_bytes));
     }
   }
 }
@@ -490,6 +503,7 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
   p.magic_tok = ((uint64_t(1) << 40) + tasks_per_tok - 1) / tasks_per_tok;
   p.magic_chunk = ((uint64_t(1) << 32) + chunks - 1) / chunks;
   p.magic_half = ((uint64_t(1) << 32) + half - 1) / half;
+  p.tok_step = unit_g && kThreads % tasks_per_tok == 0 ? static_cast<uint32_t>(kThreads / tasks_per_tok) : 0u;
   p.rcp_tok = 1.0 / static_cast<double>(tasks_per_tok);
   p.ntiles = static_cast<uint32_t>(ntiles);
   p.tile_tasks = static_cast<int32_t>(tile_tasks);
