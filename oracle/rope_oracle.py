@@ -35,6 +35,25 @@ to the incoming gradients.
 Everything is numpy float64, one operation at a time, no blocking or fusion.
 Reduced-precision outputs are produced by exact round-to-nearest-even of the
 float64 result (``bf16_rne``), a single rounding.
+
+Variants (``rope`` keyword arguments; the defaults give the formula above):
+
+* ``pos_offset``: added to the positions of the first packed segment, i.e.
+  the global position of the first token of a shard that starts inside a
+  sequence.  The pages' "positions restart per sequence" rule is kept for
+  every later segment.  Not on the pages; the plainest reading of sharding
+  one long sequence over tokens.
+* ``rotary_dim`` r < D: only elements [0, r) of each head are rotated, with
+  the frequencies of a head of size r; elements [r, D) are left as they are.
+* ``pairing="interleaved"``: element 2i pairs with 2i + 1 -- RoFormer's
+  block-diagonal matrix taken literally, with no reordering of the head.
+* ``scaling``: the Llama 3.1 frequency rescaling (the pages name Llama 3.1
+  among the supported models but do not give the rule; it is restated here
+  from the model family's published definition): frequencies whose
+  wavelength 2 pi / f is shorter than ``original_max_position /
+  high_freq_factor`` are kept, those longer than ``original_max_position /
+  low_freq_factor`` are divided by ``factor``, and those in between are
+  blended linearly in ``original_max_position / wavelength``.
 """
 
 from __future__ import annotations
@@ -44,8 +63,11 @@ import numpy as np
 __all__ = [
     "segment_positions",
     "inv_freq",
+    "llama3_inv_freq",
     "cos_sin",
     "rotate",
+    "rotate_interleaved",
+    "cos_sin_freq",
     "rope",
     "rope_qk",
     "bf16_rne",
@@ -64,7 +86,7 @@ def _check_cu(cu_seqlens, T: int) -> np.ndarray:
     return cu
 
 
-def segment_positions(cu_seqlens, T: int) -> np.ndarray:
+def segment_positions(cu_seqlens, T: int, pos_offset: int = 0) -> np.ndarray:
     """Position of each of the T tokens inside its own packed sequence.
 
     Follows the auto-packing paragraph of the Unsloth article on
@@ -75,14 +97,19 @@ def segment_positions(cu_seqlens, T: int) -> np.ndarray:
 
     Built by repeating each segment's start offset over its length (no
     search), so it is a different construction from a binary search.
+    ``pos_offset`` is added to the positions of segment 0 only.
     """
     cu = _check_cu(cu_seqlens, T)
+    if pos_offset < 0:
+        raise ValueError("pos_offset must be >= 0")
     pos = np.full(T, -1, dtype=np.int64)
     lengths = np.diff(cu)
     starts = cu[:-1]
     first, last = int(cu[0]), int(cu[-1])
     token = np.arange(first, last, dtype=np.int64)
     pos[first:last] = token - np.repeat(starts, lengths)
+    if cu.size > 1:
+        pos[int(cu[0]):int(cu[1])] += pos_offset
     return pos
 
 
@@ -101,6 +128,33 @@ def inv_freq(theta: float, D: int) -> np.ndarray:
     return np.power(np.float64(theta), -(2.0 * i) / np.float64(D))
 
 
+def llama3_inv_freq(theta: float, D: int, factor: float, low_freq_factor: float, high_freq_factor: float,
+                    original_max_position: float) -> np.ndarray:
+    """Llama 3.1 rescaling of ``inv_freq(theta, D)``, one frequency at a time.
+
+    With L = original_max_position, wavelength w = 2 pi / f:
+    w < L / high_freq_factor: f is kept; w > L / low_freq_factor: f / factor;
+    otherwise, with s = (L / w - low_freq_factor) / (high_freq_factor - low_freq_factor),
+    (1 - s) f / factor + s f.
+    """
+    if not (factor > 0 and original_max_position > 0 and high_freq_factor > low_freq_factor > 0):
+        raise ValueError("need factor > 0, original_max_position > 0, high_freq_factor > low_freq_factor > 0")
+    base = inv_freq(theta, D)
+    out = np.empty_like(base)
+    low_wavelen = original_max_position / low_freq_factor
+    high_wavelen = original_max_position / high_freq_factor
+    for i, f in enumerate(base):
+        w = 2.0 * np.pi / f
+        if w < high_wavelen:
+            out[i] = f
+        elif w > low_wavelen:
+            out[i] = f / factor
+        else:
+            s = (original_max_position / w - low_freq_factor) / (high_freq_factor - low_freq_factor)
+            out[i] = (1.0 - s) * f / factor + s * f
+    return out
+
+
 def cos_sin(pos: np.ndarray, theta: float, D: int, direction: int):
     """cos and (direction * sin) of pos * inv_freq, float64 [N, D/2].
 
@@ -109,8 +163,14 @@ def cos_sin(pos: np.ndarray, theta: float, D: int, direction: int):
     """
     if direction not in (1, -1):
         raise ValueError("direction must be +1 or -1")
-    f = inv_freq(theta, D)
-    ang = np.asarray(pos, dtype=np.float64)[:, None] * f[None, :]
+    return cos_sin_freq(pos, inv_freq(theta, D), direction)
+
+
+def cos_sin_freq(pos: np.ndarray, freq: np.ndarray, direction: int):
+    """cos and (direction * sin) of pos * freq for given frequencies, float64 [N, len(freq)]."""
+    if direction not in (1, -1):
+        raise ValueError("direction must be +1 or -1")
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * np.asarray(freq, dtype=np.float64)[None, :]
     return np.cos(ang), direction * np.sin(ang)
 
 
@@ -139,24 +199,60 @@ def rotate(x: np.ndarray, pos: np.ndarray, theta: float, direction: int) -> np.n
     return y
 
 
-def rope(x: np.ndarray, cu_seqlens, theta: float, direction: int) -> np.ndarray:
-    """Rotary embedding of a packed batch x[T, H, D] (float64 result).
-
-    Tokens outside [cu[0], cu[nseq]) are returned unchanged.
-    """
+def rotate_interleaved(x: np.ndarray, pos: np.ndarray, freq: np.ndarray, direction: int) -> np.ndarray:
+    """Rotate rows x[N, H, r] pairing element 2i with 2i + 1 (frequency freq[i])."""
     x = np.asarray(x, dtype=np.float64)
-    T = x.shape[0]
-    pos = segment_positions(cu_seqlens, T)
-    y = x.copy()
-    inside = pos >= 0
-    if inside.any():
-        y[inside] = rotate(x[inside], pos[inside], theta, direction)
+    N, H, r = x.shape
+    c, s = cos_sin_freq(pos, freq, direction)
+    c = c[:, None, :]
+    s = s[:, None, :]
+    x1 = x[:, :, 0::2]
+    x2 = x[:, :, 1::2]
+    y = np.empty_like(x)
+    y[:, :, 0::2] = x1 * c - x2 * s
+    y[:, :, 1::2] = x2 * c + x1 * s
     return y
 
 
-def rope_qk(q: np.ndarray, k: np.ndarray, cu_seqlens, theta: float, direction: int):
+def rope(x: np.ndarray, cu_seqlens, theta: float, direction: int, *, pos_offset: int = 0, rotary_dim=None,
+         pairing: str = "half", scaling=None) -> np.ndarray:
+    """Rotary embedding of a packed batch x[T, H, D] (float64 result).
+
+    Tokens outside [cu[0], cu[nseq]) are returned unchanged, and so are the
+    elements [rotary_dim, D) of every head.  ``scaling`` is None or a dict
+    with the keys of ``llama3_inv_freq``.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    T, H, D = x.shape
+    r = D if rotary_dim in (None, 0) else int(rotary_dim)
+    if r < 2 or r % 2 or r > D:
+        raise ValueError("rotary_dim must be even, in [2, D]")
+    if pairing not in ("half", "interleaved"):
+        raise ValueError("pairing is 'half' or 'interleaved'")
+    pos = segment_positions(cu_seqlens, T, pos_offset)
+    y = x.copy()
+    inside = pos >= 0
+    if not inside.any():
+        return y
+    if pairing == "half" and scaling is None:
+        y[inside, :, :r] = rotate(x[inside][:, :, :r], pos[inside], theta, direction)
+        return y
+    freq = inv_freq(theta, r) if scaling is None else llama3_inv_freq(theta, r, **scaling)
+    if pairing == "interleaved":
+        y[inside, :, :r] = rotate_interleaved(x[inside][:, :, :r], pos[inside], freq, direction)
+    else:
+        c, s = cos_sin_freq(pos[inside], freq, direction)
+        c, s = c[:, None, :], s[:, None, :]
+        xi = x[inside]
+        x1, x2 = xi[:, :, : r // 2], xi[:, :, r // 2: r]
+        y[inside, :, : r // 2] = x1 * c - x2 * s
+        y[inside, :, r // 2: r] = x2 * c + x1 * s
+    return y
+
+
+def rope_qk(q: np.ndarray, k: np.ndarray, cu_seqlens, theta: float, direction: int, **variant):
     """Both tensors of the fused call: the same positions and angles for q and k."""
-    return rope(q, cu_seqlens, theta, direction), rope(k, cu_seqlens, theta, direction)
+    return rope(q, cu_seqlens, theta, direction, **variant), rope(k, cu_seqlens, theta, direction, **variant)
 
 
 # ---------------------------------------------------------------------------

@@ -279,6 +279,105 @@ def pin_qk_share_angles(O):
     assert np.array_equal(yq[:, :2, :], yk)
 
 
+# ---------------------------------------------------------------------------
+# variants: position offset, partial rotary dim, interleaved pairing, llama3 scaling
+# ---------------------------------------------------------------------------
+
+def pin_pos_offset_shards(O):
+    """One sequence split over two token shards, the second with pos_offset = its
+    global start, gives exactly the unsharded result; later segments of a shard
+    keep restarting at 0."""
+    rng = _rng(20)
+    T, a = 300, 117
+    x = rng.standard_normal((T, 2, 16))
+    for direction in (1, -1):
+        full = O.rope(x, [0, T], 1e4, direction)
+        s1 = O.rope(x[:a], [0, a], 1e4, direction)
+        s2 = O.rope(x[a:], [0, T - a], 1e4, direction, pos_offset=a)
+        assert np.array_equal(np.concatenate([s1, s2]), full)
+    # brute-force positions: the offset lands on segment 0 only
+    for cu, T2 in (([0, 10, 50, 80], 90), ([4, 4, 9, 12], 12), ([0, 5], 5)):
+        ref = brute_positions(cu, T2)
+        for t in range(cu[0], cu[1]):
+            ref[t] += 1000
+        assert list(O.segment_positions(np.array(cu), T2, 1000)) == ref, cu
+    # only segment 0 of a packed shard moves
+    cu = np.array([0, 10, 50, 80], dtype=np.int32)
+    x = rng.standard_normal((80, 2, 8))
+    y0 = O.rope(x, cu, 1e4, 1)
+    y1 = O.rope(x, cu, 1e4, 1, pos_offset=1000)
+    assert np.array_equal(y0[10:], y1[10:]) and not np.array_equal(y0[:10], y1[:10])
+
+
+def pin_rotary_dim(O):
+    """rotary_dim r: elements [r, D) untouched; [0, r) is RoPE of a head of size r."""
+    rng = _rng(21)
+    cu = np.array([0, 13, 40], dtype=np.int32)
+    x = rng.standard_normal((40, 3, 32))
+    for r in (8, 16, 24):
+        for pairing in ("half", "interleaved"):
+            y = O.rope(x, cu, 1e4, 1, rotary_dim=r, pairing=pairing)
+            assert np.array_equal(y[:, :, r:], x[:, :, r:])
+            z = O.rope(np.ascontiguousarray(x[:, :, :r]), cu, 1e4, 1, pairing=pairing)
+            assert np.array_equal(y[:, :, :r], z)
+
+
+def pin_interleaved_roformer(O):
+    """pairing='interleaved' is RoFormer's adjacent-pair matrix applied to the head as it is."""
+    rng = _rng(22)
+    for D, theta in ((8, 1e4), (12, 1e6)):
+        ps = [0, 1, 5, 333, 90001]
+        x = rng.standard_normal((len(ps), 2, D))
+        for direction in (1, -1):
+            y = O.rotate_interleaved(x, np.array(ps), O.inv_freq(theta, D), direction)
+            for r, p in enumerate(ps):
+                R = _roformer_matrix(p, theta, D, direction)
+                for h in range(2):
+                    z = [mpmath.mpf(float(v)) for v in x[r, h]]
+                    w = [mpmath.fsum(R[a][b] * z[b] for b in range(D)) for a in range(D)]
+                    norm = math.sqrt(sum(float(v) ** 2 for v in z))
+                    tol = (8 * F64_EPS + 2 * math.ulp(float(_exact_angle(p, theta, D, 0)))) * max(norm, 1.0)
+                    for i in range(D):
+                        assert abs(y[r, h, i] - w[i]) <= tol, (D, p, h, i, direction)
+    # the packed call takes the same route
+    cu = np.array([0, 5], dtype=np.int32)
+    x = rng.standard_normal((5, 2, 8))
+    ya = O.rope(x, cu, 1e4, 1, pairing="interleaved")
+    yb = O.rotate_interleaved(x, np.arange(5), O.inv_freq(1e4, 8), 1)
+    assert np.array_equal(ya, yb)
+
+
+def pin_llama3_scaling(O):
+    """Properties of the Llama 3.1 frequency rescaling (no retyped formula):
+    factor 1 is the identity; with every wavelength above the band all
+    frequencies are divided by the factor, below it none are; the rescaled
+    frequency is continuous at both band edges, linear in L / wavelength
+    inside the band, and decreasing in i like the unscaled frequencies."""
+    theta, D = 5e5, 128
+    base = O.inv_freq(theta, D)
+    kw = dict(low_freq_factor=1.0, high_freq_factor=4.0, original_max_position=8192.0)
+    same = O.llama3_inv_freq(theta, D, factor=1.0, **kw)
+    assert np.all(np.abs(same - base) <= 2 * F64_EPS * base)
+    tiny_L = O.llama3_inv_freq(theta, D, factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0, original_max_position=1e-9)
+    assert np.all(np.abs(tiny_L - base / 8.0) <= F64_EPS * base)  # every wavelength is above L / low_freq_factor
+    huge_L = O.llama3_inv_freq(theta, D, factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0, original_max_position=1e12)
+    assert np.array_equal(huge_L, base)  # every wavelength is below L / high_freq_factor
+    got = O.llama3_inv_freq(theta, D, factor=8.0, **kw)
+    assert np.all(np.diff(got) < 0)
+    # ratio got/base as a function of u = L / wavelength (wavelength = 2 pi / f)
+    u = kw["original_max_position"] * base / (2 * math.pi)
+    ratio = got / base
+    band = (u > 1.0) & (u < 4.0)
+    assert band.sum() >= 3, "the test needs frequencies inside the band"
+    assert np.all(np.abs(ratio[u >= 4.0 + 1e-9] - 1.0) <= 2 * F64_EPS)
+    assert np.all(np.abs(ratio[u <= 1.0 - 1e-9] - 1.0 / 8.0) <= 2 * F64_EPS)
+    # continuity: extrapolating the band's line to u = 1 and u = 4 meets 1/8 and 1
+    ub, rb = u[band], ratio[band]
+    slope, icpt = np.polyfit(ub, rb, 1)
+    assert np.max(np.abs(slope * ub + icpt - rb)) <= 1e-13  # linear in u inside the band
+    assert abs(slope * 1.0 + icpt - 1.0 / 8.0) <= 1e-12 and abs(slope * 4.0 + icpt - 1.0) <= 1e-12
+
+
 ALL_PINS = [
     pin_positions,
     pin_inv_freq,
@@ -293,4 +392,8 @@ ALL_PINS = [
     pin_relative_position,
     pin_packed_equals_unpacked,
     pin_qk_share_angles,
+    pin_pos_offset_shards,
+    pin_rotary_dim,
+    pin_interleaved_roformer,
+    pin_llama3_scaling,
 ]
