@@ -77,6 +77,15 @@ extern "C" {
 #define ROPE_QK_ERR_THETA -5     /* theta not finite or <= 0 */
 #define ROPE_QK_ERR_LAUNCH -6    /* the HIP launch itself failed */
 #define ROPE_QK_ERR_LAYOUT -7    /* negative strides, or a tensor whose rows overlap */
+#define ROPE_QK_ERR_OPTION -8    /* a field of rope_qk_options out of range */
+
+/* pairing of the rotated elements of a head (rope_qk_options.pairing) */
+#define ROPE_QK_PAIR_HALF 0         /* element i with element i + r/2 ("rotate_half"; the default) */
+#define ROPE_QK_PAIR_INTERLEAVED 1  /* element 2i with element 2i + 1 */
+
+/* frequency rescaling (rope_qk_options.scaling) */
+#define ROPE_QK_SCALING_NONE 0
+#define ROPE_QK_SCALING_LLAMA3 1
 
 /*
  * Forward rotation, in place, of q and k in ONE kernel launch.
@@ -114,10 +123,64 @@ int rope_qk_bwd(void* dq, void* dk, const int32_t* cu_seqlens, int64_t nseq, int
                 int64_t k_stride_t, int64_t k_stride_h, double theta, int dtype, void* stream);
 
 /*
+ * Options of rope_qk_fwd_opt / rope_qk_bwd_opt.  Zero-initialise the struct and
+ * set what differs: an all-zero struct, or a NULL pointer, gives exactly
+ * rope_qk_fwd / rope_qk_bwd.  None of these is on the pages except the model
+ * names; each is the usual reading of the variant the named models use.
+ *
+ *   pos_offset   added to the position of every token of segment 0, i.e. of
+ *                [cu_seqlens[0], cu_seqlens[1]): the global position of the
+ *                first token of a shard that starts inside a sequence (token
+ *                or context-parallel sharding of one long sequence); later
+ *                segments still restart at 0.  0 <= pos_offset and
+ *                pos_offset + T <= 2^31 - 1.
+ *   rotary_dim   r: rotate elements [0, r) of each head and leave [r, D) not
+ *                read and not written, with the frequencies of a head of size
+ *                r, inv_freq[i] = theta^(-2i/r).  0 means D.  Even,
+ *                2 <= r <= D; (r/2)*elem_size (ROPE_QK_PAIR_HALF) or
+ *                r*elem_size (ROPE_QK_PAIR_INTERLEAVED) must be a multiple of
+ *                16 bytes.
+ *   pairing      ROPE_QK_PAIR_HALF: x1 = x[i], x2 = x[i + r/2];
+ *                ROPE_QK_PAIR_INTERLEAVED: x1 = x[2i], x2 = x[2i + 1] (RoFormer's
+ *                block-diagonal matrix taken literally); same rotation either way.
+ *   scaling      ROPE_QK_SCALING_LLAMA3: the Llama 3.1 frequency rescaling (the
+ *                pages name Llama 3.1 among the supported models).  With
+ *                L = original_max_position and wavelength w = 2 pi / f of each
+ *                inv_freq f: w < L / high_freq_factor keeps f; w > L /
+ *                low_freq_factor gives f / factor; otherwise, with
+ *                s = (L / w - low_freq_factor) / (high_freq_factor - low_freq_factor),
+ *                (1 - s) f / factor + s f.  Needs factor > 0, L > 0 and
+ *                high_freq_factor > low_freq_factor > 0 (Llama 3.1: 8, 8192, 4, 1).
+ */
+typedef struct rope_qk_options {
+  int64_t pos_offset;
+  int64_t rotary_dim;
+  int32_t pairing;
+  int32_t scaling;
+  double factor;
+  double low_freq_factor;
+  double high_freq_factor;
+  double original_max_position;
+} rope_qk_options;
+
+/*
+ * rope_qk_fwd / rope_qk_bwd with options (NULL: none).  Same arguments,
+ * layout, ownership and errors, plus ROPE_QK_ERR_OPTION for an option out of
+ * range.  The options are read during the call only.
+ */
+int rope_qk_fwd_opt(void* q, void* k, const int32_t* cu_seqlens, int64_t nseq, int64_t T,
+                    int64_t Hq, int64_t Hkv, int64_t D, int64_t q_stride_t, int64_t q_stride_h,
+                    int64_t k_stride_t, int64_t k_stride_h, double theta, int dtype,
+                    const rope_qk_options* options, void* stream);
+int rope_qk_bwd_opt(void* dq, void* dk, const int32_t* cu_seqlens, int64_t nseq, int64_t T,
+                    int64_t Hq, int64_t Hkv, int64_t D, int64_t q_stride_t, int64_t q_stride_h,
+                    int64_t k_stride_t, int64_t k_stride_h, double theta, int dtype,
+                    const rope_qk_options* options, void* stream);
+
+/*
  * The positions the rotation kernels use, for inspection: writes, for every
  * t < T, pos(t) as defined above, or -1 for tokens outside
- * [cu_seqlens[0], cu_seqlens[nseq]).  Runs the same device function as the
- * rotation kernels.  pos_out: device int32[T], caller-owned.  Asynchronous on
+ * [cu_seqlens[0], cu_seqlens[nseq]) (no pos_offset).  pos_out: device int32[T], caller-owned.  Asynchronous on
  * `stream`.  Returns ROPE_QK_OK, ROPE_QK_ERR_NULL, ROPE_QK_ERR_SHAPE or
  * ROPE_QK_ERR_LAUNCH.
  */

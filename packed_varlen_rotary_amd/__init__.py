@@ -11,10 +11,18 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     ROPE_QK_BF16,
     ROPE_QK_FP32,
+    ROPE_QK_PAIR_HALF,
+    ROPE_QK_PAIR_INTERLEAVED,
+    ROPE_QK_SCALING_LLAMA3,
+    ROPE_QK_SCALING_NONE,
     RopeQKError,
+    RopeQKOptions,
     load,
+    make_options,
     rope_qk_bwd,
+    rope_qk_bwd_opt,
     rope_qk_fwd,
+    rope_qk_fwd_opt,
     rope_qk_positions,
     rope_qk_strerror,
 )
@@ -22,6 +30,10 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "rope_qk_fwd",
     "rope_qk_bwd",
+    "rope_qk_fwd_opt",
+    "rope_qk_bwd_opt",
+    "RopeQKOptions",
+    "make_options",
     "rope_qk_positions",
     "rope_qk_strerror",
     "RopeQKError",

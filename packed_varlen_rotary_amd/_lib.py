@@ -17,9 +17,45 @@ LIB_PATH = os.path.join(_HERE, "librope_qk.so")
 
 ROPE_QK_FP32 = 0
 ROPE_QK_BF16 = 1
+ROPE_QK_PAIR_HALF = 0
+ROPE_QK_PAIR_INTERLEAVED = 1
+ROPE_QK_SCALING_NONE = 0
+ROPE_QK_SCALING_LLAMA3 = 1
 
 # names exported by include/rope_qk.h
-EXPORTS = ("rope_qk_fwd", "rope_qk_bwd", "rope_qk_positions", "rope_qk_strerror")
+EXPORTS = ("rope_qk_fwd", "rope_qk_bwd", "rope_qk_fwd_opt", "rope_qk_bwd_opt", "rope_qk_positions",
+           "rope_qk_strerror")
+
+
+class RopeQKOptions(ctypes.Structure):
+    """Mirror of ``rope_qk_options`` (include/rope_qk.h); all-zero means no options."""
+
+    _fields_ = [
+        ("pos_offset", ctypes.c_int64),
+        ("rotary_dim", ctypes.c_int64),
+        ("pairing", ctypes.c_int32),
+        ("scaling", ctypes.c_int32),
+        ("factor", ctypes.c_double),
+        ("low_freq_factor", ctypes.c_double),
+        ("high_freq_factor", ctypes.c_double),
+        ("original_max_position", ctypes.c_double),
+    ]
+
+
+def make_options(pos_offset: int = 0, rotary_dim: int = 0, interleaved: bool = False, llama3=None) -> RopeQKOptions:
+    """Options struct from keyword values; llama3 is None or a dict with factor,
+    low_freq_factor, high_freq_factor and original_max_position."""
+    o = RopeQKOptions()
+    o.pos_offset = int(pos_offset)
+    o.rotary_dim = int(rotary_dim or 0)
+    o.pairing = ROPE_QK_PAIR_INTERLEAVED if interleaved else ROPE_QK_PAIR_HALF
+    if llama3 is not None:
+        o.scaling = ROPE_QK_SCALING_LLAMA3
+        o.factor = float(llama3["factor"])
+        o.low_freq_factor = float(llama3["low_freq_factor"])
+        o.high_freq_factor = float(llama3["high_freq_factor"])
+        o.original_max_position = float(llama3["original_max_position"])
+    return o
 
 _lock = threading.Lock()
 _lib = None
@@ -53,6 +89,10 @@ def load():
         for name in ("rope_qk_fwd", "rope_qk_bwd"):
             fn = getattr(lib, name)
             fn.argtypes = rot
+            fn.restype = ctypes.c_int
+        for name in ("rope_qk_fwd_opt", "rope_qk_bwd_opt"):
+            fn = getattr(lib, name)
+            fn.argtypes = rot[:-1] + [ctypes.POINTER(RopeQKOptions), vp]
             fn.restype = ctypes.c_int
         lib.rope_qk_positions.argtypes = [vp, i64, i64, vp, vp]
         lib.rope_qk_positions.restype = ctypes.c_int
@@ -89,7 +129,7 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype}: expected torch.float32 or torch.bfloat16")
 
 
-def _rotate(entry: str, q, k, cu_seqlens, theta: float, stream=None):
+def _rotate(entry: str, q, k, cu_seqlens, theta: float, stream=None, options=None):
     import torch
 
     lib = load()
@@ -110,28 +150,59 @@ def _rotate(entry: str, q, k, cu_seqlens, theta: float, stream=None):
         raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor")
     T, Hq, D = q.shape
     Hkv = k.shape[1]
+    args = [
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+        ctypes.c_void_p(cu_seqlens.data_ptr()), cu_seqlens.numel() - 1, T, Hq, Hkv, D,
+        q.stride(0), q.stride(1), k.stride(0), k.stride(1),
+        float(theta), _dtype_code(q),
+    ]
+    if entry.endswith("_opt"):
+        args.append(ctypes.byref(options) if options is not None else None)
     with torch.cuda.device(q.device):
-        status = getattr(lib, entry)(
-            ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
-            ctypes.c_void_p(cu_seqlens.data_ptr()), cu_seqlens.numel() - 1, T, Hq, Hkv, D,
-            q.stride(0), q.stride(1), k.stride(0), k.stride(1),
-            float(theta), _dtype_code(q), _stream_ptr(q.device, stream),
-        )
+        status = getattr(lib, entry)(*args, _stream_ptr(q.device, stream))
     _check(status)
 
 
-def rope_qk_fwd(q, k, cu_seqlens, theta: float, stream=None):
+def _options_or_none(pos_offset, rotary_dim, interleaved, llama3):
+    if not pos_offset and not rotary_dim and not interleaved and llama3 is None:
+        return None
+    return make_options(pos_offset, rotary_dim, interleaved, llama3)
+
+
+def rope_qk_fwd(q, k, cu_seqlens, theta: float, stream=None, *, pos_offset: int = 0, rotary_dim: int = 0,
+                interleaved: bool = False, llama3=None):
     """Rotate q [T, Hq, D] and k [T, Hkv, D] in place (one kernel launch).
 
     cu_seqlens: int32 [nseq + 1] device tensor of packed-sequence offsets.
     stream: a torch.cuda.Stream (default: the current stream of q's device).
+    Keyword options (see rope_qk_options in include/rope_qk.h): pos_offset for
+    segment 0, rotary_dim, interleaved pairing, llama3 frequency rescaling.
     """
-    _rotate("rope_qk_fwd", q, k, cu_seqlens, theta, stream)
+    opts = _options_or_none(pos_offset, rotary_dim, interleaved, llama3)
+    if opts is None:
+        _rotate("rope_qk_fwd", q, k, cu_seqlens, theta, stream)
+    else:
+        _rotate("rope_qk_fwd_opt", q, k, cu_seqlens, theta, stream, opts)
 
 
-def rope_qk_bwd(dq, dk, cu_seqlens, theta: float, stream=None):
+def rope_qk_bwd(dq, dk, cu_seqlens, theta: float, stream=None, *, pos_offset: int = 0, rotary_dim: int = 0,
+                interleaved: bool = False, llama3=None):
     """Backward of rope_qk_fwd, in place on the incoming gradients dq and dk."""
-    _rotate("rope_qk_bwd", dq, dk, cu_seqlens, theta, stream)
+    opts = _options_or_none(pos_offset, rotary_dim, interleaved, llama3)
+    if opts is None:
+        _rotate("rope_qk_bwd", dq, dk, cu_seqlens, theta, stream)
+    else:
+        _rotate("rope_qk_bwd_opt", dq, dk, cu_seqlens, theta, stream, opts)
+
+
+def rope_qk_fwd_opt(q, k, cu_seqlens, theta: float, options=None, stream=None):
+    """rope_qk_fwd with a RopeQKOptions struct (None: no options)."""
+    _rotate("rope_qk_fwd_opt", q, k, cu_seqlens, theta, stream, options)
+
+
+def rope_qk_bwd_opt(dq, dk, cu_seqlens, theta: float, options=None, stream=None):
+    """rope_qk_bwd with a RopeQKOptions struct (None: no options)."""
+    _rotate("rope_qk_bwd_opt", dq, dk, cu_seqlens, theta, stream, options)
 
 
 def rope_qk_positions(cu_seqlens, T: int, out=None, stream=None):

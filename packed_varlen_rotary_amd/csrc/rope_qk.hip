@@ -63,6 +63,7 @@ constexpr int kMaxTableBytes = 16384;                 // cos/sin table per workg
 constexpr int kEnt = kMaxTableBytes / 16 / kThreads;  // table entries per thread, at most
 constexpr uint32_t kMaxTasksPerToken = 65535;
 constexpr int kPairTasks = 2;                         // chunk pairs per lane (pair tiles)
+constexpr int kInterleaved = -1;                      // tile mode of interleaved pairing
 constexpr int kUnitTasks = 4;                         // chunks per lane (unit tiles)
 constexpr int64_t kGridX = 65536;                     // tiles per grid row
 constexpr int64_t kLdsPerCu = 163840;                 // MI355X: 160 KiB of LDS per compute unit
@@ -109,6 +110,7 @@ struct RopeParams {
   int32_t chunks;          // 16-byte chunks per half row
   int32_t half;            // D / 2
   int32_t half_bytes;      // (D / 2) * element size
+  int32_t pos_offset;      // added to the positions of segment 0
   double sign;             // +1 forward, -1 backward
   double inv_freq[kMaxHalf];
 };
@@ -253,6 +255,37 @@ __device__ __forceinline__ void rotate_unit_f32(const u32x4& own, const u32x4& p
   }
 }
 
+// Interleaved pairing (element 2i with 2i + 1): both elements of a pair sit
+// in one chunk, so a lane rotates its own chunk with no exchange.  bf16: each
+// dword holds one pair (x[2i] low, x[2i+1] high).
+template <bool kExact>
+__device__ __forceinline__ bool rotate_pairs_bf16(const u32x4& own, const double2* __restrict__ cs, int chunks,
+                                                  u32x4& out) {
+  bool tie = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const double2 c = cs[j * chunks];
+    const double x1 = bf16_lo(own[j]), x2 = bf16_hi(own[j]);
+    const double y1 = fma(x1, c.x, -(x2 * c.y));
+    const double y2 = fma(x2, c.x, x1 * c.y);
+    out[j] = kExact ? pack_bf16_exact(y1, y2) : pack_bf16_fast(y1, y2, tie);
+  }
+  return tie;
+}
+
+// fp32: dwords (0, 1) and (2, 3) are the two pairs of a chunk.
+__device__ __forceinline__ void rotate_pairs_f32(const u32x4& own, const double2* __restrict__ cs, int chunks,
+                                                 u32x4& out) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const double2 c = cs[j * chunks];
+    const double x1 = static_cast<double>(__uint_as_float(own[2 * j]));
+    const double x2 = static_cast<double>(__uint_as_float(own[2 * j + 1]));
+    out[2 * j] = __float_as_uint(static_cast<float>(fma(x1, c.x, -(x2 * c.y))));
+    out[2 * j + 1] = __float_as_uint(static_cast<float>(fma(x2, c.x, x1 * c.y)));
+  }
+}
+
 // n / tasks_per_tok for n < 2^24 (m = ceil(2^40 / d), d < 2^16).
 __device__ __forceinline__ uint32_t div_tok(uint32_t n, uint64_t m) {
   return static_cast<uint32_t>((static_cast<uint64_t>(n) * m) >> 40);
@@ -265,9 +298,12 @@ __device__ __forceinline__ uint32_t div_tok(uint32_t n, uint64_t m) {
 // chunk; consecutive lanes cover whole rows, so every load and store of a
 // wave covers whole cache lines, and the partner chunk comes from the lane
 // kG away.
+// kG = kInterleaved: interleaved pairing; a task is one 16-byte chunk of whole
+// pairs, consecutive lanes on consecutive chunks.
 template <int kDtype, int kG, int kTPT>
 __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, int32_t* s_pos, double2* s_cs) {
   constexpr int kVec = (kDtype == ROPE_QK_BF16) ? 8 : 4;  // elements per 16 bytes
+  constexpr int kPPC = kG == kInterleaved ? kVec / 2 : kVec;  // table pairs per chunk
   const int tid = threadIdx.x;
   const cu_ptr cu = (cu_ptr)p.cu;  // address-space cast (C-style: reinterpret_cast cannot change it)
   const int32_t nseq = p.nseq;
@@ -327,7 +363,7 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
         const uint32_t tt = div_tok(l, p.magic_tok);
         const uint32_t r = l - tt * static_cast<uint32_t>(tpt);
         uint32_t h, c, cc;  // head, chunk within the row, chunk within the half row
-        if constexpr (kG == 0) {
+        if constexpr (kG == 0 || kG == kInterleaved) {
           h = div_small(r, p.magic_chunk);
           c = r - h * static_cast<uint32_t>(p.chunks);
           cc = c;
@@ -344,7 +380,7 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
         ptr[u] = row + static_cast<int64_t>(c) * 16;
         tt_of[u] = static_cast<int>(tt);
         c_of[u] = static_cast<int>(cc);
-        first[u] = c < static_cast<uint32_t>(kG);
+        first[u] = kG > 0 && c < static_cast<uint32_t>(kG);
       }
       // streamed once: non-temporal, so they do not displace other data in the caches
       a[u] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4*>(ptr[u]));
@@ -355,6 +391,7 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
     // 3. positions (scalar loads, not ordered behind the data) and the table
     const int32_t s0 = last_start_at_or_before(cu, nseq, t0);
     const int64_t cu_last = cu[nseq];
+    const int64_t cu_first_end = cu[1];  // segment 0 is [cu[0], cu[1]) (nseq >= 1 here)
     int64_t start[kEnt];
 #pragma unroll
     for (int v = 0; v < kEnt; ++v) start[v] = s0 >= 0 ? static_cast<int64_t>(cu[s0]) : INT64_MIN;
@@ -369,15 +406,15 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
       if (v > 0 && v * kThreads >= nent) break;
       const int e = tid + v * kThreads;
       const int64_t t = t0 + tt_e[v];
-      const int64_t pos64 = t - start[v];
-      const int32_t pos =
-          (start[v] != INT64_MIN && t < cu_last && pos64 <= INT32_MAX) ? static_cast<int32_t>(pos64) : -1;
+      const bool inside = start[v] != INT64_MIN && t < cu_last;
+      const int64_t pos64 = inside ? t - start[v] + (t < cu_first_end ? p.pos_offset : 0) : -1;
+      const int32_t pos = pos64 <= INT32_MAX ? static_cast<int32_t>(pos64) : -1;
       if (e < nent) {
         if (i_e[v] == 0) s_pos[tt_e[v]] = pos;
         if (pos >= 0) {
           double sn, cs;
           rope_sincos(static_cast<double>(pos) * f[v], &sn, &cs);
-          s_cs[cs_slot(tt_e[v], i_e[v], kVec, p.chunks)] = make_double2(cs, p.sign * sn);
+          s_cs[cs_slot(tt_e[v], i_e[v], kPPC, p.chunks)] = make_double2(cs, p.sign * sn);
         }
       }
     }
@@ -390,9 +427,15 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
 #pragma unroll
     for (int u = 0; u < kTPT; ++u) {
       st[u] = act[u] && s_pos[tt_of[u]] >= 0;
-      const int chunks = kG == 0 ? p.chunks : kG;
-      const double2* cs = s_cs + tt_of[u] * kVec * chunks + c_of[u];
-      if constexpr (kG == 0) {
+      const int chunks = kG > 0 ? kG : p.chunks;
+      const double2* cs = s_cs + tt_of[u] * kPPC * chunks + c_of[u];
+      if constexpr (kG == kInterleaved) {
+        if constexpr (kDtype == ROPE_QK_BF16) {
+          if (rotate_pairs_bf16<false>(a[u], cs, chunks, oa[u])) rotate_pairs_bf16<true>(a[u], cs, chunks, oa[u]);
+        } else {
+          rotate_pairs_f32(a[u], cs, chunks, oa[u]);
+        }
+      } else if constexpr (kG == 0) {
         if constexpr (kDtype == ROPE_QK_BF16) {
           if (rotate_bf16<false>(a[u], b[u], cs, chunks, oa[u], ob[u]))
             rotate_bf16<true>(a[u], b[u], cs, chunks, oa[u], ob[u]);
@@ -452,14 +495,51 @@ bool rows_overlap(int64_t T, int64_t H, int64_t D, int64_t st, int64_t sh) {
   return s_big / s_small < n_small;  // s_big < n_small * s_small, without overflow
 }
 
+// Frequencies of a head of size r (pairs i < r/2), optionally with the Llama
+// 3.1 rescaling (the rule is documented with rope_qk_options in rope_qk.h).
+void make_inv_freq(double theta, int64_t r, const rope_qk_options& o, double* out) {
+  const double kTwoPi = 6.283185307179586476925286766559;
+  const double L = o.original_max_position;
+  for (int64_t i = 0; i < kMaxHalf; ++i) {
+    if (i >= r / 2) {
+      out[i] = 0.0;
+      continue;
+    }
+    const double f = pow(theta, -static_cast<double>(2 * i) / static_cast<double>(r));
+    if (o.scaling != ROPE_QK_SCALING_LLAMA3) {
+      out[i] = f;
+      continue;
+    }
+    const double w = kTwoPi / f;
+    if (w < L / o.high_freq_factor) {
+      out[i] = f;
+    } else if (w > L / o.low_freq_factor) {
+      out[i] = f / o.factor;
+    } else {
+      const double s = (L / w - o.low_freq_factor) / (o.high_freq_factor - o.low_freq_factor);
+      out[i] = (1.0 - s) * f / o.factor + s * f;
+    }
+  }
+}
+
 int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, int64_t Hq, int64_t Hkv, int64_t D,
-                int64_t q_st, int64_t q_sh, int64_t k_st, int64_t k_sh, double theta, int dtype, void* stream,
-                double sign) {
+                int64_t q_st, int64_t q_sh, int64_t k_st, int64_t k_sh, double theta, int dtype,
+                const rope_qk_options* options, void* stream, double sign) {
+  const rope_qk_options o = options ? *options : rope_qk_options{};
   if (dtype != ROPE_QK_FP32 && dtype != ROPE_QK_BF16) return ROPE_QK_ERR_DTYPE;
   if (nseq < 0 || T < 0 || Hq < 0 || Hkv < 0 || D < 2 || (D & 1) || D > 2 * kMaxHalf || T > INT32_MAX ||
       nseq >= INT32_MAX || Hq + Hkv > INT32_MAX)
     return ROPE_QK_ERR_SHAPE;
   if (!(theta > 0.0) || !isfinite(theta)) return ROPE_QK_ERR_THETA;
+  const int64_t r = o.rotary_dim == 0 ? D : o.rotary_dim;  // elements of each head that are rotated
+  if (o.pos_offset < 0 || o.pos_offset > INT32_MAX - T || r < 2 || (r & 1) || r > D ||
+      (o.pairing != ROPE_QK_PAIR_HALF && o.pairing != ROPE_QK_PAIR_INTERLEAVED) ||
+      (o.scaling != ROPE_QK_SCALING_NONE && o.scaling != ROPE_QK_SCALING_LLAMA3))
+    return ROPE_QK_ERR_OPTION;
+  if (o.scaling == ROPE_QK_SCALING_LLAMA3 &&
+      !(o.factor > 0.0 && isfinite(o.factor) && o.original_max_position > 0.0 && isfinite(o.original_max_position) &&
+        o.low_freq_factor > 0.0 && o.high_freq_factor > o.low_freq_factor && isfinite(o.high_freq_factor)))
+    return ROPE_QK_ERR_OPTION;
   if (T == 0 || nseq == 0 || Hq + Hkv == 0) return ROPE_QK_OK;
   if (cu == nullptr || (Hq > 0 && q == nullptr) || (Hkv > 0 && k == nullptr)) return ROPE_QK_ERR_NULL;
   if ((Hq > 0 && (q_st < 0 || q_sh < 0 || rows_overlap(T, Hq, D, q_st, q_sh))) ||
@@ -467,23 +547,27 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
     return ROPE_QK_ERR_LAYOUT;
 
   const int64_t esz = dtype == ROPE_QK_BF16 ? 2 : 4;
-  const int64_t half = D / 2;
-  if ((half * esz) % 16) return ROPE_QK_ERR_ALIGN;
+  const bool interleaved = o.pairing == ROPE_QK_PAIR_INTERLEAVED;
+  const int64_t half = r / 2;  // rotated pairs per head
+  // 16-byte chunks holding the first elements of pairs: half a rotated row, or all of it when interleaved
+  if (((interleaved ? r : half) * esz) % 16) return ROPE_QK_ERR_ALIGN;
   if (Hq > 0 && ((reinterpret_cast<uintptr_t>(q) % 16) || (q_st * esz) % 16 || (q_sh * esz) % 16))
     return ROPE_QK_ERR_ALIGN;
   if (Hkv > 0 && ((reinterpret_cast<uintptr_t>(k) % 16) || (k_st * esz) % 16 || (k_sh * esz) % 16))
     return ROPE_QK_ERR_ALIGN;
 
-  const int64_t chunks = half * esz / 16;
-  // half rows of 1, 2 or 4 chunks: unit tiles (one chunk per task, partner by lane exchange)
-  const int unit_g = (chunks == 1 || chunks == 2 || chunks == 4) ? static_cast<int>(chunks) : 0;
+  const int64_t chunks = (interleaved ? r : half) * esz / 16;
+  // rotate_half with half rows of 1, 2 or 4 chunks: unit tiles (one chunk per
+  // task, partner by lane exchange); interleaved: one chunk of whole pairs per task
+  const int unit_g = !interleaved && (chunks == 1 || chunks == 2 || chunks == 4) ? static_cast<int>(chunks) : 0;
+  const bool chunk_tasks = unit_g != 0 || interleaved;
   const int64_t tasks_per_tok = (Hq + Hkv) * (unit_g ? 2 * chunks : chunks);
   if (tasks_per_tok > kMaxTasksPerToken) return ROPE_QK_ERR_SHAPE;
 
   // a tile touches at most cap_tokens tokens, so its table and positions fit in LDS
   int64_t cap_tokens = kMaxTableBytes / (half * 16);
   if (cap_tokens > kMaxTileTokens) cap_tokens = kMaxTileTokens;
-  int64_t tile_tasks = int64_t(kThreads) * (unit_g ? kUnitTasks : kPairTasks);
+  int64_t tile_tasks = int64_t(kThreads) * (chunk_tasks ? kUnitTasks : kPairTasks);
   if (tile_tasks > (cap_tokens - 1) * tasks_per_tok) tile_tasks = (cap_tokens - 1) * tasks_per_tok;
   // tokens one tile touches: exactly tile_tasks / tasks_per_tok when every tile starts on a token
   const int64_t span = tile_tasks % tasks_per_tok == 0 ? tile_tasks / tasks_per_tok
@@ -503,7 +587,7 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
   p.magic_tok = ((uint64_t(1) << 40) + tasks_per_tok - 1) / tasks_per_tok;
   p.magic_chunk = ((uint64_t(1) << 32) + chunks - 1) / chunks;
   p.magic_half = ((uint64_t(1) << 32) + half - 1) / half;
-  p.tok_step = unit_g && kThreads % tasks_per_tok == 0 ? static_cast<uint32_t>(kThreads / tasks_per_tok) : 0u;
+  p.tok_step = chunk_tasks && kThreads % tasks_per_tok == 0 ? static_cast<uint32_t>(kThreads / tasks_per_tok) : 0u;
   p.rcp_tok = 1.0 / static_cast<double>(tasks_per_tok);
   p.ntiles = static_cast<uint32_t>(ntiles);
   p.tile_tasks = static_cast<int32_t>(tile_tasks);
@@ -513,14 +597,14 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
   p.chunks = static_cast<int32_t>(chunks);
   p.half = static_cast<int32_t>(half);
   p.half_bytes = static_cast<int32_t>(half * esz);
+  p.pos_offset = static_cast<int32_t>(o.pos_offset);
   p.sign = sign;
-  for (int64_t i = 0; i < kMaxHalf; ++i)
-    p.inv_freq[i] = i < half ? pow(theta, -static_cast<double>(2 * i) / static_cast<double>(D)) : 0.0;
+  make_inv_freq(theta, r, o, p.inv_freq);
 
   // LDS: the table of the tokens one tile touches; for pair tiles, padded so
   // that at most the measured best number of workgroups share a compute unit
   size_t lds = static_cast<size_t>(span * half) * sizeof(double2);
-  if (!unit_g) {
+  if (!chunk_tasks) {
     const int64_t cap = tasks_per_tok >= kWideTasksPerToken ? kPairCapWide : kPairCapNarrow;
     const size_t pad = static_cast<size_t>(kLdsPerCu / (cap + 1) + 1024 - kMaxTileTokens * sizeof(int32_t));
     if (lds < pad) lds = pad;
@@ -531,12 +615,14 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
   const void* fn;
 #define ROPE_FN(DT, G, TPT) reinterpret_cast<const void*>(&rope_qk_kernel<DT, G, TPT>)
   if (dtype == ROPE_QK_BF16) {
-    fn = unit_g == 1   ? ROPE_FN(ROPE_QK_BF16, 1, kUnitTasks)
+    fn = interleaved   ? ROPE_FN(ROPE_QK_BF16, kInterleaved, kUnitTasks)
+         : unit_g == 1 ? ROPE_FN(ROPE_QK_BF16, 1, kUnitTasks)
          : unit_g == 2 ? ROPE_FN(ROPE_QK_BF16, 2, kUnitTasks)
          : unit_g == 4 ? ROPE_FN(ROPE_QK_BF16, 4, kUnitTasks)
                        : ROPE_FN(ROPE_QK_BF16, 0, kPairTasks);
   } else {
-    fn = unit_g == 1   ? ROPE_FN(ROPE_QK_FP32, 1, kUnitTasks)
+    fn = interleaved   ? ROPE_FN(ROPE_QK_FP32, kInterleaved, kUnitTasks)
+         : unit_g == 1 ? ROPE_FN(ROPE_QK_FP32, 1, kUnitTasks)
          : unit_g == 2 ? ROPE_FN(ROPE_QK_FP32, 2, kUnitTasks)
          : unit_g == 4 ? ROPE_FN(ROPE_QK_FP32, 4, kUnitTasks)
                        : ROPE_FN(ROPE_QK_FP32, 0, kPairTasks);
@@ -555,14 +641,28 @@ int rope_qk_fwd(void* q, void* k, const int32_t* cu_seqlens, int64_t nseq, int64
                 int64_t D, int64_t q_stride_t, int64_t q_stride_h, int64_t k_stride_t, int64_t k_stride_h,
                 double theta, int dtype, void* stream) {
   return launch_rope(q, k, cu_seqlens, nseq, T, Hq, Hkv, D, q_stride_t, q_stride_h, k_stride_t, k_stride_h, theta,
-                     dtype, stream, 1.0);
+                     dtype, nullptr, stream, 1.0);
 }
 
 int rope_qk_bwd(void* dq, void* dk, const int32_t* cu_seqlens, int64_t nseq, int64_t T, int64_t Hq, int64_t Hkv,
                 int64_t D, int64_t q_stride_t, int64_t q_stride_h, int64_t k_stride_t, int64_t k_stride_h,
                 double theta, int dtype, void* stream) {
   return launch_rope(dq, dk, cu_seqlens, nseq, T, Hq, Hkv, D, q_stride_t, q_stride_h, k_stride_t, k_stride_h,
-                     theta, dtype, stream, -1.0);
+                     theta, dtype, nullptr, stream, -1.0);
+}
+
+int rope_qk_fwd_opt(void* q, void* k, const int32_t* cu_seqlens, int64_t nseq, int64_t T, int64_t Hq, int64_t Hkv,
+                    int64_t D, int64_t q_stride_t, int64_t q_stride_h, int64_t k_stride_t, int64_t k_stride_h,
+                    double theta, int dtype, const rope_qk_options* options, void* stream) {
+  return launch_rope(q, k, cu_seqlens, nseq, T, Hq, Hkv, D, q_stride_t, q_stride_h, k_stride_t, k_stride_h, theta,
+                     dtype, options, stream, 1.0);
+}
+
+int rope_qk_bwd_opt(void* dq, void* dk, const int32_t* cu_seqlens, int64_t nseq, int64_t T, int64_t Hq,
+                    int64_t Hkv, int64_t D, int64_t q_stride_t, int64_t q_stride_h, int64_t k_stride_t,
+                    int64_t k_stride_h, double theta, int dtype, const rope_qk_options* options, void* stream) {
+  return launch_rope(dq, dk, cu_seqlens, nseq, T, Hq, Hkv, D, q_stride_t, q_stride_h, k_stride_t, k_stride_h,
+                     theta, dtype, options, stream, -1.0);
 }
 
 int rope_qk_positions(const int32_t* cu_seqlens, int64_t nseq, int64_t T, int32_t* pos_out, void* stream) {
@@ -589,6 +689,7 @@ const char* rope_qk_strerror(int status) {
     case ROPE_QK_ERR_THETA: return "theta must be finite and > 0";
     case ROPE_QK_ERR_LAUNCH: return "HIP kernel launch failed";
     case ROPE_QK_ERR_LAYOUT: return "negative strides or overlapping rows";
+    case ROPE_QK_ERR_OPTION: return "an option is out of range (pos_offset, rotary_dim, pairing or scaling)";
     default: return "unknown status";
   }
 }

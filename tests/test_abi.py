@@ -142,3 +142,66 @@ def test_library_shares_torchs_hip_runtime():
     maps = open("/proc/self/maps").read()
     hips = set(re.findall(r"\S*libamdhip64\S*", maps))
     assert len(hips) == 1, hips
+
+
+def fwd_opt(opts, which="rope_qk_fwd_opt", **kw):
+    args = dict(q=Q, k=K, cu=CU, nseq=4, T=256, Hq=14, Hkv=2, D=64, theta=1e6, dtype=1)
+    args.update(kw)
+    D, Hq, Hkv = args["D"], args["Hq"], args["Hkv"]
+    return getattr(lib, which)(ctypes.c_void_p(args["q"]), ctypes.c_void_p(args["k"]), ctypes.c_void_p(args["cu"]),
+                               args["nseq"], args["T"], Hq, Hkv, D, Hq * D, D, Hkv * D, D, args["theta"],
+                               args["dtype"], ctypes.byref(opts) if opts is not None else None, None)
+
+
+LLAMA3 = dict(factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0, original_max_position=8192.0)
+
+
+@pytest.mark.parametrize("which", ["rope_qk_fwd_opt", "rope_qk_bwd_opt"])
+def test_option_error_codes(which):
+    E = C["ROPE_QK_ERR_OPTION"]
+    f = lambda o, **kw: fwd_opt(o, which=which, **kw)  # noqa: E731
+    mk = P.make_options
+    assert f(mk(pos_offset=-1)) == E
+    assert f(mk(pos_offset=2 ** 31 - 256)) == E  # pos_offset + T past 2^31 - 1
+    assert f(mk(pos_offset=2 ** 31 - 257), cu=0) == C["ROPE_QK_ERR_NULL"]  # just fits: reaches the next check
+    for r in (1, 3, 66, 128):  # odd, odd, > D, > D
+        assert f(mk(rotary_dim=r)) == E, r
+    o = mk()
+    o.pairing = 5
+    assert f(o) == E
+    o = mk()
+    o.scaling = 7
+    assert f(o) == E
+    for bad in (dict(factor=0.0), dict(high_freq_factor=1.0), dict(original_max_position=0.0),
+                dict(low_freq_factor=0.0), dict(factor=float("inf"))):
+        assert f(mk(llama3={**LLAMA3, **bad})) == E, bad
+    # options are checked before the no-op shapes return
+    assert f(mk(rotary_dim=3), T=0) == E
+    # alignment of the rotated part: rotate_half needs (r/2)*elem, interleaved r*elem to be 16-byte multiples
+    assert f(mk(rotary_dim=24)) == C["ROPE_QK_ERR_ALIGN"]  # 12 bf16 = 24 bytes
+    assert f(mk(rotary_dim=24, interleaved=True), cu=0) == C["ROPE_QK_ERR_NULL"]  # 24 bf16 = 48 bytes: fine
+    assert f(mk(rotary_dim=4, interleaved=True)) == C["ROPE_QK_ERR_ALIGN"]  # 8 bytes
+    # valid options reach the pointer checks; NULL options behave like the plain call
+    assert f(mk(pos_offset=5, rotary_dim=32, interleaved=True, llama3=LLAMA3), cu=0) == C["ROPE_QK_ERR_NULL"]
+    assert f(None, dtype=7) == C["ROPE_QK_ERR_DTYPE"]
+    assert f(None, T=0) == C["ROPE_QK_OK"]
+
+
+def test_options_struct_layout_matches_header(tmp_path):
+    """The ctypes mirror has the C struct's size and field offsets (gcc on the header)."""
+    src = tmp_path / "layout.c"
+    names = [n for n, _ in P.RopeQKOptions._fields_]
+    body = "".join(f'  printf("%zu\\n", offsetof(rope_qk_options, {n}));\n' for n in names)
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "rope_qk.h"\nint main(void) {\n'
+                   '  printf("%zu\\n", sizeof(rope_qk_options));\n' + body + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = [ctypes.sizeof(P.RopeQKOptions)] + [getattr(P.RopeQKOptions, n).offset for n in names]
+    assert got == want
+
+
+def test_pairing_and_scaling_constants_match_binding():
+    assert C["ROPE_QK_PAIR_HALF"] == P.ROPE_QK_PAIR_HALF and C["ROPE_QK_PAIR_INTERLEAVED"] == P.ROPE_QK_PAIR_INTERLEAVED
+    assert C["ROPE_QK_SCALING_NONE"] == P.ROPE_QK_SCALING_NONE
+    assert C["ROPE_QK_SCALING_LLAMA3"] == P.ROPE_QK_SCALING_LLAMA3
