@@ -252,6 +252,41 @@ def run_copy_calibration(args):
     log(f"[bench] copied {n * 2} bytes x {args.steps}")
 
 
+def run_copy_ceiling(args):
+    """Context for the roofline: the runtime's device-to-device copy moving the
+    same HBM traffic as one launch of the workload (read + write of
+    bytes_per_pass / 2 bytes), replayed from a HIP graph over rotating buffers
+    of >= 1 GiB, timed with events around the replay."""
+    import torch
+
+    import workloads as W
+
+    w = W.make_workload(args.workload)
+    n = w.bytes_per_pass // 2
+    nb = max(2, min(64, -(-(1 << 30) // n)))
+    src = [torch.ones(n, dtype=torch.uint8, device="cuda") for _ in range(nb)]
+    dst = [torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(nb)]
+    for i in range(args.warmup):
+        dst[i % nb].copy_(src[i % nb])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(args.steps):
+            dst[i % nb].copy_(src[(i + 1) % nb])
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / args.steps
+    gbs = w.bytes_per_pass / (us * 1e-6) / 1e9
+    log(f"[bench] copy of {n} bytes ({w.bytes_per_pass} bytes of traffic): {us:.2f} us, {gbs:.0f} GB/s")
+    print(json.dumps({"metric": "device-to-device copy with one launch's HBM traffic", "workload": w.name,
+                      "traffic_bytes": w.bytes_per_pass, "us_per_copy": us, "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,6 +300,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of --copy-bytes (for HBM counter scaling)")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--copy-ceiling", action="store_true",
+                    help="only time the runtime's device copy with one launch's HBM traffic (roofline context)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -274,6 +311,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         run_copy_calibration(args)
+        return
+    if args.copy_ceiling:
+        run_copy_ceiling(args)
         return
 
     w, r = run_gpu(args)

@@ -74,6 +74,10 @@ __all__ = [
     "bf16_bits",
     "bits_to_f64",
     "ulp_distance_bf16",
+    "fp16_rne",
+    "fp16_bits",
+    "fp16_bits_to_f64",
+    "ulp_distance_16",
 ]
 
 
@@ -303,4 +307,46 @@ def _order_key(bits: np.ndarray) -> np.ndarray:
 
 def ulp_distance_bf16(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
     """Number of bfloat16 grid steps between two bit patterns (+0 and -0 coincide)."""
+    return np.abs(_order_key(a_bits) - _order_key(b_bits))
+
+
+# ---------------------------------------------------------------------------
+# IEEE binary16 (fp16) rounding and comparison helpers
+# ---------------------------------------------------------------------------
+
+_FP16_MIN_NORMAL = 2.0 ** -14
+_FP16_MAX = (2.0 - 2.0 ** -10) * 2.0 ** 15  # 65504
+
+
+def fp16_rne(y: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest IEEE half-precision value, ties to even.
+
+    Normal range: y = m * 2^e with 0.5 <= |m| < 1 (frexp); half precision keeps
+    11 significant bits, so the result is rint(m * 2^11) * 2^(e-11).  Below the
+    smallest normal 2^-14 the grid is fixed at 2^-24.  Values that round past
+    the largest finite half, 65504, become +-inf; NaN stays NaN.  Returned as
+    float64 holding exactly representable half values.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    m, e = np.frexp(y)
+    r = np.ldexp(np.rint(m * 2048.0), e - 11)
+    small = np.abs(y) < _FP16_MIN_NORMAL
+    if np.any(small):
+        r = np.where(small, np.ldexp(np.rint(np.ldexp(y, 24)), -24), r)
+    r = np.where(np.abs(r) > _FP16_MAX, np.copysign(np.inf, y), r)
+    return np.where(np.isnan(y), np.nan, r)
+
+
+def fp16_bits(y: np.ndarray) -> np.ndarray:
+    """uint16 bit patterns of float64 values that are exactly half-representable."""
+    return np.asarray(y, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def fp16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """float64 values of uint16 half-precision bit patterns."""
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def ulp_distance_16(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """Grid steps between two 16-bit sign-magnitude float patterns (bf16 or fp16; +0 and -0 coincide)."""
     return np.abs(_order_key(a_bits) - _order_key(b_bits))

@@ -82,3 +82,38 @@ def test_ulp_distance():
     assert list(oracle.ulp_distance_bf16(a, b)) == [0, 1, 0, 1, 2, 2]
     v = np.array([1.0, -2.5, 0.15625])
     assert np.array_equal(oracle.bits_to_f64(oracle.bf16_bits(v)), v)
+
+
+def test_fp16_rne_hand_cases():
+    """Ties to even, subnormal grid and the overflow boundary, worked out by hand."""
+    cases = [
+        (1.0 + 2.0 ** -11, 1.0),                   # halfway between 1 and 1 + 2^-10: even is 1
+        (1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -9),   # halfway between 1 + 2^-10 and 1 + 2^-9: even is 1 + 2^-9
+        (1.0 + 2.0 ** -11 + 2.0 ** -40, 1.0 + 2.0 ** -10),  # just above the tie
+        (-(1.0 + 2.0 ** -11), -1.0),
+        (65504.0, 65504.0),
+        (65519.99, 65504.0),                       # below the midpoint 65520
+        (65520.0, float("inf")),                   # the midpoint rounds to even, past the largest finite
+        (2.0 ** -14, 2.0 ** -14),                  # smallest normal
+        (2.0 ** -25, 0.0),                         # halfway between 0 and 2^-24: even is 0
+        (3 * 2.0 ** -25, 2.0 ** -23),              # halfway between 2^-24 and 2^-23: even is 2^-23
+        (5 * 2.0 ** -26, 2.0 ** -24),              # 1.25 * 2^-24
+        (2.0 ** -14 - 2.0 ** -25, 2.0 ** -14),     # tie at the top of the subnormal range: even is 2^-14
+    ]
+    for y, want in cases:
+        got = float(oracle.fp16_rne(np.array([y]))[0])
+        assert got == want, (y, got, want)
+    assert np.isnan(oracle.fp16_rne(np.array([np.nan]))[0])
+
+
+def test_fp16_rne_matches_an_independent_conversion():
+    """numpy's float64 -> float16 cast is a separate implementation of the same rounding."""
+    rng = np.random.default_rng(5)
+    y = np.concatenate([rng.standard_normal(200000) * 10.0 ** rng.integers(-9, 5, size=200000),
+                        (np.arange(-4096, 4096) + 0.5) * 2.0 ** -24,  # every subnormal tie
+                        1.0 + (np.arange(2048) + 0.5) * 2.0 ** -10])  # every tie in [1, 2)
+    with np.errstate(over="ignore"):
+        ref = y.astype(np.float16).astype(np.float64)
+    got = oracle.fp16_rne(y)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(oracle.fp16_bits_to_f64(oracle.fp16_bits(got)), got)

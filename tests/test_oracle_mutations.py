@@ -173,3 +173,42 @@ def test_pins_catch_mutant(name, monkeypatch):
         except Exception:  # any failure of a pin is a detection
             caught.append(pin.__name__)
     assert caught, f"mutant {name} passed every pin"
+
+
+# ---------------------------------------------------------------------------
+# the fp16 rounding helper
+# ---------------------------------------------------------------------------
+
+_orig_fp16 = R.fp16_rne
+
+
+def _fp16_variant(y, bits=11, sub_exp=24, rnd=np.rint, overflow=True):
+    y = np.asarray(y, dtype=np.float64)
+    m, e = np.frexp(y)
+    r = np.ldexp(rnd(m * 2.0 ** bits), e - bits)
+    small = np.abs(y) < 2.0 ** -14
+    r = np.where(small, np.ldexp(rnd(np.ldexp(y, sub_exp)), -sub_exp), r)
+    if overflow:
+        r = np.where(np.abs(r) > 65504.0, np.copysign(np.inf, y), r)
+    return r
+
+
+FP16_MUTANTS = {
+    "truncates": lambda y: _fp16_variant(y, rnd=np.trunc),
+    "ties_away_from_zero": lambda y: _fp16_variant(y, rnd=lambda v: np.sign(v) * np.floor(np.abs(v) + 0.5)),
+    "ten_significant_bits": lambda y: _fp16_variant(y, bits=10),
+    "subnormal_grid_2^-25": lambda y: _fp16_variant(y, sub_exp=25),
+    "no_overflow_to_inf": lambda y: _fp16_variant(y, overflow=False),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP16_MUTANTS))
+def test_fp16_pins_catch_mutant(name, monkeypatch):
+    from tests import test_oracle
+
+    import oracle
+
+    monkeypatch.setattr(R, "fp16_rne", FP16_MUTANTS[name])
+    monkeypatch.setattr(oracle, "fp16_rne", FP16_MUTANTS[name])  # the package re-exports the module's names
+    with pytest.raises(AssertionError):
+        test_oracle.test_fp16_rne_hand_cases()
