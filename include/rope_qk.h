@@ -33,8 +33,8 @@
  * so positions restart at 0 at every sequence boundary.  Tokens t < cu_seqlens[0]
  * and t >= cu_seqlens[nseq] are not read and not written.  The rotation is
  * evaluated in float64 and rounded once to the storage type (round to nearest,
- * ties to even): bf16 results are the correctly rounded bf16 of the float64
- * rotation, fp32 results the correctly rounded fp32.
+ * ties to even): bf16 and fp16 results are the correctly rounded bf16 or fp16
+ * of the float64 rotation, fp32 results the correctly rounded fp32.
  *
  * Memory, ownership, ordering
  * ---------------------------
@@ -67,12 +67,13 @@ extern "C" {
 /* storage types of q and k (both tensors share one type) */
 #define ROPE_QK_FP32 0
 #define ROPE_QK_BF16 1
+#define ROPE_QK_FP16 2  /* IEEE binary16, subnormals included; results past 65504 become inf */
 
 /* status codes */
 #define ROPE_QK_OK 0
 #define ROPE_QK_ERR_NULL -1      /* a required pointer is NULL */
 #define ROPE_QK_ERR_SHAPE -2     /* negative size, D odd or < 2 or > 512, T >= 2^31, too many heads */
-#define ROPE_QK_ERR_DTYPE -3     /* dtype not ROPE_QK_FP32 / ROPE_QK_BF16 */
+#define ROPE_QK_ERR_DTYPE -3     /* dtype not ROPE_QK_FP32 / ROPE_QK_BF16 / ROPE_QK_FP16 */
 #define ROPE_QK_ERR_ALIGN -4     /* base, stride*elem or (D/2)*elem not a multiple of 16 bytes */
 #define ROPE_QK_ERR_THETA -5     /* theta not finite or <= 0 */
 #define ROPE_QK_ERR_LAUNCH -6    /* the HIP launch itself failed */
@@ -101,7 +102,7 @@ extern "C" {
  *                element strides of the token and head axes (contiguous:
  *                (Hq*D, D) and (Hkv*D, D)); must be >= 0
  *   theta        rotary base (e.g. 1e6 for Qwen2.5/Qwen3, 5e5 for Llama-3.1)
- *   dtype        ROPE_QK_FP32 or ROPE_QK_BF16
+ *   dtype        ROPE_QK_FP32, ROPE_QK_BF16 or ROPE_QK_FP16
  *   stream       hipStream_t to launch on
  *
  * Alignment (16-byte vector path): q, k, every stride * elem_size and

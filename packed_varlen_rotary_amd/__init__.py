@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     ROPE_QK_BF16,
+    ROPE_QK_FP16,
     ROPE_QK_FP32,
     ROPE_QK_PAIR_HALF,
     ROPE_QK_PAIR_INTERLEAVED,
@@ -42,4 +43,5 @@ __all__ = [
     "EXPORTS",
     "ROPE_QK_FP32",
     "ROPE_QK_BF16",
+    "ROPE_QK_FP16",
 ]

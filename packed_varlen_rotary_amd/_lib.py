@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "librope_qk.so")
 
 ROPE_QK_FP32 = 0
 ROPE_QK_BF16 = 1
+ROPE_QK_FP16 = 2
 ROPE_QK_PAIR_HALF = 0
 ROPE_QK_PAIR_INTERLEAVED = 1
 ROPE_QK_SCALING_NONE = 0
@@ -124,9 +125,11 @@ def _dtype_code(t):
 
     if t.dtype == torch.bfloat16:
         return ROPE_QK_BF16
+    if t.dtype == torch.float16:
+        return ROPE_QK_FP16
     if t.dtype == torch.float32:
         return ROPE_QK_FP32
-    raise TypeError(f"unsupported dtype {t.dtype}: expected torch.float32 or torch.bfloat16")
+    raise TypeError(f"unsupported dtype {t.dtype}: expected torch.float32, torch.bfloat16 or torch.float16")
 
 
 def _rotate(entry: str, q, k, cu_seqlens, theta: float, stream=None, options=None):

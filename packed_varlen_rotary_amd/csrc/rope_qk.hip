@@ -41,9 +41,10 @@
 //    cannot be reused until it completes, so an early store would make the
 //    next task wait for a write acknowledgement.
 //  * The rotation is done in float64 and rounded once: fp32 output is the
-//    correctly rounded fp32; bf16 output is the correctly rounded bf16 (fast
-//    float64->fp32->bf16 path, and an exact re-rounding for the rare values
-//    whose fp32 rounding lands exactly on a bf16 midpoint).
+//    correctly rounded fp32; bf16 and fp16 output is the correctly rounded
+//    bf16 or fp16 (fast float64->fp32->16-bit path, and an exact re-rounding
+//    for the rare values whose fp32 rounding lands exactly on a midpoint of
+//    the 16-bit grid, or, for fp16, in its subnormal range).
 //  * All offsets are 64-bit; one build covers every tensor size.
 
 #include <hip/hip_runtime.h>
@@ -75,12 +76,14 @@ constexpr int64_t kLdsPerCu = 163840;                 // MI355X: 160 KiB of LDS 
 // (e.g. 40 or 72 heads) 3 resident tiles stream 2-5% faster than 4-6, with
 // fewer (e.g. 16 heads) 4 are best.  Unit tiles run uncapped (5 per CU at
 // their register count); any cap costs them 2-17%.
+constexpr uint32_t kF16MinNormalBits = 0x38800000u;  // fp32 bit pattern of 2^-14, the smallest normal fp16
 constexpr int kPairCapWide = 3;
 constexpr int kPairCapNarrow = 4;
 constexpr int64_t kWideTasksPerToken = 256;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef double f64x2 __attribute__((ext_vector_type(2)));
 // cu_seqlens is only read, with wave-uniform indices: through the constant
@@ -155,48 +158,96 @@ __device__ __forceinline__ int cs_slot(int tt, int i, int vec, int chunks) {
   return (tt * vec + j) * chunks + c;
 }
 
-// Fast rounding of two float64 values to a packed bf16 pair: round each to
-// fp32, then the pair to bf16 (both round to nearest even; one packed
-// conversion).  The result equals the single correctly rounded bf16 unless
-// an fp32 value is exactly a bf16 midpoint, which sets `tie`.
-__device__ __forceinline__ uint32_t pack_bf16_fast(double lo, double hi, bool& tie) {
+// ---- 16-bit storage (bf16, fp16): two elements per dword, the lower-indexed
+// element in the low half ----
+
+// Exact float64 values of the two elements of a dword.
+template <int kDtype>
+__device__ __forceinline__ f64x2 unpack16(uint32_t w) {
+  if constexpr (kDtype == ROPE_QK_BF16) {
+    return f64x2{static_cast<double>(__uint_as_float(w << 16)), static_cast<double>(__uint_as_float(w & 0xFFFF0000u))};
+  } else {
+    return __builtin_convertvector(__builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2), f64x2);
+  }
+}
+
+// Is an fp32 value one that the fp32 -> fp16 step may round differently from
+// a direct float64 -> fp16 rounding?  Midpoints of the fp16 grid in its normal
+// range (low 13 of 24 significant bits 1 followed by zeros), and every nonzero
+// value below 2^-14, where the grid of fp16 subnormals is coarser.
+__device__ __forceinline__ bool fp16_hard(uint32_t b) {
+  return (b & 0x1FFFu) == 0x1000u || (b & 0x7FFFFFFFu) - 1u < kF16MinNormalBits - 1u;
+}
+
+// Fast rounding of two float64 values to a packed 16-bit pair: round each to
+// fp32, then the pair to the storage format (both round to nearest even; one
+// packed conversion).  The result equals the single correctly rounded value
+// unless an fp32 value is exactly a midpoint of the storage grid (bf16: low 16
+// bits 0x8000), or is otherwise hard (fp16_hard), which sets `tie`.
+template <int kDtype>
+__device__ __forceinline__ uint32_t pack16_fast(double lo, double hi, bool& tie) {
   const f32x2 f = {static_cast<float>(lo), static_cast<float>(hi)};
-  tie |= (__float_as_uint(f.x) & 0xFFFFu) == 0x8000u;
-  tie |= (__float_as_uint(f.y) & 0xFFFFu) == 0x8000u;
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+  if constexpr (kDtype == ROPE_QK_BF16) {
+    tie |= (__float_as_uint(f.x) & 0xFFFFu) == 0x8000u;
+    tie |= (__float_as_uint(f.y) & 0xFFFFu) == 0x8000u;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+  } else {
+    tie |= fp16_hard(__float_as_uint(f.x));
+    tie |= fp16_hard(__float_as_uint(f.y));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+  }
 }
 
-// Exact: one rounding from float64 to bf16 (the compiler's float64->bf16
-// conversion rounds to odd at fp32 precision, then to nearest even).
-__device__ __forceinline__ uint32_t pack_bf16_exact(double lo, double hi) {
-  const f64x2 d = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(d, bf16x2));
+// float64 -> fp32 rounded to odd: the fp32 neighbour of y toward zero, with
+// its last bit set when y is not exactly representable.  Rounding that value
+// to nearest even in a format with at least two fewer significant bits gives
+// the correctly rounded y (Boldo and Melquiond, "Emulation of FMA and
+// correctly rounded sums: proved algorithms using rounding to odd", IEEE
+// Trans. Computers 2008).
+__device__ __forceinline__ float f32_round_odd(double y) {
+  const float f = static_cast<float>(y);
+  const uint32_t b = __float_as_uint(f);
+  const bool even_inexact = static_cast<double>(f) != y && !(b & 1u);
+  // the other fp32 neighbour of y, which is odd: one step down or up in magnitude
+  const uint32_t other = fabs(static_cast<double>(f)) > fabs(y) ? b - 1u : b + 1u;
+  return __uint_as_float(even_inexact ? other : b);
 }
 
-__device__ __forceinline__ double bf16_lo(uint32_t w) { return static_cast<double>(__uint_as_float(w << 16)); }
-__device__ __forceinline__ double bf16_hi(uint32_t w) { return static_cast<double>(__uint_as_float(w & 0xFFFF0000u)); }
+// Exact: one rounding from float64 to the storage format.  bf16: the
+// compiler's float64 -> bf16 conversion (rounds to odd at fp32 precision,
+// then to nearest even).  fp16: round to odd at fp32, then the packed
+// fp32 -> fp16 conversion (nearest even).
+template <int kDtype>
+__device__ __forceinline__ uint32_t pack16_exact(double lo, double hi) {
+  if constexpr (kDtype == ROPE_QK_BF16) {
+    const f64x2 d = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(d, bf16x2));
+  } else {
+    const f32x2 f = {f32_round_odd(lo), f32_round_odd(hi)};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+  }
+}
 
-// Rotate one task of bf16 data: a holds x[i .. i+7], b holds x[i+D/2 .. i+D/2+7].
-template <bool kExact>
-__device__ __forceinline__ bool rotate_bf16(const u32x4& a, const u32x4& b, const double2* __restrict__ cs,
-                                            int chunks, u32x4& oa, u32x4& ob) {
+// Rotate one task of 16-bit data: a holds x[i .. i+7], b holds x[i+D/2 .. i+D/2+7].
+template <int kDtype, bool kExact>
+__device__ __forceinline__ bool rotate_pair16(const u32x4& a, const u32x4& b, const double2* __restrict__ cs,
+                                              int chunks, u32x4& oa, u32x4& ob) {
   bool tie = false;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const double2 c0 = cs[(2 * j) * chunks];
     const double2 c1 = cs[(2 * j + 1) * chunks];
-    const double x1l = bf16_lo(a[j]), x1h = bf16_hi(a[j]);
-    const double x2l = bf16_lo(b[j]), x2h = bf16_hi(b[j]);
-    const double y1l = fma(x1l, c0.x, -(x2l * c0.y));
-    const double y2l = fma(x2l, c0.x, x1l * c0.y);
-    const double y1h = fma(x1h, c1.x, -(x2h * c1.y));
-    const double y2h = fma(x2h, c1.x, x1h * c1.y);
+    const f64x2 x1 = unpack16<kDtype>(a[j]), x2 = unpack16<kDtype>(b[j]);
+    const double y1l = fma(x1.x, c0.x, -(x2.x * c0.y));
+    const double y2l = fma(x2.x, c0.x, x1.x * c0.y);
+    const double y1h = fma(x1.y, c1.x, -(x2.y * c1.y));
+    const double y2h = fma(x2.y, c1.x, x1.y * c1.y);
     if (kExact) {
-      oa[j] = pack_bf16_exact(y1l, y1h);
-      ob[j] = pack_bf16_exact(y2l, y2h);
+      oa[j] = pack16_exact<kDtype>(y1l, y1h);
+      ob[j] = pack16_exact<kDtype>(y2l, y2h);
     } else {
-      oa[j] = pack_bf16_fast(y1l, y1h, tie);
-      ob[j] = pack_bf16_fast(y2l, y2h, tie);
+      oa[j] = pack16_fast<kDtype>(y1l, y1h, tie);
+      ob[j] = pack16_fast<kDtype>(y2l, y2h, tie);
     }
   }
   return tie;
@@ -227,21 +278,22 @@ __device__ __forceinline__ uint32_t partner_dword(uint32_t x) {
   return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(x), kPattern));
 }
 
-// Rotate one 16-byte chunk of bf16 data in place of its row: own holds
+// Rotate one 16-byte chunk of 16-bit data in place of its row: own holds
 // x[m .. m+7], par the partner elements D/2 away, negated when own lies in
 // the first half, so every output is own * cos + par * sin (the same
 // float64 operations as the paired form).
-template <bool kExact>
-__device__ __forceinline__ bool rotate_unit_bf16(const u32x4& own, const u32x4& par, const double2* __restrict__ cs,
-                                                 int chunks, u32x4& out) {
+template <int kDtype, bool kExact>
+__device__ __forceinline__ bool rotate_unit16(const u32x4& own, const u32x4& par, const double2* __restrict__ cs,
+                                              int chunks, u32x4& out) {
   bool tie = false;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const double2 c0 = cs[(2 * j) * chunks];
     const double2 c1 = cs[(2 * j + 1) * chunks];
-    const double yl = fma(bf16_lo(own[j]), c0.x, bf16_lo(par[j]) * c0.y);
-    const double yh = fma(bf16_hi(own[j]), c1.x, bf16_hi(par[j]) * c1.y);
-    out[j] = kExact ? pack_bf16_exact(yl, yh) : pack_bf16_fast(yl, yh, tie);
+    const f64x2 x = unpack16<kDtype>(own[j]), y = unpack16<kDtype>(par[j]);
+    const double yl = fma(x.x, c0.x, y.x * c0.y);
+    const double yh = fma(x.y, c1.x, y.y * c1.y);
+    out[j] = kExact ? pack16_exact<kDtype>(yl, yh) : pack16_fast<kDtype>(yl, yh, tie);
   }
   return tie;
 }
@@ -258,19 +310,19 @@ __device__ __forceinline__ void rotate_unit_f32(const u32x4& own, const u32x4& p
 }
 
 // Interleaved pairing (element 2i with 2i + 1): both elements of a pair sit
-// in one chunk, so a lane rotates its own chunk with no exchange.  bf16: each
-// dword holds one pair (x[2i] low, x[2i+1] high).
-template <bool kExact>
-__device__ __forceinline__ bool rotate_pairs_bf16(const u32x4& own, const double2* __restrict__ cs, int chunks,
-                                                  u32x4& out) {
+// in one chunk, so a lane rotates its own chunk with no exchange.  16-bit
+// data: each dword holds one pair (x[2i] low, x[2i+1] high).
+template <int kDtype, bool kExact>
+__device__ __forceinline__ bool rotate_pairs16(const u32x4& own, const double2* __restrict__ cs, int chunks,
+                                               u32x4& out) {
   bool tie = false;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const double2 c = cs[j * chunks];
-    const double x1 = bf16_lo(own[j]), x2 = bf16_hi(own[j]);
-    const double y1 = fma(x1, c.x, -(x2 * c.y));
-    const double y2 = fma(x2, c.x, x1 * c.y);
-    out[j] = kExact ? pack_bf16_exact(y1, y2) : pack_bf16_fast(y1, y2, tie);
+    const f64x2 x = unpack16<kDtype>(own[j]);
+    const double y1 = fma(x.x, c.x, -(x.y * c.y));
+    const double y2 = fma(x.y, c.x, x.x * c.y);
+    out[j] = kExact ? pack16_exact<kDtype>(y1, y2) : pack16_fast<kDtype>(y1, y2, tie);
   }
   return tie;
 }
@@ -304,7 +356,8 @@ __device__ __forceinline__ uint32_t div_tok(uint32_t n, uint64_t m) {
 // pairs, consecutive lanes on consecutive chunks.
 template <int kDtype, int kG, int kTPT>
 __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, int32_t* s_pos, double2* s_cs) {
-  constexpr int kVec = (kDtype == ROPE_QK_BF16) ? 8 : 4;  // elements per 16 bytes
+  constexpr bool k16 = kDtype != ROPE_QK_FP32;            // bf16 or fp16 storage
+  constexpr int kVec = k16 ? 8 : 4;                        // elements per 16 bytes
   constexpr int kPPC = kG == kInterleaved ? kVec / 2 : kVec;  // table pairs per chunk
   const int tid = threadIdx.x;
   const cu_ptr cu = (cu_ptr)p.cu;  // address-space cast (C-style: reinterpret_cast cannot change it)
@@ -432,27 +485,28 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
       const int chunks = kG > 0 ? kG : p.chunks;
       const double2* cs = s_cs + tt_of[u] * kPPC * chunks + c_of[u];
       if constexpr (kG == kInterleaved) {
-        if constexpr (kDtype == ROPE_QK_BF16) {
-          if (rotate_pairs_bf16<false>(a[u], cs, chunks, oa[u])) rotate_pairs_bf16<true>(a[u], cs, chunks, oa[u]);
+        if constexpr (k16) {
+          if (rotate_pairs16<kDtype, false>(a[u], cs, chunks, oa[u]))
+            rotate_pairs16<kDtype, true>(a[u], cs, chunks, oa[u]);
         } else {
           rotate_pairs_f32(a[u], cs, chunks, oa[u]);
         }
       } else if constexpr (kG == 0) {
-        if constexpr (kDtype == ROPE_QK_BF16) {
-          if (rotate_bf16<false>(a[u], b[u], cs, chunks, oa[u], ob[u]))
-            rotate_bf16<true>(a[u], b[u], cs, chunks, oa[u], ob[u]);
+        if constexpr (k16) {
+          if (rotate_pair16<kDtype, false>(a[u], b[u], cs, chunks, oa[u], ob[u]))
+            rotate_pair16<kDtype, true>(a[u], b[u], cs, chunks, oa[u], ob[u]);
         } else {
           rotate_f32(a[u], b[u], cs, chunks, oa[u], ob[u]);
         }
       } else {
         // partner chunk from the lane kG away; negated when this chunk is in the first half
-        const uint32_t neg = first[u] ? (kDtype == ROPE_QK_BF16 ? 0x80008000u : 0x80000000u) : 0u;
+        const uint32_t neg = first[u] ? (k16 ? 0x80008000u : 0x80000000u) : 0u;
         u32x4 par;
 #pragma unroll
         for (int d = 0; d < 4; ++d) par[d] = partner_dword<kG>(a[u][d]) ^ neg;
-        if constexpr (kDtype == ROPE_QK_BF16) {
-          if (rotate_unit_bf16<false>(a[u], par, cs, chunks, oa[u]))
-            rotate_unit_bf16<true>(a[u], par, cs, chunks, oa[u]);
+        if constexpr (k16) {
+          if (rotate_unit16<kDtype, false>(a[u], par, cs, chunks, oa[u]))
+            rotate_unit16<kDtype, true>(a[u], par, cs, chunks, oa[u]);
         } else {
           rotate_unit_f32(a[u], par, cs, chunks, oa[u]);
         }
@@ -528,7 +582,7 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
                 int64_t q_st, int64_t q_sh, int64_t k_st, int64_t k_sh, double theta, int dtype,
                 const rope_qk_options* options, void* stream, double sign) {
   const rope_qk_options o = options ? *options : rope_qk_options{};
-  if (dtype != ROPE_QK_FP32 && dtype != ROPE_QK_BF16) return ROPE_QK_ERR_DTYPE;
+  if (dtype != ROPE_QK_FP32 && dtype != ROPE_QK_BF16 && dtype != ROPE_QK_FP16) return ROPE_QK_ERR_DTYPE;
   if (nseq < 0 || T < 0 || Hq < 0 || Hkv < 0 || D < 2 || (D & 1) || D > 2 * kMaxHalf || T > INT32_MAX ||
       nseq >= INT32_MAX || Hq + Hkv > INT32_MAX)
     return ROPE_QK_ERR_SHAPE;
@@ -548,7 +602,7 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
       (Hkv > 0 && (k_st < 0 || k_sh < 0 || rows_overlap(T, Hkv, D, k_st, k_sh))))
     return ROPE_QK_ERR_LAYOUT;
 
-  const int64_t esz = dtype == ROPE_QK_BF16 ? 2 : 4;
+  const int64_t esz = dtype == ROPE_QK_FP32 ? 4 : 2;
   const bool interleaved = o.pairing == ROPE_QK_PAIR_INTERLEAVED;
   const int64_t half = r / 2;  // rotated pairs per head
   // 16-byte chunks holding the first elements of pairs: half a rotated row, or all of it when interleaved
@@ -563,13 +617,13 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
   // task, partner by lane exchange); interleaved: one chunk of whole pairs per task
   const int unit_g = !interleaved && (chunks == 1 || chunks == 2 || chunks == 4) ? static_cast<int>(chunks) : 0;
   const bool chunk_tasks = unit_g != 0 || interleaved;
-  // chunks per lane: 8 amortises the per-tile work best for bf16 unit tiles
+  // chunks per lane: 8 amortises the per-tile work best for 16-bit unit tiles
   // (5% faster than 4 at D = 64) and for interleaved rows of up to 8 chunks;
   // longer interleaved rows (D = 128 bf16) measured 7% faster with 4 (register
   // count 128 -> 90, occupancy 4 -> 5), and fp32 unit tiles would spill at 8
   const int64_t lane_tasks = !chunk_tasks ? kPairTasks
                              : interleaved ? (chunks > kShortRowChunks ? kLongRowTasks : kUnitTasks)
-                             : (dtype == ROPE_QK_BF16 ? kUnitTasks : kLongRowTasks);
+                             : (dtype != ROPE_QK_FP32 ? kUnitTasks : kLongRowTasks);
   const int64_t tasks_per_tok = (Hq + Hkv) * (unit_g ? 2 * chunks : chunks);
   if (tasks_per_tok > kMaxTasksPerToken) return ROPE_QK_ERR_SHAPE;
 
@@ -623,21 +677,17 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
 
   const void* fn;
 #define ROPE_FN(DT, G, TPT) reinterpret_cast<const void*>(&rope_qk_kernel<DT, G, TPT>)
-  if (dtype == ROPE_QK_BF16) {
-    fn = interleaved   ? (lane_tasks == kUnitTasks ? ROPE_FN(ROPE_QK_BF16, kInterleaved, kUnitTasks)
-                                               : ROPE_FN(ROPE_QK_BF16, kInterleaved, kLongRowTasks))
-         : unit_g == 1 ? ROPE_FN(ROPE_QK_BF16, 1, kUnitTasks)
-         : unit_g == 2 ? ROPE_FN(ROPE_QK_BF16, 2, kUnitTasks)
-         : unit_g == 4 ? ROPE_FN(ROPE_QK_BF16, 4, kUnitTasks)
-                       : ROPE_FN(ROPE_QK_BF16, 0, kPairTasks);
-  } else {
-    fn = interleaved   ? (lane_tasks == kUnitTasks ? ROPE_FN(ROPE_QK_FP32, kInterleaved, kUnitTasks)
-                                               : ROPE_FN(ROPE_QK_FP32, kInterleaved, kLongRowTasks))
-         : unit_g == 1 ? ROPE_FN(ROPE_QK_FP32, 1, kLongRowTasks)
-         : unit_g == 2 ? ROPE_FN(ROPE_QK_FP32, 2, kLongRowTasks)
-         : unit_g == 4 ? ROPE_FN(ROPE_QK_FP32, 4, kLongRowTasks)
-                       : ROPE_FN(ROPE_QK_FP32, 0, kPairTasks);
-  }
+#define ROPE_PICK(DT, UNIT)                                                                    \
+  (interleaved   ? (lane_tasks == kUnitTasks ? ROPE_FN(DT, kInterleaved, kUnitTasks)           \
+                                             : ROPE_FN(DT, kInterleaved, kLongRowTasks))        \
+   : unit_g == 1 ? ROPE_FN(DT, 1, UNIT)                                                         \
+   : unit_g == 2 ? ROPE_FN(DT, 2, UNIT)                                                         \
+   : unit_g == 4 ? ROPE_FN(DT, 4, UNIT)                                                         \
+                 : ROPE_FN(DT, 0, kPairTasks))
+  fn = dtype == ROPE_QK_BF16   ? ROPE_PICK(ROPE_QK_BF16, kUnitTasks)
+       : dtype == ROPE_QK_FP16 ? ROPE_PICK(ROPE_QK_FP16, kUnitTasks)
+                               : ROPE_PICK(ROPE_QK_FP32, kLongRowTasks);
+#undef ROPE_PICK
 #undef ROPE_FN
   void* args[] = {&p};
   const hipError_t err = hipLaunchKernel(fn, grid, dim3(kThreads), args, lds, static_cast<hipStream_t>(stream));
@@ -695,7 +745,7 @@ const char* rope_qk_strerror(int status) {
     case ROPE_QK_OK: return "ok";
     case ROPE_QK_ERR_NULL: return "a required pointer is NULL";
     case ROPE_QK_ERR_SHAPE: return "unsupported shape (negative size, D odd/<2/>512, T >= 2^31, too many heads)";
-    case ROPE_QK_ERR_DTYPE: return "unsupported dtype (expected ROPE_QK_FP32 or ROPE_QK_BF16)";
+    case ROPE_QK_ERR_DTYPE: return "unsupported dtype (expected ROPE_QK_FP32, ROPE_QK_BF16 or ROPE_QK_FP16)";
     case ROPE_QK_ERR_ALIGN: return "misaligned: pointers, strides and D/2 must be multiples of 16 bytes";
     case ROPE_QK_ERR_THETA: return "theta must be finite and > 0";
     case ROPE_QK_ERR_LAUNCH: return "HIP kernel launch failed";

@@ -9,10 +9,11 @@ import oracle
 
 FP32_TOL = 1e-5  # max-abs against the float64 oracle
 BF16_MAX_ULP = 1  # bf16 grid steps from the oracle's correctly rounded value
+FP16_MAX_ULP = 1  # fp16 grid steps from the oracle's correctly rounded value
 
 
 def f64(t: torch.Tensor) -> np.ndarray:
-    """Exact float64 copy of a float32/bfloat16 tensor on the host."""
+    """Exact float64 copy of a float32/bfloat16/float16 tensor on the host."""
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
@@ -23,21 +24,24 @@ def bits16(t: torch.Tensor) -> np.ndarray:
 def check_against(gpu_out: torch.Tensor, ref: np.ndarray, what: str = "") -> dict:
     """Element-by-element check of a GPU output against the oracle's float64 values.
 
-    fp32: max |gpu - ref| <= 1e-5.  bf16: at most one bf16 ulp from the
-    oracle's correctly rounded bf16 (and we also count exact matches).
+    fp32: max |gpu - ref| <= 1e-5.  bf16 / fp16: at most one grid step from
+    the oracle's correctly rounded bf16 / fp16 (and we also count exact matches).
     """
     if gpu_out.dtype == torch.float32:
         err = np.abs(f64(gpu_out) - ref)
         m = float(err.max()) if err.size else 0.0
         assert m <= FP32_TOL, f"{what}: fp32 max-abs error {m}"
         return {"max_abs": m}
-    assert gpu_out.dtype == torch.bfloat16
-    want = oracle.bf16_bits(oracle.bf16_rne(ref))
+    if gpu_out.dtype == torch.float16:
+        want, tol, name = oracle.fp16_bits(oracle.fp16_rne(ref)), FP16_MAX_ULP, "fp16"
+    else:
+        assert gpu_out.dtype == torch.bfloat16
+        want, tol, name = oracle.bf16_bits(oracle.bf16_rne(ref)), BF16_MAX_ULP, "bf16"
     got = bits16(gpu_out)
-    d = oracle.ulp_distance_bf16(got, want)
+    d = oracle.ulp_distance_16(got, want)
     m = int(d.max()) if d.size else 0
     exact = float(np.mean(d == 0)) if d.size else 1.0
-    assert m <= BF16_MAX_ULP, f"{what}: bf16 max ulp {m} (exact fraction {exact})"
+    assert m <= tol, f"{what}: {name} max ulp {m} (exact fraction {exact})"
     return {"max_ulp": m, "exact_fraction": exact, "n": int(d.size)}
 
 

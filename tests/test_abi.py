@@ -63,6 +63,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_constants_match_binding():
     assert C["ROPE_QK_FP32"] == P.ROPE_QK_FP32 and C["ROPE_QK_BF16"] == P.ROPE_QK_BF16
+    assert C["ROPE_QK_FP16"] == P.ROPE_QK_FP16
     for name, code in C.items():
         if "_ERR_" in name or name == "ROPE_QK_OK":
             s = P.rope_qk_strerror(code)
@@ -99,6 +100,12 @@ def test_error_codes(which):
     assert f(qst=64 * 13) == C["ROPE_QK_ERR_LAYOUT"]  # tokens overlap
     assert f(kst=64, ksh=64) == C["ROPE_QK_ERR_LAYOUT"]
     assert f(Hq=70000, Hkv=0, qst=70000 * 64) == C["ROPE_QK_ERR_SHAPE"]  # too many 16-byte chunks per token
+    # fp16 shares bf16's 2-byte element checks
+    assert f(D=72, dtype=2) == C["ROPE_QK_ERR_ALIGN"]
+    assert f(q=Q + 8, dtype=2) == C["ROPE_QK_ERR_ALIGN"]
+    assert f(qst=14 * 64 + 4, dtype=2) == C["ROPE_QK_ERR_ALIGN"]
+    assert f(qsh=32, dtype=2) == C["ROPE_QK_ERR_LAYOUT"]
+    assert f(dtype=3) == C["ROPE_QK_ERR_DTYPE"]
 
 
 def test_no_ops_launch_nothing():

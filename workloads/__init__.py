@@ -39,7 +39,7 @@ class Workload:
     Hkv: int
     D: int
     theta: float
-    dtype: str  # "fp32" or "bf16"
+    dtype: str  # "fp32", "bf16" or "fp16"
     cu_seqlens: np.ndarray  # int32 [nseq + 1]
 
     @property
@@ -210,7 +210,7 @@ def qwen25_05b_row_count() -> int:
 def torch_dtype(name: str):
     import torch
 
-    return {"fp32": torch.float32, "bf16": torch.bfloat16}[name]
+    return {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[name]
 
 
 def randn(shape, dtype: str, seed: int, device="cpu"):
