@@ -68,6 +68,7 @@ __all__ = [
     "rotate",
     "rotate_interleaved",
     "cos_sin_freq",
+    "fp32_angles",
     "rope",
     "rope_qk",
     "bf16_rne",
@@ -170,11 +171,34 @@ def cos_sin(pos: np.ndarray, theta: float, D: int, direction: int):
     return cos_sin_freq(pos, inv_freq(theta, D), direction)
 
 
-def cos_sin_freq(pos: np.ndarray, freq: np.ndarray, direction: int):
-    """cos and (direction * sin) of pos * freq for given frequencies, float64 [N, len(freq)]."""
+def fp32_angles(pos: np.ndarray, freq: np.ndarray) -> np.ndarray:
+    """Angles as a float32 frequency table forms them, float64 [N, len(freq)].
+
+    Each frequency is rounded to float32, each position converted to
+    float32, and the angle is their float32 product; every step is one IEEE
+    round-to-nearest-even.  (Compatibility reading: the common tables of
+    models trained this way hold float32 frequencies and multiply in
+    float32; the pages fix neither convention.)
+    """
+    f32 = np.asarray(freq, dtype=np.float64).astype(np.float32)
+    p32 = np.asarray(pos, dtype=np.float64).astype(np.float32)
+    return (p32[:, None] * f32[None, :]).astype(np.float64)
+
+
+def cos_sin_freq(pos: np.ndarray, freq: np.ndarray, direction: int, freq_precision: str = "fp64"):
+    """cos and (direction * sin) of pos * freq for given frequencies, float64 [N, len(freq)].
+
+    freq_precision "fp64": the angle is the float64 product; "fp32": the
+    angle of ``fp32_angles``.  cos and sin are float64 either way.
+    """
     if direction not in (1, -1):
         raise ValueError("direction must be +1 or -1")
-    ang = np.asarray(pos, dtype=np.float64)[:, None] * np.asarray(freq, dtype=np.float64)[None, :]
+    if freq_precision == "fp64":
+        ang = np.asarray(pos, dtype=np.float64)[:, None] * np.asarray(freq, dtype=np.float64)[None, :]
+    elif freq_precision == "fp32":
+        ang = fp32_angles(pos, freq)
+    else:
+        raise ValueError("freq_precision is 'fp64' or 'fp32'")
     return np.cos(ang), direction * np.sin(ang)
 
 
@@ -203,11 +227,12 @@ def rotate(x: np.ndarray, pos: np.ndarray, theta: float, direction: int) -> np.n
     return y
 
 
-def rotate_interleaved(x: np.ndarray, pos: np.ndarray, freq: np.ndarray, direction: int) -> np.ndarray:
+def rotate_interleaved(x: np.ndarray, pos: np.ndarray, freq: np.ndarray, direction: int,
+                       freq_precision: str = "fp64") -> np.ndarray:
     """Rotate rows x[N, H, r] pairing element 2i with 2i + 1 (frequency freq[i])."""
     x = np.asarray(x, dtype=np.float64)
     N, H, r = x.shape
-    c, s = cos_sin_freq(pos, freq, direction)
+    c, s = cos_sin_freq(pos, freq, direction, freq_precision)
     c = c[:, None, :]
     s = s[:, None, :]
     x1 = x[:, :, 0::2]
@@ -219,12 +244,13 @@ def rotate_interleaved(x: np.ndarray, pos: np.ndarray, freq: np.ndarray, directi
 
 
 def rope(x: np.ndarray, cu_seqlens, theta: float, direction: int, *, pos_offset: int = 0, rotary_dim=None,
-         pairing: str = "half", scaling=None) -> np.ndarray:
+         pairing: str = "half", scaling=None, freq_precision: str = "fp64") -> np.ndarray:
     """Rotary embedding of a packed batch x[T, H, D] (float64 result).
 
     Tokens outside [cu[0], cu[nseq]) are returned unchanged, and so are the
     elements [rotary_dim, D) of every head.  ``scaling`` is None or a dict
-    with the keys of ``llama3_inv_freq``.
+    with the keys of ``llama3_inv_freq``; ``freq_precision`` "fp32" forms the
+    angles as ``fp32_angles`` does (after any scaling).
     """
     x = np.asarray(x, dtype=np.float64)
     T, H, D = x.shape
@@ -238,14 +264,14 @@ def rope(x: np.ndarray, cu_seqlens, theta: float, direction: int, *, pos_offset:
     inside = pos >= 0
     if not inside.any():
         return y
-    if pairing == "half" and scaling is None:
+    if pairing == "half" and scaling is None and freq_precision == "fp64":
         y[inside, :, :r] = rotate(x[inside][:, :, :r], pos[inside], theta, direction)
         return y
     freq = inv_freq(theta, r) if scaling is None else llama3_inv_freq(theta, r, **scaling)
     if pairing == "interleaved":
-        y[inside, :, :r] = rotate_interleaved(x[inside][:, :, :r], pos[inside], freq, direction)
+        y[inside, :, :r] = rotate_interleaved(x[inside][:, :, :r], pos[inside], freq, direction, freq_precision)
     else:
-        c, s = cos_sin_freq(pos[inside], freq, direction)
+        c, s = cos_sin_freq(pos[inside], freq, direction, freq_precision)
         c, s = c[:, None, :], s[:, None, :]
         xi = x[inside]
         x1, x2 = xi[:, :, : r // 2], xi[:, :, r // 2: r]

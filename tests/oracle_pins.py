@@ -378,6 +378,56 @@ def pin_llama3_scaling(O):
     assert abs(slope * 1.0 + icpt - 1.0 / 8.0) <= 1e-12 and abs(slope * 4.0 + icpt - 1.0) <= 1e-12
 
 
+# float32-convention angles, worked by hand in exact rational arithmetic
+# (theta = 1e6, D = 128): (pair i, position, the float32 angle, and for
+# contrast the angle with only the frequency rounded, with only the product
+# rounded, and the float64 angle).  i = 0 has frequency 1, so its float32
+# angle is the position rounded to float32 (2^24 + 1 is a tie, to even).
+FP32_ANGLE_CASES = [
+    (1, 77777, 62675.984375, 62675.985769987106, 62675.98828125, 62675.98783752477),
+    (31, 77777, 96.51641082763672, 96.51641442882828, 96.51641845703125, 96.51641621798649),
+    (0, 2 ** 24 + 1, 16777216.0, 16777217.0, 16777216.0, 16777217.0),
+    (0, 2 ** 24 + 3, 16777220.0, 16777219.0, 16777220.0, 16777219.0),
+    (31, 2 ** 24 + 1, 20819.48046875, 20819.481709687738, 20819.482421875, 20819.48209562568),  # position rounded first
+]
+
+
+def pin_fp32_freq_angles(O):
+    """freq_precision='fp32': the hand-worked angles above (a unit vector in
+    pair i rotates to (cos a, sin a)); a power-of-two base whose frequencies
+    and products are exact in float32 gives the float64 result bit for bit;
+    elsewhere the angles move by at most two float32 roundings (2^-23
+    relative), and do move."""
+    theta, D = 1e6, 128
+    for i, p, a32, *_ in FP32_ANGLE_CASES:
+        for pairing in ("half", "interleaved"):
+            x = np.zeros((1, 1, D))
+            j1, j2 = (i, i + D // 2) if pairing == "half" else (2 * i, 2 * i + 1)
+            x[0, 0, j1] = 1.0
+            y = O.rope(x, [0, 1], theta, 1, pos_offset=p, pairing=pairing, freq_precision="fp32")
+            assert abs(y[0, 0, j1] - math.cos(a32)) <= 4 * F64_EPS, (i, p, pairing)
+            assert abs(y[0, 0, j2] - math.sin(a32)) <= 4 * F64_EPS, (i, p, pairing)
+    rng = _rng(23)
+    x = rng.standard_normal((64, 2, 4))
+    for off in (0, 2 ** 24 - 64):  # theta = 2^16, D = 4: frequencies 1 and 2^-8
+        a = O.rope(x, [0, 64], 2.0 ** 16, 1, pos_offset=off, freq_precision="fp32")
+        b = O.rope(x, [0, 64], 2.0 ** 16, 1, pos_offset=off)
+        assert np.array_equal(a, b), off
+    pos = rng.integers(0, 2 ** 21, size=300)
+    x = rng.standard_normal((300, 1, D))
+    ys = []
+    for fp in ("fp32", "fp64"):
+        ys.append(np.stack([O.rope(x[n:n + 1], [0, 1], theta, 1, pos_offset=int(pos[n]), freq_precision=fp)[0]
+                            for n in range(300)]))
+    y32, y64 = ys
+    ang_max = pos.astype(np.float64)[:, None] * O.inv_freq(theta, D)[None, :]  # [N, D/2]
+    norm = np.hypot(x[:, 0, : D // 2], x[:, 0, D // 2:])
+    bound = norm * ang_max * 2.0 ** -23 * 1.01 + 1e-12
+    dev = np.hypot(y32[:, 0, : D // 2] - y64[:, 0, : D // 2], y32[:, 0, D // 2:] - y64[:, 0, D // 2:])
+    assert np.all(dev <= bound)
+    assert np.count_nonzero(dev > 1e-9) > 100
+
+
 ALL_PINS = [
     pin_positions,
     pin_inv_freq,
@@ -396,4 +446,5 @@ ALL_PINS = [
     pin_rotary_dim,
     pin_interleaved_roformer,
     pin_llama3_scaling,
+    pin_fp32_freq_angles,
 ]

@@ -157,6 +157,21 @@ MUTANTS = {
     # partial rotary dim
     "partial_uses_full_head_freqs": ("rope", lambda *a, **kw: _rope_partial_full_freqs(*a, **kw)),
     "partial_rotates_whole_head": ("rope", lambda x, cu, th, d, **kw: _orig_rope(x, cu, th, d, **{**kw, "rotary_dim": None})),
+    # float32-convention angles
+    "fp32_mode_ignored": ("fp32_angles", lambda pos, f: np.asarray(pos, np.float64)[:, None] * np.asarray(f)[None, :]),
+    "fp32_only_frequencies_rounded": (
+        "fp32_angles",
+        lambda pos, f: np.asarray(pos, np.float64)[:, None] * np.asarray(f).astype(np.float32).astype(np.float64)[None, :],
+    ),
+    "fp32_only_product_rounded": (
+        "fp32_angles",
+        lambda pos, f: (np.asarray(pos, np.float64)[:, None] * np.asarray(f)[None, :]).astype(np.float32).astype(np.float64),
+    ),
+    "fp32_position_not_rounded": (
+        "fp32_angles",
+        lambda pos, f: (np.asarray(pos, np.float64)[:, None] * np.asarray(f).astype(np.float32).astype(np.float64)[None, :])
+        .astype(np.float32).astype(np.float64),
+    ),
     # the fused call
     "k_left_unrotated": ("rope_qk", lambda q, k, cu, th, d: (_orig_rope(q, cu, th, d), np.asarray(k, np.float64).copy())),
 }
