@@ -88,6 +88,10 @@ extern "C" {
 #define ROPE_QK_SCALING_NONE 0
 #define ROPE_QK_SCALING_LLAMA3 1
 
+/* how angles are formed (rope_qk_options.freq_precision) */
+#define ROPE_QK_FREQ_FP64 0  /* float64 frequency times the position, in float64 (the default) */
+#define ROPE_QK_FREQ_FP32 1  /* float32 frequency times the float32 position, in float32 */
+
 /*
  * Forward rotation, in place, of q and k in ONE kernel launch.
  *
@@ -152,6 +156,15 @@ int rope_qk_bwd(void* dq, void* dk, const int32_t* cu_seqlens, int64_t nseq, int
  *                s = (L / w - low_freq_factor) / (high_freq_factor - low_freq_factor),
  *                (1 - s) f / factor + s f.  Needs factor > 0, L > 0 and
  *                high_freq_factor > low_freq_factor > 0 (Llama 3.1: 8, 8192, 4, 1).
+ *   freq_precision
+ *                ROPE_QK_FREQ_FP32: form each angle the way float32 frequency
+ *                tables do, for models trained with them: the frequency (after
+ *                any scaling) rounded to float32, the position converted to
+ *                float32, their float32 product; each step rounds to nearest
+ *                even.  At positions near 5e5 this moves angles by up to
+ *                ~0.03 rad from the float64 angles.  cos, sin and the rotation
+ *                stay float64, rounded once.  The pages fix neither convention.
+ *   reserved     must be 0.
  */
 typedef struct rope_qk_options {
   int64_t pos_offset;
@@ -162,6 +175,8 @@ typedef struct rope_qk_options {
   double low_freq_factor;
   double high_freq_factor;
   double original_max_position;
+  int32_t freq_precision;
+  int32_t reserved;
 } rope_qk_options;
 
 /*

@@ -11,6 +11,8 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     ROPE_QK_BF16,
     ROPE_QK_FP16,
+    ROPE_QK_FREQ_FP32,
+    ROPE_QK_FREQ_FP64,
     ROPE_QK_FP32,
     ROPE_QK_PAIR_HALF,
     ROPE_QK_PAIR_INTERLEAVED,

@@ -22,6 +22,8 @@ ROPE_QK_PAIR_HALF = 0
 ROPE_QK_PAIR_INTERLEAVED = 1
 ROPE_QK_SCALING_NONE = 0
 ROPE_QK_SCALING_LLAMA3 = 1
+ROPE_QK_FREQ_FP64 = 0
+ROPE_QK_FREQ_FP32 = 1
 
 # names exported by include/rope_qk.h
 EXPORTS = ("rope_qk_fwd", "rope_qk_bwd", "rope_qk_fwd_opt", "rope_qk_bwd_opt", "rope_qk_positions",
@@ -40,13 +42,18 @@ class RopeQKOptions(ctypes.Structure):
         ("low_freq_factor", ctypes.c_double),
         ("high_freq_factor", ctypes.c_double),
         ("original_max_position", ctypes.c_double),
+        ("freq_precision", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
-def make_options(pos_offset: int = 0, rotary_dim: int = 0, interleaved: bool = False, llama3=None) -> RopeQKOptions:
+def make_options(pos_offset: int = 0, rotary_dim: int = 0, interleaved: bool = False, llama3=None,
+                 freq_fp32: bool = False) -> RopeQKOptions:
     """Options struct from keyword values; llama3 is None or a dict with factor,
-    low_freq_factor, high_freq_factor and original_max_position."""
+    low_freq_factor, high_freq_factor and original_max_position; freq_fp32
+    selects ROPE_QK_FREQ_FP32 angles."""
     o = RopeQKOptions()
+    o.freq_precision = ROPE_QK_FREQ_FP32 if freq_fp32 else ROPE_QK_FREQ_FP64
     o.pos_offset = int(pos_offset)
     o.rotary_dim = int(rotary_dim or 0)
     o.pairing = ROPE_QK_PAIR_INTERLEAVED if interleaved else ROPE_QK_PAIR_HALF
@@ -166,22 +173,23 @@ def _rotate(entry: str, q, k, cu_seqlens, theta: float, stream=None, options=Non
     _check(status)
 
 
-def _options_or_none(pos_offset, rotary_dim, interleaved, llama3):
-    if not pos_offset and not rotary_dim and not interleaved and llama3 is None:
+def _options_or_none(pos_offset, rotary_dim, interleaved, llama3, freq_fp32):
+    if not pos_offset and not rotary_dim and not interleaved and llama3 is None and not freq_fp32:
         return None
-    return make_options(pos_offset, rotary_dim, interleaved, llama3)
+    return make_options(pos_offset, rotary_dim, interleaved, llama3, freq_fp32)
 
 
 def rope_qk_fwd(q, k, cu_seqlens, theta: float, stream=None, *, pos_offset: int = 0, rotary_dim: int = 0,
-                interleaved: bool = False, llama3=None):
+                interleaved: bool = False, llama3=None, freq_fp32: bool = False):
     """Rotate q [T, Hq, D] and k [T, Hkv, D] in place (one kernel launch).
 
     cu_seqlens: int32 [nseq + 1] device tensor of packed-sequence offsets.
     stream: a torch.cuda.Stream (default: the current stream of q's device).
     Keyword options (see rope_qk_options in include/rope_qk.h): pos_offset for
-    segment 0, rotary_dim, interleaved pairing, llama3 frequency rescaling.
+    segment 0, rotary_dim, interleaved pairing, llama3 frequency rescaling,
+    freq_fp32 for float32-convention angles.
     """
-    opts = _options_or_none(pos_offset, rotary_dim, interleaved, llama3)
+    opts = _options_or_none(pos_offset, rotary_dim, interleaved, llama3, freq_fp32)
     if opts is None:
         _rotate("rope_qk_fwd", q, k, cu_seqlens, theta, stream)
     else:
@@ -189,9 +197,9 @@ def rope_qk_fwd(q, k, cu_seqlens, theta: float, stream=None, *, pos_offset: int 
 
 
 def rope_qk_bwd(dq, dk, cu_seqlens, theta: float, stream=None, *, pos_offset: int = 0, rotary_dim: int = 0,
-                interleaved: bool = False, llama3=None):
+                interleaved: bool = False, llama3=None, freq_fp32: bool = False):
     """Backward of rope_qk_fwd, in place on the incoming gradients dq and dk."""
-    opts = _options_or_none(pos_offset, rotary_dim, interleaved, llama3)
+    opts = _options_or_none(pos_offset, rotary_dim, interleaved, llama3, freq_fp32)
     if opts is None:
         _rotate("rope_qk_bwd", dq, dk, cu_seqlens, theta, stream)
     else:

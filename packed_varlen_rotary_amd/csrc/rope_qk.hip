@@ -116,6 +116,7 @@ struct RopeParams {
   int32_t half;            // D / 2
   int32_t half_bytes;      // (D / 2) * element size
   int32_t pos_offset;      // added to the positions of segment 0
+  int32_t freq_fp32;       // 1: angles as float32 tables form them (inv_freq already rounded to float32)
   double sign;             // +1 forward, -1 backward
   double inv_freq[kMaxHalf];
 };
@@ -468,7 +469,10 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
         if (i_e[v] == 0) s_pos[tt_e[v]] = pos;
         if (pos >= 0) {
           double sn, cs;
-          rope_sincos(static_cast<double>(pos) * f[v], &sn, &cs);
+          // float32 convention: float32 position times float32 frequency, one rounding
+          const double ang = p.freq_fp32 ? static_cast<double>(static_cast<float>(pos) * static_cast<float>(f[v]))
+                                         : static_cast<double>(pos) * f[v];
+          rope_sincos(ang, &sn, &cs);
           s_cs[cs_slot(tt_e[v], i_e[v], kPPC, p.chunks)] = make_double2(cs, p.sign * sn);
         }
       }
@@ -590,7 +594,8 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
   const int64_t r = o.rotary_dim == 0 ? D : o.rotary_dim;  // elements of each head that are rotated
   if (o.pos_offset < 0 || o.pos_offset > INT32_MAX - T || r < 2 || (r & 1) || r > D ||
       (o.pairing != ROPE_QK_PAIR_HALF && o.pairing != ROPE_QK_PAIR_INTERLEAVED) ||
-      (o.scaling != ROPE_QK_SCALING_NONE && o.scaling != ROPE_QK_SCALING_LLAMA3))
+      (o.scaling != ROPE_QK_SCALING_NONE && o.scaling != ROPE_QK_SCALING_LLAMA3) ||
+      (o.freq_precision != ROPE_QK_FREQ_FP64 && o.freq_precision != ROPE_QK_FREQ_FP32) || o.reserved != 0)
     return ROPE_QK_ERR_OPTION;
   if (o.scaling == ROPE_QK_SCALING_LLAMA3 &&
       !(o.factor > 0.0 && isfinite(o.factor) && o.original_max_position > 0.0 && isfinite(o.original_max_position) &&
@@ -661,8 +666,11 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
   p.half = static_cast<int32_t>(half);
   p.half_bytes = static_cast<int32_t>(half * esz);
   p.pos_offset = static_cast<int32_t>(o.pos_offset);
+  p.freq_fp32 = o.freq_precision == ROPE_QK_FREQ_FP32;
   p.sign = sign;
   make_inv_freq(theta, r, o, p.inv_freq);
+  if (p.freq_fp32)
+    for (int i = 0; i < kMaxHalf; ++i) p.inv_freq[i] = static_cast<double>(static_cast<float>(p.inv_freq[i]));
 
   // LDS: the table of the tokens one tile touches; for pair tiles, padded so
   // that at most the measured best number of workgroups share a compute unit
@@ -750,7 +758,8 @@ const char* rope_qk_strerror(int status) {
     case ROPE_QK_ERR_THETA: return "theta must be finite and > 0";
     case ROPE_QK_ERR_LAUNCH: return "HIP kernel launch failed";
     case ROPE_QK_ERR_LAYOUT: return "negative strides or overlapping rows";
-    case ROPE_QK_ERR_OPTION: return "an option is out of range (pos_offset, rotary_dim, pairing or scaling)";
+    case ROPE_QK_ERR_OPTION:
+      return "an option is out of range (pos_offset, rotary_dim, pairing, scaling, freq_precision or reserved)";
     default: return "unknown status";
   }
 }

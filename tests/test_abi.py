@@ -179,6 +179,13 @@ def test_option_error_codes(which):
     o = mk()
     o.scaling = 7
     assert f(o) == E
+    o = mk()
+    o.freq_precision = 2
+    assert f(o) == E
+    o = mk()
+    o.reserved = 1
+    assert f(o) == E
+    assert f(mk(freq_fp32=True), cu=0) == C["ROPE_QK_ERR_NULL"]
     for bad in (dict(factor=0.0), dict(high_freq_factor=1.0), dict(original_max_position=0.0),
                 dict(low_freq_factor=0.0), dict(factor=float("inf"))):
         assert f(mk(llama3={**LLAMA3, **bad})) == E, bad
@@ -212,3 +219,4 @@ def test_pairing_and_scaling_constants_match_binding():
     assert C["ROPE_QK_PAIR_HALF"] == P.ROPE_QK_PAIR_HALF and C["ROPE_QK_PAIR_INTERLEAVED"] == P.ROPE_QK_PAIR_INTERLEAVED
     assert C["ROPE_QK_SCALING_NONE"] == P.ROPE_QK_SCALING_NONE
     assert C["ROPE_QK_SCALING_LLAMA3"] == P.ROPE_QK_SCALING_LLAMA3
+    assert C["ROPE_QK_FREQ_FP64"] == P.ROPE_QK_FREQ_FP64 and C["ROPE_QK_FREQ_FP32"] == P.ROPE_QK_FREQ_FP32

@@ -1,6 +1,7 @@
 """Variants through the C ABI vs the fp64 oracle (needs an MI355X): position
-offset of a token shard, partial rotary dim, interleaved pairing and the
-Llama 3.1 frequency rescaling, each alone and combined, forward and backward.
+offset of a token shard, partial rotary dim, interleaved pairing, the
+Llama 3.1 frequency rescaling and float32-convention angles, each alone and
+combined, forward and backward.
 """
 
 import numpy as np
@@ -29,12 +30,17 @@ def rotate(direction, q, k, cu, theta, **opts):
 def oracle_opts(opts):
     """rope_qk_fwd keyword options -> oracle.rope keyword options."""
     return dict(pos_offset=opts.get("pos_offset", 0), rotary_dim=opts.get("rotary_dim") or None,
-                pairing="interleaved" if opts.get("interleaved") else "half", scaling=opts.get("llama3"))
+                pairing="interleaved" if opts.get("interleaved") else "half", scaling=opts.get("llama3"),
+                freq_precision="fp32" if opts.get("freq_fp32") else "fp64")
 
 
 def check_case(T, Hq, Hkv, D, dt, cu, theta, direction, seed, **opts):
     q = W.randn((T, Hq, D), dt, seed=seed, device=DEV)
     k = W.randn((T, Hkv, D), dt, seed=seed + 1, device=DEV)
+    return check_case_tensors(q, k, cu, theta, direction, **opts)
+
+
+def check_case_tensors(q, k, cu, theta, direction, **opts):
     xq, xk = f64(q), f64(k)
     rotate(direction, q, k, cu, theta, **opts)
     torch.cuda.synchronize()
@@ -188,3 +194,50 @@ def test_backward_undoes_forward_with_options():
     P.rope_qk_bwd(q, k, cu, 5e5, **opts)
     torch.cuda.synchronize()
     assert float((q - q0).abs().max()) <= 1e-6 and float((k - k0).abs().max()) <= 1e-6
+
+
+# ---------------------------------------------------------------------------
+# float32-convention angles
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32", "fp16"])
+@pytest.mark.parametrize("direction", [1, -1])
+def test_fp32_angles_long_positions(dt, direction):
+    """Positions around 5e5 (an offset shard of a long sequence), where the
+    float32 angles differ from the float64 ones by up to ~0.03 rad."""
+    T, Hq, Hkv, D = 700, 8, 2, 128
+    q = W.randn((T, Hq, D), dt, seed=61, device=DEV)
+    k = W.randn((T, Hkv, D), dt, seed=62, device=DEV)
+    q64, k64 = q.clone(), k.clone()
+    s = check_case_tensors(q, k, [0, 300, T], 5e5, direction, pos_offset=500_000, freq_fp32=True)
+    if dt != "fp32":
+        assert s[0]["exact_fraction"] == 1.0 and s[1]["exact_fraction"] == 1.0, s
+    rotate(direction, q64, k64, [0, 300, T], 5e5, pos_offset=500_000)
+    assert not torch.equal(q, q64)  # the two conventions really differ here
+
+
+def test_fp32_angles_across_2_pow_24():
+    """Positions 2^24 - 150 .. 2^24 + 150: past 2^24 the float32 position itself rounds."""
+    T = 300
+    s = check_case(T, 4, 2, 64, "bf16", [0, T], 1e6, 1, 63, pos_offset=2 ** 24 - 150, freq_fp32=True)
+    assert s[0]["exact_fraction"] == 1.0 and s[1]["exact_fraction"] == 1.0, s
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_fp32_angles_with_every_option(dt):
+    cu = [0, 100, 100, 620, 700]
+    check_case(720, 6, 2, 128, dt, cu, 5e5, 1, 64, pos_offset=40960, rotary_dim=64, interleaved=True,
+               llama3=LLAMA3, freq_fp32=True)
+
+
+def test_fp32_angles_equal_fp64_where_exact():
+    """Base 2^16 at D = 4: frequencies 1 and 2^-8 and every product below 2^24
+    are exact in float32, so both conventions give identical results."""
+    T = 512
+    q = W.randn((T, 3, 4 * 8), "fp32", seed=65, device=DEV)[:, :, :4].contiguous()
+    k = torch.empty((T, 0, 4), dtype=q.dtype, device=DEV)
+    a, b = q.clone(), q.clone()
+    # D = 4 fp32 has 8-byte half rows: rotate_half needs 16; interleaved pairs need r * 4 = 16 bytes
+    rotate(1, a, k, [0, T], 2.0 ** 16, interleaved=True, freq_fp32=True, pos_offset=2 ** 24 - T)
+    rotate(1, b, k, [0, T], 2.0 ** 16, interleaved=True, pos_offset=2 ** 24 - T)
+    assert torch.equal(a, b)
