@@ -78,7 +78,8 @@ extern "C" {
 #define ROPE_QK_ERR_THETA -5     /* theta not finite or <= 0 */
 #define ROPE_QK_ERR_LAUNCH -6    /* the HIP launch itself failed */
 #define ROPE_QK_ERR_LAYOUT -7    /* negative strides, or a tensor whose rows overlap */
-#define ROPE_QK_ERR_OPTION -8    /* a field of rope_qk_options out of range */
+#define ROPE_QK_ERR_OPTION -8    /* a field of rope_qk_options out of range (or eps, for the norm calls) */
+#define ROPE_QK_ERR_WORKSPACE -9 /* workspace NULL or smaller than rope_qk_norm_bwd_workspace_bytes */
 
 /* pairing of the rotated elements of a head (rope_qk_options.pairing) */
 #define ROPE_QK_PAIR_HALF 0         /* element i with element i + r/2 ("rotate_half"; the default) */
@@ -192,6 +193,92 @@ int rope_qk_bwd_opt(void* dq, void* dk, const int32_t* cu_seqlens, int64_t nseq,
                     int64_t Hq, int64_t Hkv, int64_t D, int64_t q_stride_t, int64_t q_stride_h,
                     int64_t k_stride_t, int64_t k_stride_h, double theta, int dtype,
                     const rope_qk_options* options, void* stream);
+
+/*
+ * Per-head RMSNorm followed by the rotation, forward, in ONE kernel launch.
+ *
+ * "Chronicals: A High-Performance Framework for LLM Fine-Tuning with 3.51x
+ * Speedup over Unsloth", abstract, optimisation (1): RMSNorm and QK-RoPE are
+ * among its fused kernels.  The pages give no formula; the reading is RMSNorm
+ * (Zhang and Sennrich, 2019) of each head of q and of k on its own, placed
+ * before the rotation as in Qwen3 (q_norm / k_norm), then the rotation of
+ * rope_qk_fwd_opt.  For every token inside a sequence and every head, with
+ * w = q_weight for q and k_weight for k:
+ *
+ *   r = 1 / sqrt(mean_j x_j^2 + eps),   n_j = x_j * r * w_j,   y = rope(n)
+ *
+ * evaluated in float64 and rounded once to the storage type.  Tokens outside
+ * [cu_seqlens[0], cu_seqlens[nseq]) are copied unchanged from the input to a
+ * separate output, and not written when the output is the input.
+ *
+ *   q, k           inputs [T, Hq, D], [T, Hkv, D] (device; NULL only without heads)
+ *   q_out, k_out   outputs of the same shapes; each may be exactly its input
+ *                  (same pointer and strides: in place) or must not overlap
+ *                  any input
+ *   q_weight, k_weight
+ *                  device float32 [D], 16-byte aligned (NULL only without heads)
+ *   eps            finite, > 0 (else ROPE_QK_ERR_OPTION; Qwen3 uses 1e-6)
+ *   strides        host int64[8], element strides: q (t, h), k (t, h),
+ *                  q_out (t, h), k_out (t, h); unit stride along D
+ *   options        as for rope_qk_fwd_opt, except that rotary_dim must be 0 or
+ *                  D (the norm covers the whole head)
+ *   D              D * element size must be 32, 64, ..., 1024 bytes (a whole
+ *                  head is a power-of-two number of 16-byte chunks, at most
+ *                  64); Hq + Hkv <= 65535; else ROPE_QK_ERR_SHAPE
+ *
+ * Other arguments, alignment, errors and stream semantics as rope_qk_fwd.
+ * T == 0 or no heads is a no-op; so is nseq == 0 when both outputs are their
+ * inputs.
+ */
+int rope_qk_norm_fwd(const void* q, const void* k, void* q_out, void* k_out, const float* q_weight,
+                     const float* k_weight, double eps, const int32_t* cu_seqlens, int64_t nseq, int64_t T,
+                     int64_t Hq, int64_t Hkv, int64_t D, const int64_t* strides, double theta, int dtype,
+                     const rope_qk_options* options, void* stream);
+
+/*
+ * Bytes of device workspace rope_qk_norm_bwd needs for these sizes (>= 0), or
+ * a negative status (ROPE_QK_ERR_DTYPE, ROPE_QK_ERR_SHAPE): 16 * D bytes for
+ * every tile of rows_per_tile = 1024 / (D * element size / 16) rows, plus
+ * 16 * D for each of up to 256 slices.
+ */
+int64_t rope_qk_norm_bwd_workspace_bytes(int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int dtype);
+
+/*
+ * Backward of rope_qk_norm_fwd.  Inputs: dq_out, dk_out (the gradients of the
+ * forward's outputs) and q, k (the forward's INPUTS, which the caller keeps);
+ * outputs: dq, dk (gradients of the inputs; each may be exactly its dq_out /
+ * dk_out, i.e. in place, or must not overlap any input) and dq_weight,
+ * dk_weight (device float32 [D], 16-byte aligned, overwritten with the
+ * gradient of q_weight / k_weight summed over every normalised head; NULL
+ * only without heads).  With n, r as in the forward and dn = rope^T(dy) (the
+ * rotation by -angle), g_j = dn_j w_j:
+ *
+ *   dx_j = r * (g_j - x_j * r^2 * (sum_k g_k x_k) / D),   dw_j = sum dn_j x_j r
+ *
+ * in float64, dx rounded once to the storage type, dw once to float32; the
+ * sum over heads runs in a fixed order, so repeated calls give identical
+ * bits.  Tokens outside every sequence pass dq_out / dk_out through to a
+ * separate dq / dk (as the forward's identity there) and add nothing to the
+ * weight gradients.
+ *
+ *   workspace, workspace_size
+ *                  device memory of at least rope_qk_norm_bwd_workspace_bytes
+ *                  bytes, 16-byte aligned, owned by the caller; its contents
+ *                  on entry do not matter, and it must not be used by another
+ *                  call until this one has completed on `stream`
+ *                  (else ROPE_QK_ERR_WORKSPACE / ROPE_QK_ERR_ALIGN)
+ *   strides        host int64[12], element strides: dq_out, dk_out, q, k, dq,
+ *                  dk, each (t, h)
+ *
+ * Everything else as rope_qk_norm_fwd (same eps, weights, options, theta).
+ * Up to three launches on `stream`; with T == 0 or no heads only the weight
+ * gradients are written (zeros).
+ */
+int rope_qk_norm_bwd(const void* dq_out, const void* dk_out, const void* q, const void* k, void* dq, void* dk,
+                     const float* q_weight, const float* k_weight, double eps, float* dq_weight, float* dk_weight,
+                     void* workspace, int64_t workspace_size, const int32_t* cu_seqlens, int64_t nseq, int64_t T,
+                     int64_t Hq, int64_t Hkv, int64_t D, const int64_t* strides, double theta, int dtype,
+                     const rope_qk_options* options, void* stream);
 
 /*
  * The positions the rotation kernels use, for inspection: writes, for every

@@ -26,6 +26,9 @@ from ._lib import (  # noqa: F401
     rope_qk_bwd_opt,
     rope_qk_fwd,
     rope_qk_fwd_opt,
+    rope_qk_norm_bwd,
+    rope_qk_norm_bwd_workspace_bytes,
+    rope_qk_norm_fwd,
     rope_qk_positions,
     rope_qk_strerror,
 )
@@ -35,6 +38,9 @@ __all__ = [
     "rope_qk_bwd",
     "rope_qk_fwd_opt",
     "rope_qk_bwd_opt",
+    "rope_qk_norm_fwd",
+    "rope_qk_norm_bwd",
+    "rope_qk_norm_bwd_workspace_bytes",
     "RopeQKOptions",
     "make_options",
     "rope_qk_positions",

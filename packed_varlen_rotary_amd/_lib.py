@@ -26,8 +26,8 @@ ROPE_QK_FREQ_FP64 = 0
 ROPE_QK_FREQ_FP32 = 1
 
 # names exported by include/rope_qk.h
-EXPORTS = ("rope_qk_fwd", "rope_qk_bwd", "rope_qk_fwd_opt", "rope_qk_bwd_opt", "rope_qk_positions",
-           "rope_qk_strerror")
+EXPORTS = ("rope_qk_fwd", "rope_qk_bwd", "rope_qk_fwd_opt", "rope_qk_bwd_opt", "rope_qk_norm_fwd",
+           "rope_qk_norm_bwd", "rope_qk_norm_bwd_workspace_bytes", "rope_qk_positions", "rope_qk_strerror")
 
 
 class RopeQKOptions(ctypes.Structure):
@@ -102,6 +102,17 @@ def load():
             fn = getattr(lib, name)
             fn.argtypes = rot[:-1] + [ctypes.POINTER(RopeQKOptions), vp]
             fn.restype = ctypes.c_int
+        dbl = ctypes.c_double
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        optp = ctypes.POINTER(RopeQKOptions)
+        lib.rope_qk_norm_fwd.argtypes = [vp, vp, vp, vp, vp, vp, dbl, vp, i64, i64, i64, i64, i64, i64p, dbl,
+                                         ctypes.c_int, optp, vp]
+        lib.rope_qk_norm_fwd.restype = ctypes.c_int
+        lib.rope_qk_norm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, dbl, vp, vp, vp, i64, vp, i64, i64, i64,
+                                         i64, i64, i64p, dbl, ctypes.c_int, optp, vp]
+        lib.rope_qk_norm_bwd.restype = ctypes.c_int
+        lib.rope_qk_norm_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+        lib.rope_qk_norm_bwd_workspace_bytes.restype = ctypes.c_int64
         lib.rope_qk_positions.argtypes = [vp, i64, i64, vp, vp]
         lib.rope_qk_positions.restype = ctypes.c_int
         lib.rope_qk_strerror.argtypes = [ctypes.c_int]
@@ -234,3 +245,116 @@ def rope_qk_positions(cu_seqlens, T: int, out=None, stream=None):
         )
     _check(status)
     return out
+
+
+# ---------------------------------------------------------------------------
+# per-head RMSNorm + rotation
+# ---------------------------------------------------------------------------
+
+def _check_rows(name, t, ref):
+    if t.dim() != 3 or not t.is_cuda or (t.shape[2] > 1 and t.stride(2) != 1):
+        raise ValueError(f"{name} must be a [T, H, D] GPU tensor, unit-stride along D")
+    if t.dtype != ref.dtype or t.device != ref.device or t.shape[0] != ref.shape[0] or t.shape[2] != ref.shape[2]:
+        raise ValueError(f"{name} must match q's dtype, device, T and D")
+
+
+def _check_weight(name, w, D, device):
+    import torch
+
+    if w is None:
+        return None
+    if w.dtype != torch.float32 or w.dim() != 1 or w.numel() != D or not w.is_contiguous() or w.device != device:
+        raise ValueError(f"{name} must be a contiguous float32 [D] tensor on q's device")
+    return ctypes.c_void_p(w.data_ptr())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _strides(*ts):
+    vals = []
+    for t in ts:
+        vals += [t.stride(0), t.stride(1)]
+    return (ctypes.c_int64 * len(vals))(*vals)
+
+
+def rope_qk_norm_fwd(q, k, q_weight, k_weight, eps: float, cu_seqlens, theta: float, q_out=None, k_out=None,
+                     stream=None, *, pos_offset: int = 0, interleaved: bool = False, llama3=None,
+                     freq_fp32: bool = False):
+    """Per-head RMSNorm of q [T, Hq, D] and k [T, Hkv, D] followed by the rotation, one launch.
+
+    q_weight, k_weight: float32 [D].  q_out / k_out: output tensors of the
+    same shapes (default: q and k themselves, i.e. in place).  Returns
+    (q_out, k_out).  Options as rope_qk_fwd (no rotary_dim: the norm covers
+    the whole head).
+    """
+    import torch
+
+    lib = load()
+    q_out = q if q_out is None else q_out
+    k_out = k if k_out is None else k_out
+    for name, t in (("k", k), ("q_out", q_out), ("k_out", k_out)):
+        _check_rows(name, t, q)
+    _check_rows("q", q, q)
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor")
+    T, Hq, D = q.shape
+    opts = make_options(pos_offset, 0, interleaved, llama3, freq_fp32)
+    with torch.cuda.device(q.device):
+        status = lib.rope_qk_norm_fwd(
+            _ptr(q), _ptr(k), _ptr(q_out), _ptr(k_out),
+            _check_weight("q_weight", q_weight, D, q.device), _check_weight("k_weight", k_weight, D, q.device),
+            float(eps), _ptr(cu_seqlens), cu_seqlens.numel() - 1, T, Hq, k.shape[1], D,
+            _strides(q, k, q_out, k_out), float(theta), _dtype_code(q), ctypes.byref(opts),
+            _stream_ptr(q.device, stream))
+    _check(status)
+    return q_out, k_out
+
+
+def rope_qk_norm_bwd_workspace_bytes(T: int, Hq: int, Hkv: int, D: int, dtype_code: int) -> int:
+    n = load().rope_qk_norm_bwd_workspace_bytes(int(T), int(Hq), int(Hkv), int(D), int(dtype_code))
+    if n < 0:
+        _check(int(n))
+    return int(n)
+
+
+def rope_qk_norm_bwd(dq_out, dk_out, q, k, q_weight, k_weight, eps: float, cu_seqlens, theta: float, dq=None,
+                     dk=None, dq_weight=None, dk_weight=None, workspace=None, stream=None, *, pos_offset: int = 0,
+                     interleaved: bool = False, llama3=None, freq_fp32: bool = False):
+    """Backward of rope_qk_norm_fwd: returns (dq, dk, dq_weight, dk_weight).
+
+    q, k are the forward's INPUTS.  dq / dk default to dq_out / dk_out (in
+    place); dq_weight / dk_weight default to new float32 [D] tensors; the
+    workspace (uint8 device tensor) is allocated when not given.
+    """
+    import torch
+
+    lib = load()
+    dq = dq_out if dq is None else dq
+    dk = dk_out if dk is None else dk
+    for name, t in (("dk_out", dk_out), ("k", k), ("dq", dq), ("dk", dk), ("dq_out", dq_out)):
+        _check_rows(name, t, q)
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor")
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    code = _dtype_code(q)
+    if dq_weight is None:
+        dq_weight = torch.empty(D, dtype=torch.float32, device=q.device)
+    if dk_weight is None:
+        dk_weight = torch.empty(D, dtype=torch.float32, device=q.device)
+    need = rope_qk_norm_bwd_workspace_bytes(T, Hq, Hkv, D, code)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    opts = make_options(pos_offset, 0, interleaved, llama3, freq_fp32)
+    with torch.cuda.device(q.device):
+        status = lib.rope_qk_norm_bwd(
+            _ptr(dq_out), _ptr(dk_out), _ptr(q), _ptr(k), _ptr(dq), _ptr(dk),
+            _check_weight("q_weight", q_weight, D, q.device), _check_weight("k_weight", k_weight, D, q.device),
+            float(eps), _check_weight("dq_weight", dq_weight, D, q.device),
+            _check_weight("dk_weight", dk_weight, D, q.device), _ptr(workspace), workspace.numel(),
+            _ptr(cu_seqlens), cu_seqlens.numel() - 1, T, Hq, Hkv, D, _strides(dq_out, dk_out, q, k, dq, dk),
+            float(theta), code, ctypes.byref(opts), _stream_ptr(q.device, stream))
+    _check(status)
+    return dq, dk, dq_weight, dk_weight

@@ -13,7 +13,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "rope_qk.hip")
+SRCS = [os.path.join(PKG, "csrc", n) for n in ("rope_qk.hip", "rope_qk_norm.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librope_qk.so")
 
@@ -32,7 +32,7 @@ FLAGS = [
 
 
 def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
-    cmd = [HIPCC, *FLAGS, *extra_flags, "-I", INCLUDE, "-o", out + ".tmp", SRC]
+    cmd = [HIPCC, *FLAGS, *extra_flags, "-I", INCLUDE, "-o", out + ".tmp", *SRCS]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

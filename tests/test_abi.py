@@ -220,3 +220,74 @@ def test_pairing_and_scaling_constants_match_binding():
     assert C["ROPE_QK_SCALING_NONE"] == P.ROPE_QK_SCALING_NONE
     assert C["ROPE_QK_SCALING_LLAMA3"] == P.ROPE_QK_SCALING_LLAMA3
     assert C["ROPE_QK_FREQ_FP64"] == P.ROPE_QK_FREQ_FP64 and C["ROPE_QK_FREQ_FP32"] == P.ROPE_QK_FREQ_FP32
+
+
+# ---------------------------------------------------------------------------
+# per-head RMSNorm + rotation: argument checks (nothing is launched)
+# ---------------------------------------------------------------------------
+
+W_Q, W_K, WS = 0x40000, 0x50000, 0x60000
+
+
+def norm_fwd(q=Q, k=K, qo=None, ko=None, wq=W_Q, wk=W_K, eps=1e-6, cu=CU, nseq=4, T=256, Hq=14, Hkv=2, D=64,
+             strides="default", theta=1e6, dtype=1, opts=None):
+    qo = q if qo is None else qo
+    ko = k if ko is None else ko
+    st = None if strides is None else (ctypes.c_int64 * 8)(*(
+        [Hq * D, D, Hkv * D, D, Hq * D, D, Hkv * D, D] if strides == "default" else strides))
+    return lib.rope_qk_norm_fwd(ctypes.c_void_p(q), ctypes.c_void_p(k), ctypes.c_void_p(qo), ctypes.c_void_p(ko),
+                                ctypes.c_void_p(wq), ctypes.c_void_p(wk), eps, ctypes.c_void_p(cu), nseq, T, Hq, Hkv,
+                                D, st, theta, dtype, ctypes.byref(opts) if opts is not None else None, None)
+
+
+def norm_bwd(ws=WS, ws_size=1 << 30, dwq=0x70000, dwk=0x80000, wq=W_Q, eps=1e-6, T=256, Hq=14, Hkv=2, D=64,
+             dtype=1, cu=CU, opts=None):
+    st = (ctypes.c_int64 * 12)(*([Hq * D, D, Hkv * D, D] * 3))
+    return lib.rope_qk_norm_bwd(ctypes.c_void_p(Q), ctypes.c_void_p(K), ctypes.c_void_p(Q + (1 << 24)),
+                                ctypes.c_void_p(K + (1 << 24)), ctypes.c_void_p(Q), ctypes.c_void_p(K),
+                                ctypes.c_void_p(wq), ctypes.c_void_p(W_K), eps, ctypes.c_void_p(dwq),
+                                ctypes.c_void_p(dwk), ctypes.c_void_p(ws), ws_size, ctypes.c_void_p(cu), 4, T, Hq,
+                                Hkv, D, st, 1e6, dtype, ctypes.byref(opts) if opts is not None else None, None)
+
+
+def test_norm_fwd_error_codes():
+    assert norm_fwd(dtype=7) == C["ROPE_QK_ERR_DTYPE"]
+    assert norm_fwd(D=96) == C["ROPE_QK_ERR_SHAPE"]  # 12 chunks per head: not a power of two
+    assert norm_fwd(D=8) == C["ROPE_QK_ERR_SHAPE"]  # one chunk per head
+    assert norm_fwd(D=24, dtype=0) == C["ROPE_QK_ERR_SHAPE"]  # 6 chunks
+    assert norm_fwd(Hq=65535, Hkv=1, strides=[65535 * 64, 64, 64, 64, 65535 * 64, 64, 64, 64]) == \
+        C["ROPE_QK_ERR_SHAPE"]  # more heads than the row division allows
+    for eps in (0.0, -1e-6, float("inf"), float("nan")):
+        assert norm_fwd(eps=eps) == C["ROPE_QK_ERR_OPTION"], eps
+    assert norm_fwd(opts=P.make_options(rotary_dim=32)) == C["ROPE_QK_ERR_OPTION"]  # the norm covers the whole head
+    assert norm_fwd(opts=P.make_options(rotary_dim=64), cu=0) == C["ROPE_QK_ERR_NULL"]  # r = D is fine
+    assert norm_fwd(strides=None) == C["ROPE_QK_ERR_NULL"]
+    assert norm_fwd(wq=0) == C["ROPE_QK_ERR_NULL"]
+    assert norm_fwd(wk=0, Hkv=0, strides=[14 * 64, 64, 0, 64, 14 * 64, 64, 0, 64], cu=0) == C["ROPE_QK_ERR_NULL"]
+    assert norm_fwd(wq=W_Q + 4) == C["ROPE_QK_ERR_ALIGN"]
+    assert norm_fwd(qo=Q + 8 + (1 << 24)) == C["ROPE_QK_ERR_ALIGN"]
+    assert norm_fwd(strides=[14 * 64, 32, 2 * 64, 64, 14 * 64, 64, 2 * 64, 64]) == C["ROPE_QK_ERR_LAYOUT"]
+    assert norm_fwd(cu=0) == C["ROPE_QK_ERR_NULL"]
+    assert norm_fwd(T=0) == C["ROPE_QK_OK"]
+    assert norm_fwd(nseq=0) == C["ROPE_QK_OK"]  # in place with nothing inside: no launch
+    assert norm_fwd(theta=0.0) == C["ROPE_QK_ERR_THETA"]
+
+
+def test_norm_bwd_error_codes_and_workspace_size():
+    need = lib.rope_qk_norm_bwd_workspace_bytes(256, 14, 2, 64, 1)
+    assert need > 0 and need % 16 == 0
+    assert lib.rope_qk_norm_bwd_workspace_bytes(256, 14, 2, 64, 9) == C["ROPE_QK_ERR_DTYPE"]
+    assert lib.rope_qk_norm_bwd_workspace_bytes(256, 14, 2, 96, 1) == C["ROPE_QK_ERR_SHAPE"]
+    assert lib.rope_qk_norm_bwd_workspace_bytes(0, 14, 2, 64, 1) == 0
+    # Qwen3-8B-shaped batch: 16 bytes per column per tile of 64 rows, an eighth of q and k
+    big = lib.rope_qk_norm_bwd_workspace_bytes(65536, 32, 8, 128, 1)
+    assert 0 < big <= 0.13 * 65536 * 40 * 128 * 2
+    assert norm_bwd(ws=0) == C["ROPE_QK_ERR_WORKSPACE"]
+    assert norm_bwd(ws_size=need - 16) == C["ROPE_QK_ERR_WORKSPACE"]
+    assert norm_bwd(ws=WS + 8) == C["ROPE_QK_ERR_ALIGN"]
+    assert norm_bwd(dwq=0) == C["ROPE_QK_ERR_NULL"]
+    assert norm_bwd(dwq=0x70004) == C["ROPE_QK_ERR_ALIGN"]
+    assert norm_bwd(eps=0.0) == C["ROPE_QK_ERR_OPTION"]
+    assert norm_bwd(wq=0) == C["ROPE_QK_ERR_NULL"]
+    assert norm_bwd(cu=0) == C["ROPE_QK_ERR_NULL"]
+    assert norm_bwd(dtype=5) == C["ROPE_QK_ERR_DTYPE"]

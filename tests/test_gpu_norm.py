@@ -1,0 +1,246 @@
+"""Per-head RMSNorm + rotation through the C ABI vs the fp64 oracle (needs an MI355X).
+
+Forward: every row shape (2 to 64 chunks of 16 bytes per head) in bf16, fp16
+and fp32, in place and out of place, with the rotation options.  Backward:
+dx element by element like the forward; the weight gradients against the
+oracle's float64 sums to within about one float32 ulp, and run-to-run
+identical.  The Qwen3-8B-shaped batch runs at full size: dx on sampled
+tokens, the weight gradients against the oracle summed over every token.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import packed_varlen_rotary_amd as P
+import workloads as W
+from tests.gpu_util import check_against, f64, sample_tokens
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+EPS = 1e-6
+LLAMA3 = dict(factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0, original_max_position=8192.0)
+
+
+def cu_dev(cu):
+    return torch.as_tensor(np.asarray(cu, dtype=np.int32), device=DEV)
+
+
+def weights(D, seed):
+    """A norm weight near 1, like trained q/k norm weights (float32)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return (1.0 + 0.25 * torch.randn(D, generator=g)).float().to(DEV)
+
+
+def oracle_opts(opts):
+    return dict(pos_offset=opts.get("pos_offset", 0), pairing="interleaved" if opts.get("interleaved") else "half",
+                scaling=opts.get("llama3"), freq_precision="fp32" if opts.get("freq_fp32") else "fp64")
+
+
+def w64(w):
+    return w.detach().cpu().double().numpy()
+
+
+def check_dw(got, ref, S, what):
+    """float32 weight gradient vs the oracle's float64 sum: half an fp32 ulp of
+    the value, plus 1e-11 of the sum of |terms| for float64 summation order."""
+    got = got.detach().cpu().double().numpy()
+    err = np.abs(got - ref)
+    bound = 2.0 ** -24 * np.abs(ref) + 1e-11 * S + 1e-30
+    assert np.all(err <= bound), f"{what}: worst {np.max(err / bound)} of the bound"
+
+
+def dw_terms(dy, x, w, cu, theta, o):
+    """sum over normalised heads of |dn_j x_j r|: the scale of the weight-gradient sums."""
+    T = x.shape[0]
+    inside = oracle.segment_positions(cu, T, o["pos_offset"]) >= 0
+    dn = oracle.rope(dy, cu, theta, -1, **o)
+    _, r = oracle.rms_norm(x, w, EPS)
+    return np.sum(np.abs(dn * x * r[..., None])[inside], axis=(0, 1))
+
+
+SHAPES = [
+    # T, Hq, Hkv, D, dtype (chunks per head = D * size / 16)
+    (300, 6, 2, 128, "bf16"),  # 16
+    (257, 5, 3, 64, "bf16"),  # 8
+    (129, 4, 2, 256, "bf16"),  # 32
+    (65, 3, 2, 512, "bf16"),  # 64: a row fills a wave
+    (400, 7, 1, 16, "bf16"),  # 2
+    (300, 4, 4, 32, "bf16"),  # 4
+    (300, 6, 2, 64, "fp32"),  # 16
+    (200, 3, 1, 128, "fp32"),  # 32
+    (500, 5, 3, 8, "fp32"),  # 2
+    (150, 2, 2, 256, "fp32"),  # 64
+    (300, 6, 2, 128, "fp16"),
+    (257, 5, 3, 64, "fp16"),
+]
+
+
+def run_fwd(q, k, wq, wk, cu, theta, out_of_place, **opts):
+    xq, xk = f64(q), f64(k)
+    q0, k0 = q.clone(), k.clone()
+    if out_of_place:
+        qo, ko = torch.full_like(q, 3.0), torch.full_like(k, 3.0)
+    else:
+        qo, ko = q, k
+    P.rope_qk_norm_fwd(q, k, wq, wk, EPS, cu_dev(cu), theta, qo, ko, **opts)
+    torch.cuda.synchronize()
+    o = oracle_opts(opts)
+    rq, _ = oracle.norm_rope(xq, w64(wq), EPS, cu, theta, **o)
+    rk, _ = oracle.norm_rope(xk, w64(wk), EPS, cu, theta, **o)
+    sq = check_against(qo, rq, f"q {opts}")
+    sk = check_against(ko, rk, f"k {opts}")
+    if out_of_place:
+        assert torch.equal(q, q0) and torch.equal(k, k0)  # inputs untouched
+    return sq, sk
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"T{s[0]}_H{s[1]}x{s[2]}_D{s[3]}_{s[4]}")
+@pytest.mark.parametrize("out_of_place", [False, True], ids=["inplace", "outofplace"])
+def test_norm_fwd_shapes(shape, out_of_place):
+    T, Hq, Hkv, D, dt = shape
+    q = W.randn((T, Hq, D), dt, seed=T + D, device=DEV)
+    k = W.randn((T, Hkv, D), dt, seed=T + D + 1, device=DEV)
+    cu = [0, 1, T // 3, T // 3, T - 5]  # a 1-token sequence, an empty one, 5 tokens outside
+    sq, sk = run_fwd(q, k, weights(D, D), weights(D, D + 1), cu, 1e4, out_of_place)
+    if dt != "fp32":
+        assert sq["exact_fraction"] == 1.0 and sk["exact_fraction"] == 1.0, (sq, sk)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+@pytest.mark.parametrize("opts", [dict(interleaved=True), dict(pos_offset=123456, llama3=LLAMA3),
+                                  dict(freq_fp32=True, pos_offset=500000),
+                                  dict(interleaved=True, pos_offset=77, llama3=LLAMA3, freq_fp32=True)],
+                         ids=["interleaved", "offset_llama3", "fp32_angles", "everything"])
+def test_norm_fwd_options(dt, opts):
+    T, Hq, Hkv, D = 300, 6, 2, 128
+    q = W.randn((T, Hq, D), dt, seed=11, device=DEV)
+    k = W.randn((T, Hkv, D), dt, seed=12, device=DEV)
+    run_fwd(q, k, weights(D, 5), weights(D, 6), [0, 100, 100, 290], 5e5, True, **opts)
+
+
+def run_bwd(T, Hq, Hkv, D, dt, cu, theta, seed, in_place, **opts):
+    q = W.randn((T, Hq, D), dt, seed=seed, device=DEV)
+    k = W.randn((T, Hkv, D), dt, seed=seed + 1, device=DEV)
+    dyq = W.randn((T, Hq, D), dt, seed=seed + 2, device=DEV)
+    dyk = W.randn((T, Hkv, D), dt, seed=seed + 3, device=DEV)
+    wq, wk = weights(D, seed + 4), weights(D, seed + 5)
+    xq, xk, gq, gk = f64(q), f64(k), f64(dyq), f64(dyk)
+    if in_place:
+        dq, dk = dyq, dyk
+    else:
+        dq, dk = torch.full_like(q, 5.0), torch.full_like(k, 5.0)
+    dq, dk, dwq, dwk = P.rope_qk_norm_bwd(dyq, dyk, q, k, wq, wk, EPS, cu_dev(cu), theta, dq, dk, **opts)
+    torch.cuda.synchronize()
+    o = oracle_opts(opts)
+    out = {}
+    for name, dx, dw, x, g, w in (("q", dq, dwq, xq, gq, wq), ("k", dk, dwk, xk, gk, wk)):
+        rdx, rdw = oracle.norm_rope_bwd(g, x, w64(w), EPS, cu, theta, **o)
+        out[name] = check_against(dx, rdx, f"d{name} {opts}")
+        check_dw(dw, rdw, dw_terms(g, x, w64(w), cu, theta, o), f"dw{name} {opts}")
+    return out
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"T{s[0]}_H{s[1]}x{s[2]}_D{s[3]}_{s[4]}")
+def test_norm_bwd_shapes(shape):
+    T, Hq, Hkv, D, dt = shape
+    cu = [0, 1, T // 3, T // 3, T - 5]
+    s = run_bwd(T, Hq, Hkv, D, dt, cu, 1e4, seed=7 * T + D, in_place=True)
+    if dt != "fp32":
+        assert s["q"]["exact_fraction"] == 1.0 and s["k"]["exact_fraction"] == 1.0, s
+
+
+@pytest.mark.parametrize("opts", [dict(), dict(interleaved=True), dict(pos_offset=4096, llama3=LLAMA3, freq_fp32=True)],
+                         ids=["plain", "interleaved", "offset_llama3_fp32"])
+def test_norm_bwd_out_of_place_and_options(opts):
+    run_bwd(700, 8, 2, 128, "bf16", [3, 100, 100, 620, 690], 5e5, seed=91, in_place=False, **opts)
+
+
+def test_norm_bwd_is_deterministic():
+    T, Hq, Hkv, D = 3000, 16, 4, 128
+    q = W.randn((T, Hq, D), "bf16", seed=1, device=DEV)
+    k = W.randn((T, Hkv, D), "bf16", seed=2, device=DEV)
+    dyq = W.randn((T, Hq, D), "bf16", seed=3, device=DEV)
+    dyk = W.randn((T, Hkv, D), "bf16", seed=4, device=DEV)
+    wq, wk = weights(D, 1), weights(D, 2)
+    cu = cu_dev([0, 1000, 2500, T])
+    res = [P.rope_qk_norm_bwd(dyq.clone(), dyk.clone(), q, k, wq, wk, EPS, cu, 1e6) for _ in range(3)]
+    torch.cuda.synchronize()
+    for r in res[1:]:
+        for a, b in zip(res[0], r):
+            assert torch.equal(a.view(torch.int16) if a.dtype != torch.float32 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype != torch.float32 else b.view(torch.int32))
+
+
+def test_norm_bwd_matches_finite_differences_of_the_forward():
+    """The GPU backward's dx against a central difference of the GPU forward's
+    sum(G * y) along a random direction V (fp32 storage; independent of the
+    oracle)."""
+    T, Hq, Hkv, D = 64, 4, 2, 64
+    q = W.randn((T, Hq, D), "fp32", seed=21, device=DEV)
+    k = W.randn((T, Hkv, D), "fp32", seed=22, device=DEV)
+    G = W.randn((T, Hq, D), "fp32", seed=23, device=DEV)
+    V = W.randn((T, Hq, D), "fp32", seed=24, device=DEV)
+    wq, wk = weights(D, 3), weights(D, 4)
+    cu = cu_dev([0, 30, T])
+
+    def loss(xq):
+        yq, _ = P.rope_qk_norm_fwd(xq, k, wq, wk, EPS, cu, 1e4, torch.empty_like(xq), torch.empty_like(k))
+        return float((G.double() * yq.double()).sum())
+
+    h = 1e-2
+    fd = (loss(q + h * V) - loss(q - h * V)) / (2 * h)
+    dq, _, _, _ = P.rope_qk_norm_bwd(G.clone(), torch.zeros_like(k), q, k, wq, wk, EPS, cu, 1e4)
+    an = float((dq.double() * V.double()).sum())
+    assert abs(fd - an) <= 1e-3 * (abs(an) + 1.0), (fd, an)
+
+
+def test_norm_qwen3_8b_shape_full_size():
+    """Qwen3-8B-shaped packed batch (T = 65536, 32 + 8 heads, D = 128, bf16):
+    forward out of place and backward in place at full size; outputs of
+    sampled tokens (every head and element) and the weight gradients summed
+    by the oracle over every token."""
+    w = W.make_workload(3)
+    T, Hq, Hkv, D = w.T, w.Hq, w.Hkv, w.D
+    t = W.make_tensors(w, ("q", "k", "dq", "dk"), device=DEV)
+    wq, wk = weights(D, 31), weights(D, 32)
+    cu = cu_dev(w.cu_seqlens)
+    idx = sample_tokens(w.cu_seqlens, T, 512, seed=3)
+    idx_d = torch.as_tensor(idx, device=DEV)
+    pos = oracle.segment_positions(w.cu_seqlens, T)[idx]
+    qo, ko = torch.empty_like(t["q"]), torch.empty_like(t["k"])
+    P.rope_qk_norm_fwd(t["q"], t["k"], wq, wk, EPS, cu, w.theta, qo, ko)
+    for x, y, wt, nm in ((t["q"], qo, wq, "q"), (t["k"], ko, wk, "k")):
+        n, _ = oracle.rms_norm(f64(x.index_select(0, idx_d)), w64(wt), EPS)
+        s = check_against(y.index_select(0, idx_d), oracle.rotate(n, pos, w.theta, 1), f"fwd {nm}")
+        assert s["exact_fraction"] == 1.0, s
+    del qo, ko
+    g_s = {nm: f64(t["d" + nm].index_select(0, idx_d)) for nm in ("q", "k")}
+    dq, dk, dwq, dwk = P.rope_qk_norm_bwd(t["dq"], t["dk"], t["q"], t["k"], wq, wk, EPS, cu, w.theta)
+    torch.cuda.synchronize()
+    for x, dx, wt, nm in ((t["q"], dq, wq, "q"), (t["k"], dk, wk, "k")):
+        dn = oracle.rotate(g_s[nm], pos, w.theta, -1)
+        rdx, _ = oracle.rms_norm_bwd(dn, f64(x.index_select(0, idx_d)), w64(wt), EPS)
+        s = check_against(dx.index_select(0, idx_d), rdx, f"bwd d{nm}")
+        assert s["exact_fraction"] == 1.0, s
+    # weight gradients: the oracle over every token, in chunks of 4096 tokens
+    make = W.make_tensors(w, ("dq", "dk"), device=DEV)  # the incoming gradients again (dq, dk were overwritten)
+    all_pos = oracle.segment_positions(w.cu_seqlens, T)
+    for x, gt, dw, wt, nm in ((t["q"], make["dq"], dwq, wq, "q"), (t["k"], make["dk"], dwk, wk, "k")):
+        ref = np.zeros(D)
+        S = np.zeros(D)
+        for a in range(0, T, 4096):
+            sl = slice(a, min(a + 4096, T))
+            inside = all_pos[sl] >= 0
+            xs, gs = f64(x[sl])[inside], f64(gt[sl])[inside]
+            dn = oracle.rotate(gs, all_pos[sl][inside], w.theta, -1)
+            _, dwc = oracle.rms_norm_bwd(dn, xs, w64(wt), EPS)
+            _, r = oracle.rms_norm(xs, w64(wt), EPS)
+            ref += dwc
+            S += np.sum(np.abs(dn * xs * r[..., None]), axis=(0, 1))
+        check_dw(dw, ref, S, f"dw{nm} full size")
+    del t, make
+    torch.cuda.empty_cache()
