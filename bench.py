@@ -41,7 +41,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused QK-RoPE fwd+bwd tokens/s and achieved HBM GB/s (% of MI355X peak)"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "packed_varlen_rotary_amd", "csrc", "rope_qk.hip")
+# the sources the rotation kernels are compiled from
+KERNEL_SRCS = [os.path.join(ROOT, "packed_varlen_rotary_amd", "csrc", n)
+               for n in ("rope_qk.hip", "rope_common.h", "rope_sincos.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rope_qk_kernel_traffic.md")
 
 
@@ -50,8 +52,12 @@ def log(*a):
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """SHA-256 over the rotation kernels' sources, in a fixed order."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload_name: str):
@@ -287,6 +293,80 @@ def run_copy_ceiling(args):
                       "traffic_bytes": w.bytes_per_pass, "us_per_copy": us, "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS}))
 
 
+def run_norm(args):
+    """The fused per-head RMSNorm + rotation (rope_qk_norm_fwd out of place,
+    rope_qk_norm_bwd into a separate dx) on a workload's shapes: each pass
+    timed on its own as a graph of K calls over resident sets of >= 1 GiB,
+    HIP events around the replay.  Algorithmic bytes: forward read x + write
+    y, backward read x and dy + write dx (the weight-gradient workspace is
+    extra traffic, reported separately)."""
+    import torch
+
+    import packed_varlen_rotary_amd as P
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    w = W.make_workload(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cu = torch.as_tensor(w.cu_seqlens, device=dev)
+    qk_bytes = w.bytes_per_pass // 2  # q and k once
+    nsets = max(1, min(16, -(-(1 << 30) // (4 * qk_bytes))))
+    sets = []
+    for s in range(nsets):
+        b = W.make_tensors(w, ("q", "k", "dq", "dk"), device=dev, salt=s)
+        b["yq"], b["yk"] = torch.empty_like(b["q"]), torch.empty_like(b["k"])
+        b["xq"], b["xk"] = torch.empty_like(b["q"]), torch.empty_like(b["k"])
+        sets.append(b)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(7)
+    wq = (1.0 + 0.25 * torch.randn(w.D, generator=g)).float().to(dev)
+    wk = (1.0 + 0.25 * torch.randn(w.D, generator=g)).float().to(dev)
+    eps = 1e-6
+    code = {"bf16": P.ROPE_QK_BF16, "fp16": P.ROPE_QK_FP16, "fp32": P.ROPE_QK_FP32}[w.dtype]
+    ws_bytes = P.rope_qk_norm_bwd_workspace_bytes(w.T, w.Hq, w.Hkv, w.D, code)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    dwq = torch.empty(w.D, dtype=torch.float32, device=dev)
+    dwk = torch.empty(w.D, dtype=torch.float32, device=dev)
+    log(f"[bench] norm {w.name}: {nsets} resident sets of {4 * qk_bytes / 2**20:.1f} MiB, "
+        f"workspace {ws_bytes / 2**20:.2f} MiB")
+
+    def fwd(i):
+        b = sets[i % nsets]
+        P.rope_qk_norm_fwd(b["q"], b["k"], wq, wk, eps, cu, w.theta, b["yq"], b["yk"])
+
+    def bwd(i):
+        b = sets[i % nsets]
+        P.rope_qk_norm_bwd(b["dq"], b["dk"], b["q"], b["k"], wq, wk, eps, cu, w.theta, b["xq"], b["xk"],
+                           dwq, dwk, ws)
+
+    res = {}
+    for name, fn, nbytes in (("fwd", fwd, 2 * qk_bytes), ("bwd", bwd, 3 * qk_bytes)):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                fn(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b_.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b_) * 1e3 / args.steps
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = {"us_per_call": us, "algorithmic_bytes": nbytes, "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS}
+        log(f"[bench] norm {name}: {us:.2f} us per call, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak)")
+        del graph
+    print(json.dumps({"metric": "fused per-head QK-RMSNorm + RoPE, achieved HBM GB/s per pass", "workload": w.name,
+                      "io_dtype": w.dtype, "resident_sets": nsets, "workspace_bytes": ws_bytes, "steps": args.steps,
+                      "peak": HBM_PEAK_GBS, **res}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -300,6 +380,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of --copy-bytes (for HBM counter scaling)")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--norm", action="store_true",
+                    help="only time the fused RMSNorm + rotation kernels (forward and backward) on --workload")
     ap.add_argument("--copy-ceiling", action="store_true",
                     help="only time the runtime's device copy with one launch's HBM traffic (roofline context)")
     args = ap.parse_args()
@@ -314,6 +396,9 @@ def main():
         return
     if args.copy_ceiling:
         run_copy_ceiling(args)
+        return
+    if args.norm:
+        run_norm(args)
         return
 
     w, r = run_gpu(args)

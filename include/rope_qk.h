@@ -224,7 +224,7 @@ int rope_qk_bwd_opt(void* dq, void* dk, const int32_t* cu_seqlens, int64_t nseq,
  *                  D (the norm covers the whole head)
  *   D              D * element size must be 32, 64, ..., 1024 bytes (a whole
  *                  head is a power-of-two number of 16-byte chunks, at most
- *                  64); Hq + Hkv <= 65535; else ROPE_QK_ERR_SHAPE
+ *                  64); Hq <= 65535 and Hkv <= 65535; else ROPE_QK_ERR_SHAPE
  *
  * Other arguments, alignment, errors and stream semantics as rope_qk_fwd.
  * T == 0 or no heads is a no-op; so is nseq == 0 when both outputs are their
@@ -238,8 +238,8 @@ int rope_qk_norm_fwd(const void* q, const void* k, void* q_out, void* k_out, con
 /*
  * Bytes of device workspace rope_qk_norm_bwd needs for these sizes (>= 0), or
  * a negative status (ROPE_QK_ERR_DTYPE, ROPE_QK_ERR_SHAPE): 16 * D bytes for
- * every tile of rows_per_tile = 1024 / (D * element size / 16) rows, plus
- * 16 * D for each of up to 256 slices.
+ * each of the backward's workgroups, of which there are at most 1024 (at
+ * most 8 MiB; 2 MiB at D = 128).
  */
 int64_t rope_qk_norm_bwd_workspace_bytes(int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int dtype);
 

@@ -25,57 +25,63 @@
 //    rotation exactly as in the rotation kernels: the rotate_half partner
 //    chunk comes from lane l ^ L/2 (negated in the first half), interleaved
 //    pairs sit inside a chunk; the cos/sin table is built once per tile.
+//  * A tile holds rows of q only or of k only, so it needs one weight vector
+//    and one set of weight-gradient sums.
 //  * Backward: the rotation by -angle (the table holds -sin), then the RMSNorm
-//    gradient with a second row sum (sum_j g_j x_j); the weight gradient is
-//    summed per lane over its rows, then across the lanes of a wave that hold
-//    the same chunk, then across the 4 waves in LDS, into one float64 partial
-//    per tile and column, which two small kernels sum in a fixed order: the
-//    result is deterministic.
+//    gradient with a second row sum (sum_j g_j x_j).  A fixed number of
+//    workgroups loop over the tiles; each sums the weight gradient of its
+//    rows per lane, then across the lanes of a wave that hold the same chunk,
+//    then across the 4 waves, into float64 sums in LDS that it writes once at
+//    the end; a small kernel adds the workgroups' sums in a fixed tree order,
+//    so the result is deterministic.
 //  * Everything is evaluated in float64 and rounded once to the storage type.
 
 #include "rope_common.h"
 
 namespace {
 
-constexpr int kNormTasks = 4;        // rows per lane per tile
+constexpr int kFwdTasks = 4;          // rows per lane per forward tile
+constexpr int kBwdTasks = 2;          // rows per lane per backward tile (register-bound: ~180 VGPRs)
 constexpr int64_t kMaxHeads = 65535;  // row -> (token, head) division limit
-constexpr uint32_t kReduceSlices = 256;
 constexpr int kWaves = kThreads / 64;
+constexpr int kFwdTableBytes = 32768;  // forward table per workgroup (one entry per element)
+constexpr int64_t kBwdGroups = 1024;  // backward workgroups (4 per compute unit), each looping over tiles
+
+// One of the two tensors (q, k) of a call.
+struct NormTensor {
+  const char* x;         // forward: input; backward: the forward's input
+  const char* g;         // backward: incoming gradient of the forward's output
+  char* o;               // forward: output; backward: gradient of the input
+  const float* w;        // [D] weights
+  int64_t x_st, x_sh;    // byte strides along tokens / heads
+  int64_t g_st, g_sh;
+  int64_t o_st, o_sh;
+  uint64_t magic_heads;  // ceil(2^40 / H): exact n / H for n < 2^24
+  double rcp_heads;      // 1 / H, rounded
+  int32_t H;             // heads
+  int32_t tile_rows;     // rows per tile
+  uint32_t ntiles;
+  int32_t copy;          // 1: tokens outside every sequence are copied to a separate output
+};
 
 struct NormParams {
-  const char* xq;          // forward: q; backward: the forward's input q
-  const char* xk;
-  const char* gq;          // backward: incoming gradient of the forward's output q
-  const char* gk;
-  char* oq;                // forward: output q; backward: gradient of the input q
-  char* ok;
-  const float* wq;         // [D] weights of q and of k
-  const float* wk;
-  double* partial;         // backward: [ntiles][2 D] weight-gradient partials
-  const int32_t* cu;
+  NormTensor ten[2];     // q, k; tiles [0, ten[0].ntiles) are q's, the rest k's
+  double* partial;       // backward: [gridDim.x][2 D] weight-gradient sums per workgroup
+  const int32_t* cu;     // cu_seqlens[nseq + 1]
   int64_t T;
-  int64_t xq_st, xq_sh, xk_st, xk_sh;  // byte strides
-  int64_t gq_st, gq_sh, gk_st, gk_sh;
-  int64_t oq_st, oq_sh, ok_st, ok_sh;
-  uint64_t magic_heads;    // ceil(2^40 / H): exact n / H for n < 2^24
-  uint64_t magic_half;     // ceil(2^32 / half)
-  double rcp_heads;        // 1 / H, rounded
+  uint64_t magic_half;   // ceil(2^32 / half)
   double eps;
-  double inv_d;            // 1 / D (exact: D is a power of two)
-  double sign;             // +1 forward, -1 backward
-  uint32_t ntiles;
-  int32_t tile_rows;
+  double inv_d;          // 1 / D (exact: D is a power of two)
+  double sign;           // +1 forward, -1 backward
+  uint32_t ntiles;       // both tensors' tiles
+  int32_t table_bytes;   // LDS bytes of the cos/sin table
   int32_t nseq;
-  int32_t Hq;
-  int32_t H;               // Hq + Hkv
   int32_t D;
-  int32_t half;            // D / 2
-  int32_t L;               // chunks per row
-  int32_t lshift;          // log2(L)
+  int32_t half;          // D / 2
+  int32_t L;             // chunks per row
+  int32_t lshift;        // log2(L)
   int32_t pos_offset;
   int32_t freq_fp32;
-  int32_t copy_q;          // 1: tokens outside every sequence are copied to the output of q
-  int32_t copy_k;
   double inv_freq[kMaxHalf];
 };
 
@@ -85,13 +91,6 @@ __device__ __forceinline__ double lane_f64(double v, int addr) {
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(addr, static_cast<int>(b)));
   const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(addr, static_cast<int>(b >> 32)));
   return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
-}
-
-// Sum over the L consecutive lanes of a row (xor butterfly; a + b and b + a
-// are the same float64, so every lane of the row ends with the same bits).
-__device__ __forceinline__ double row_sum(double v, int L, int lane) {
-  for (int m = 1; m < L; m <<= 1) v += lane_f64(v, (lane ^ m) << 2);
-  return v;
 }
 
 // 1 / sqrt(a) for finite a > 0: the hardware estimate refined by three
@@ -107,40 +106,15 @@ __device__ __forceinline__ double rsqrt_f64(double a) {
   return y;
 }
 
-// kVec storage elements of a 16-byte chunk as float64.
+// Elements 2d and 2d + 1 (16-bit storage) or element d (fp32) of a chunk as
+// float64; for fp32 the second value is unused.
 template <int kDtype>
-__device__ __forceinline__ void unpack_chunk(const u32x4& w, double* x) {
+__device__ __forceinline__ f64x2 element_pair(const u32x4& w, int d) {
   if constexpr (kDtype == ROPE_QK_FP32) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) x[j] = static_cast<double>(__uint_as_float(w[j]));
+    return f64x2{static_cast<double>(__uint_as_float(w[d])), 0.0};
   } else {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const f64x2 v = unpack16<kDtype>(w[d]);
-      x[2 * d] = v.x;
-      x[2 * d + 1] = v.y;
-    }
+    return unpack16<kDtype>(w[d]);
   }
-}
-
-// One rounding of kVec float64 values to the storage type (16-bit: fast path,
-// redone exactly when a value is hard; see pack16_fast).
-template <int kDtype>
-__device__ __forceinline__ u32x4 pack_chunk(const double* y) {
-  u32x4 out;
-  if constexpr (kDtype == ROPE_QK_FP32) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = __float_as_uint(static_cast<float>(y[j]));
-  } else {
-    bool tie = false;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) out[d] = pack16_fast<kDtype>(y[2 * d], y[2 * d + 1], tie);
-    if (tie) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) out[d] = pack16_exact<kDtype>(y[2 * d], y[2 * d + 1]);
-    }
-  }
-  return out;
 }
 
 // The 16-byte chunk lane (addr / 4) holds, with the sign of every element
@@ -150,36 +124,150 @@ __device__ __forceinline__ u32x4 partner_chunk(const u32x4& v, int addr, bool ne
   const uint32_t flip = neg ? (kDtype == ROPE_QK_FP32 ? 0x80000000u : 0x80008000u) : 0u;
   u32x4 out;
 #pragma unroll
-  for (int d = 0; d < 4; ++d) out[d] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(addr, static_cast<int>(v[d]))) ^ flip;
+  for (int d = 0; d < 4; ++d)
+    out[d] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(addr, static_cast<int>(v[d]))) ^ flip;
   return out;
 }
 
-// The rotation of one chunk of normalised values n (own) with the partner's p
-// (rotate_half; p already negated in the first half) or of the pairs inside
-// the chunk (interleaved); cs points at the chunk's first table entry, stride
-// `step` entries apart.
-template <bool kIl, int kVec>
-__device__ __forceinline__ void rotate_chunk(const double* n, const double* p, const double2* cs, int step, double* y) {
-  if constexpr (kIl) {
+// Sum of squares of a chunk's elements, in float64.
+template <int kDtype>
+__device__ __forceinline__ double chunk_squares(const u32x4& a) {
+  double ss = 0.0;
 #pragma unroll
-    for (int jj = 0; jj < kVec / 2; ++jj) {
-      const double2 c = cs[jj * step];
-      const double a = n[2 * jj], b = n[2 * jj + 1];
-      y[2 * jj] = fma(a, c.x, -(b * c.y));
-      y[2 * jj + 1] = fma(b, c.x, a * c.y);
+  for (int d = 0; d < 4; ++d) {
+    const f64x2 v = element_pair<kDtype>(a, d);
+    ss = fma(v.x, v.x, ss);
+    if constexpr (kDtype != ROPE_QK_FP32) ss = fma(v.y, v.y, ss);
+  }
+  return ss;
+}
+
+// Sums over the L consecutive lanes of a row for kN rows at once (xor
+// butterfly; a + b and b + a are the same float64, so every lane of a row
+// ends with the same bits), so that the lane exchanges of the rows overlap.
+template <int kN>
+__device__ __forceinline__ void row_sums(double* v, int L, int lane) {
+  for (int m = 1; m < L; m <<= 1) {
+    const int addr = (lane ^ m) << 2;
+    double o[kN];
+#pragma unroll
+    for (int u = 0; u < kN; ++u) o[u] = lane_f64(v[u], addr);
+#pragma unroll
+    for (int u = 0; u < kN; ++u) v[u] += o[u];
+  }
+}
+
+// The forward output of one chunk from the weight-folded table: element e
+// becomes r * (x_e * A_e + x_p * B_e), with p its pair partner (rotate_half:
+// the same element of the partner chunk pr; interleaved: its neighbour in
+// the chunk) and (A_e, B_e) = (w_e cos, -w_p sin) for the first element of a
+// pair, (w_e cos, w_p sin) for the second.  tab: the chunk's first entry,
+// consecutive elements L entries apart.  16-bit storage: kExact selects the
+// exact rounding; returns whether a value was hard for the fast one.
+template <int kDtype, bool kIl, bool kExact>
+__device__ __forceinline__ bool fwd_chunk(const u32x4& own, const u32x4& pr, double r, const double2* tab, int L,
+                                          u32x4& out) {
+  bool tie = false;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const f64x2 x = element_pair<kDtype>(own, d);
+    if constexpr (kDtype == ROPE_QK_FP32) {
+      const double xp = kIl ? element_pair<kDtype>(own, d ^ 1).x : element_pair<kDtype>(pr, d).x;
+      const double2 c = tab[d * L];
+      out[d] = __float_as_uint(static_cast<float>(r * fma(x.x, c.x, xp * c.y)));
+    } else {
+      double p0, p1;
+      if constexpr (kIl) {
+        p0 = x.y;
+        p1 = x.x;
+      } else {
+        const f64x2 px = element_pair<kDtype>(pr, d);
+        p0 = px.x;
+        p1 = px.y;
+      }
+      const double2 c0 = tab[(2 * d) * L];
+      const double2 c1 = tab[(2 * d + 1) * L];
+      const double y0 = r * fma(x.x, c0.x, p0 * c0.y);
+      const double y1 = r * fma(x.y, c1.x, p1 * c1.y);
+      out[d] = kExact ? pack16_exact<kDtype>(y0, y1) : pack16_fast<kDtype>(y0, y1, tie);
     }
-  } else {
+  }
+  return tie;
+}
+
+// Backward of one chunk, first part: dn = rotation of the incoming gradient
+// by -angle (the table holds -sin; pr is the rotate_half partner chunk,
+// already negated in the first half), g = dn * w; adds sum_j g_j x_j to gx
+// and dn_j x_j r to acc (when `use`).
+template <int kDtype, bool kIl>
+__device__ __forceinline__ void bwd_chunk_grad(const u32x4& x, const u32x4& dy, const u32x4& pr, double r,
+                                               const float* w_own, const double2* cs, int step, bool use,
+                                               double* gw, double& gx, double* acc) {
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) {
-      const double2 c = cs[j * step];
-      y[j] = fma(n[j], c.x, p[j] * c.y);
+  for (int d = 0; d < 4; ++d) {
+    const f64x2 xv = element_pair<kDtype>(x, d);
+    const f64x2 dv = element_pair<kDtype>(dy, d);
+    if constexpr (kDtype == ROPE_QK_FP32) {
+      double dn;
+      if constexpr (kIl) {
+        const f64x2 dz = element_pair<kDtype>(dy, d ^ 1);
+        const double2 c = cs[(d >> 1) * step];
+        dn = (d & 1) ? fma(dv.x, c.x, dz.x * c.y) : fma(dv.x, c.x, -(dz.x * c.y));
+      } else {
+        const f64x2 pv = element_pair<kDtype>(pr, d);
+        const double2 c = cs[d * step];
+        dn = fma(dv.x, c.x, pv.x * c.y);
+      }
+      gw[d] = dn * static_cast<double>(w_own[d]);
+      gx = fma(gw[d], xv.x, gx);
+      acc[d] += use ? dn * xv.x * r : 0.0;
+    } else {
+      double dn0, dn1;
+      if constexpr (kIl) {
+        const double2 c = cs[d * step];
+        dn0 = fma(dv.x, c.x, -(dv.y * c.y));
+        dn1 = fma(dv.y, c.x, dv.x * c.y);
+      } else {
+        const f64x2 pv = element_pair<kDtype>(pr, d);
+        const double2 c0 = cs[(2 * d) * step];
+        const double2 c1 = cs[(2 * d + 1) * step];
+        dn0 = fma(dv.x, c0.x, pv.x * c0.y);
+        dn1 = fma(dv.y, c1.x, pv.y * c1.y);
+      }
+      gw[2 * d] = dn0 * static_cast<double>(w_own[2 * d]);
+      gw[2 * d + 1] = dn1 * static_cast<double>(w_own[2 * d + 1]);
+      gx = fma(gw[2 * d], xv.x, gx);
+      gx = fma(gw[2 * d + 1], xv.y, gx);
+      acc[2 * d] += use ? dn0 * xv.x * r : 0.0;
+      acc[2 * d + 1] += use ? dn1 * xv.y * r : 0.0;
     }
   }
 }
 
+// Backward of one chunk, second part: dx_j = r (g_j - x_j coef), rounded.
+template <int kDtype, bool kExact>
+__device__ __forceinline__ bool bwd_chunk_dx(const u32x4& x, const double* gw, double r, double coef, u32x4& out) {
+  bool tie = false;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const f64x2 xv = element_pair<kDtype>(x, d);
+    if constexpr (kDtype == ROPE_QK_FP32) {
+      out[d] = __float_as_uint(static_cast<float>(r * (gw[d] - xv.x * coef)));
+    } else {
+      const double y0 = r * (gw[2 * d] - xv.x * coef);
+      const double y1 = r * (gw[2 * d + 1] - xv.y * coef);
+      out[d] = kExact ? pack16_exact<kDtype>(y0, y1) : pack16_fast<kDtype>(y0, y1, tie);
+    }
+  }
+  return tie;
+}
+
+// One tile: tile_rows consecutive rows of one tensor.  s_w holds both
+// tensors' weights (q then k); acc (backward) receives this lane's
+// weight-gradient terms.
 template <int kDtype, bool kIl, bool kBwd, int kTPT>
 __device__ __forceinline__ void norm_tile(const NormParams& p, uint32_t tile, int32_t* s_pos, double2* s_cs,
-                                          float* s_w, double* s_dw) {
+                                          const float* s_w, double* acc) {
   constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;  // elements per chunk
   constexpr int kPPC = kIl ? kVec / 2 : kVec;          // table pairs per chunk
   const int tid = threadIdx.x;
@@ -189,22 +277,25 @@ __device__ __forceinline__ void norm_tile(const NormParams& p, uint32_t tile, in
   const int hl = L >> 1;        // chunks per half row
   const cu_ptr cu = (cu_ptr)p.cu;
   const int32_t nseq = p.nseq;
-  const int32_t H = p.H;
+  const int sel = tile >= p.ten[0].ntiles ? 1 : 0;  // 0: q, 1: k (wave-uniform)
+  const NormTensor& tn = p.ten[sel];
+  const uint32_t lt = tile - (sel ? p.ten[0].ntiles : 0u);
+  const int32_t H = tn.H;
 
   // first row n0 = t0 * H + r0 (n0 < 2^47 is exact in float64; the rounded quotient is off by at most one)
-  const int64_t n0 = static_cast<int64_t>(tile) * p.tile_rows;
-  int32_t t0i = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(static_cast<double>(n0) * p.rcp_heads));
+  const int64_t n0 = static_cast<int64_t>(lt) * tn.tile_rows;
+  int32_t t0i = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(static_cast<double>(n0) * tn.rcp_heads));
   int64_t r0l = n0 - static_cast<int64_t>(t0i) * H;
   if (r0l < 0) { t0i -= 1; r0l += H; }
   if (r0l >= H) { t0i += 1; r0l -= H; }
   const int64_t t0 = t0i;
   const uint32_t r0 = static_cast<uint32_t>(r0l);
-  const int64_t n_end = min(n0 + p.tile_rows, p.T * H);
-  const int ntok = static_cast<int>(div_tok(static_cast<uint32_t>(n_end - n0) + r0 - 1, p.magic_heads)) + 1;
+  const int64_t n_end = min(n0 + tn.tile_rows, p.T * H);
+  const int ntok = static_cast<int>(div_tok(static_cast<uint32_t>(n_end - n0) + r0 - 1, tn.magic_heads)) + 1;
   const int64_t t_end = t0 + ntok;
   const int nent = ntok * p.half;
 
-  // 1. inv_freq of this thread's table entries and the weights, before the data
+  // 1. inv_freq of this thread's table entries, before the data
   double f[kEnt];
   int tt_e[kEnt], i_e[kEnt];
 #pragma unroll
@@ -215,12 +306,15 @@ __device__ __forceinline__ void norm_tile(const NormParams& p, uint32_t tile, in
     i_e[v] = e < nent ? e - tt * p.half : 0;
     f[v] = (v == 0 || v * kThreads < nent) ? p.inv_freq[i_e[v]] : 0.0;
   }
-  const int nw4 = p.D >> 1;  // float4s of the two weight vectors
-  float4 wv = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (tid < nw4) {
-    const bool of_k = tid * 4 >= p.D;
-    const float* base = of_k ? p.wk : p.wq;  // NULL for a tensor without heads
-    if (base != nullptr) wv = *reinterpret_cast<const float4*>(base + (of_k ? tid * 4 - p.D : tid * 4));
+  // forward: the weights of each table pair's two elements, folded into the table
+  float w1[kEnt], w2[kEnt];
+#pragma unroll
+  for (int v = 0; v < kEnt; ++v) {
+    w1[v] = w2[v] = 0.f;
+    if (!kBwd && (v == 0 || v * kThreads < nent)) {
+      w1[v] = tn.w[kIl ? 2 * i_e[v] : i_e[v]];
+      w2[v] = tn.w[kIl ? 2 * i_e[v] + 1 : i_e[v] + p.half];
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -228,35 +322,28 @@ __device__ __forceinline__ void norm_tile(const NormParams& p, uint32_t tile, in
   u32x4 a[kTPT], g[kTPT];
   gchar* optr[kTPT];
   int tt_of[kTPT];
-  bool act[kTPT], isq[kTPT];
+  bool act[kTPT];
   const int rows_per_step = kThreads >> p.lshift;
+  const int64_t off = static_cast<int64_t>(c) * 16;
 #pragma unroll
   for (int u = 0; u < kTPT; ++u) {
     const int lr = u * rows_per_step + (tid >> p.lshift);
     act[u] = n0 + lr < n_end;
     const uint32_t l = act[u] ? r0 + static_cast<uint32_t>(lr) : r0;
-    const uint32_t tt = div_tok(l, p.magic_heads);
-    const uint32_t h = l - tt * static_cast<uint32_t>(H);
+    const uint32_t tt = div_tok(l, tn.magic_heads);
+    const int64_t h = static_cast<int64_t>(l - tt * static_cast<uint32_t>(H));
     const int64_t t = t0 + tt;
-    const bool is_q = static_cast<int32_t>(h) < p.Hq;
-    const int64_t hh = is_q ? static_cast<int64_t>(h) : static_cast<int64_t>(h) - p.Hq;
-    const int64_t off = static_cast<int64_t>(c) * 16;
-    const gchar* xrow = is_q ? (const gchar*)p.xq + t * p.xq_st + hh * p.xq_sh
-                             : (const gchar*)p.xk + t * p.xk_st + hh * p.xk_sh;
-    a[u] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4*>(xrow + off));
-    if constexpr (kBwd) {
-      const gchar* grow = is_q ? (const gchar*)p.gq + t * p.gq_st + hh * p.gq_sh
-                               : (const gchar*)p.gk + t * p.gk_st + hh * p.gk_sh;
-      g[u] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4*>(grow + off));
-    }
-    optr[u] = (is_q ? (gchar*)p.oq + t * p.oq_st + hh * p.oq_sh : (gchar*)p.ok + t * p.ok_st + hh * p.ok_sh) + off;
+    a[u] = __builtin_nontemporal_load(
+        reinterpret_cast<const gu32x4*>((const gchar*)tn.x + t * tn.x_st + h * tn.x_sh + off));
+    if constexpr (kBwd)
+      g[u] = __builtin_nontemporal_load(
+          reinterpret_cast<const gu32x4*>((const gchar*)tn.g + t * tn.g_st + h * tn.g_sh + off));
+    optr[u] = (gchar*)tn.o + t * tn.o_st + h * tn.o_sh + off;
     tt_of[u] = static_cast<int>(tt);
-    isq[u] = is_q;
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // 3. positions and the cos/sin table; the weights into LDS
-  if (tid < nw4) reinterpret_cast<float4*>(s_w)[tid] = wv;
+  // 3. positions and the table
   const int32_t s0 = last_start_at_or_before(cu, nseq, t0);
   const int64_t cu_last = cu[nseq];
   const int64_t cu_first_end = nseq >= 1 ? static_cast<int64_t>(cu[1]) : INT64_MIN;  // cu[1] exists only then
@@ -284,77 +371,71 @@ __device__ __forceinline__ void norm_tile(const NormParams& p, uint32_t tile, in
         const double ang = p.freq_fp32 ? static_cast<double>(static_cast<float>(pos) * static_cast<float>(f[v]))
                                        : static_cast<double>(pos) * f[v];
         rope_sincos(ang, &sn, &cs);
-        s_cs[cs_slot(tt_e[v], i_e[v], kPPC, kIl ? L : hl)] = make_double2(cs, p.sign * sn);
+        if constexpr (kBwd) {
+          s_cs[cs_slot(tt_e[v], i_e[v], kPPC, kIl ? L : hl)] = make_double2(cs, p.sign * sn);
+        } else {
+          // one entry per element: element e of token tt at (tt * kVec + e % kVec) * L + e / kVec
+          const int e1 = kIl ? 2 * i_e[v] : i_e[v];
+          const int e2 = kIl ? 2 * i_e[v] + 1 : i_e[v] + p.half;
+          const double a = static_cast<double>(w1[v]), b = static_cast<double>(w2[v]);
+          s_cs[(tt_e[v] * kVec + e1 % kVec) * L + e1 / kVec] = make_double2(a * cs, -(b * sn));
+          s_cs[(tt_e[v] * kVec + e2 % kVec) * L + e2 / kVec] = make_double2(b * cs, a * sn);
+        }
       }
     }
   }
   __syncthreads();
 
-  // 4. normalise and rotate every row (forward), or undo the rotation and take
-  //    the norm's gradient (backward); then store
+  // 4. every row of the tile: r for all rows (their lane sums together),
+  //    then the forward rows one at a time, or the backward in phases
   const int paddr = (lane ^ hl) << 2;  // rotate_half partner lane
   const bool first = c < hl;
-  const int cw = c * kVec;                      // this lane's first element
-  const int pw = (kIl ? c : (c ^ hl)) * kVec;  // the partner chunk's first element
-  double acc_q[kVec], acc_k[kVec];
-#pragma unroll
-  for (int j = 0; j < kVec; ++j) acc_q[j] = acc_k[j] = 0.0;
-  bool st[kTPT];
+  bool st[kTPT], inside[kTPT];
   u32x4 out[kTPT];
+  double r[kTPT];
 #pragma unroll
   for (int u = 0; u < kTPT; ++u) {
-    const int tt = tt_of[u];
-    const bool inside = s_pos[tt] >= 0;
-    st[u] = act[u] && (inside || (isq[u] ? p.copy_q : p.copy_k));
-    const float* w = s_w + (isq[u] ? 0 : p.D);
-    const double2* cs = kIl ? s_cs + tt * kPPC * L + c : s_cs + tt * kPPC * hl + (c & (hl - 1));
+    inside[u] = s_pos[tt_of[u]] >= 0;
+    st[u] = act[u] && (inside[u] || tn.copy);
+    r[u] = chunk_squares<kDtype>(a[u]);
+  }
+  row_sums<kTPT>(r, L, lane);
+#pragma unroll
+  for (int u = 0; u < kTPT; ++u) r[u] = rsqrt_f64(fma(r[u], p.inv_d, p.eps));
+  if constexpr (!kBwd) {
+#pragma unroll
+    for (int u = 0; u < kTPT; ++u) {
+      // one row at a time: interleaving rows would keep several rows' float64
+      // values live and cut the occupancy
+      __builtin_amdgcn_sched_barrier(0);
+      const double2* tab = s_cs + tt_of[u] * kVec * L + c;
+      u32x4 pr = a[u];
+      if constexpr (!kIl) pr = partner_chunk<kDtype>(a[u], paddr, false);  // signs are in the table
+      u32x4 y;
+      if (fwd_chunk<kDtype, kIl, false>(a[u], pr, r[u], tab, L, y)) fwd_chunk<kDtype, kIl, true>(a[u], pr, r[u], tab, L, y);
+      out[u] = inside[u] ? y : a[u];
+    }
+  } else {
+    const float* w_own = s_w + sel * p.D + c * kVec;
     const int step = kIl ? L : hl;
-    double x[kVec];
-    unpack_chunk<kDtype>(a[u], x);
-    double ss = 0.0;
+    double gw[kTPT][kVec];
+    double gx[kTPT];
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) ss = fma(x[j], x[j], ss);
-    ss = row_sum(ss, L, lane);
-    const double r = rsqrt_f64(fma(ss, p.inv_d, p.eps));
-    double y[kVec];
-    if constexpr (!kBwd) {
-      double n[kVec], pn[kVec];
+    for (int u = 0; u < kTPT; ++u) {
+      const int tt = tt_of[u];
+      const double2* cs = kIl ? s_cs + tt * kPPC * L + c : s_cs + tt * kPPC * hl + (c & (hl - 1));
+      u32x4 pr = g[u];
+      if constexpr (!kIl) pr = partner_chunk<kDtype>(g[u], paddr, first);
+      gx[u] = 0.0;
+      bwd_chunk_grad<kDtype, kIl>(a[u], g[u], pr, r[u], w_own, cs, step, act[u] && inside[u], gw[u], gx[u], acc);
+    }
+    row_sums<kTPT>(gx, L, lane);
 #pragma unroll
-      for (int j = 0; j < kVec; ++j) n[j] = (x[j] * r) * static_cast<double>(w[cw + j]);
-      if constexpr (!kIl) {
-        const u32x4 pr = partner_chunk<kDtype>(a[u], paddr, first);
-        double px[kVec];
-        unpack_chunk<kDtype>(pr, px);
-#pragma unroll
-        for (int j = 0; j < kVec; ++j) pn[j] = (px[j] * r) * static_cast<double>(w[pw + j]);
-      }
-      rotate_chunk<kIl, kVec>(n, pn, cs, step, y);
-      out[u] = inside ? pack_chunk<kDtype>(y) : a[u];
-    } else {
-      double dy[kVec], pdy[kVec], dn[kVec];
-      unpack_chunk<kDtype>(g[u], dy);
-      if constexpr (!kIl) {
-        const u32x4 pr = partner_chunk<kDtype>(g[u], paddr, first);
-        unpack_chunk<kDtype>(pr, pdy);
-      }
-      rotate_chunk<kIl, kVec>(dy, pdy, cs, step, dn);  // rotation by -angle: the table holds -sin
-      double gx = 0.0;
-      double gw[kVec];
-#pragma unroll
-      for (int j = 0; j < kVec; ++j) {
-        gw[j] = dn[j] * static_cast<double>(w[cw + j]);
-        gx = fma(gw[j], x[j], gx);
-      }
-      gx = row_sum(gx, L, lane);
-      const double coef = (r * r) * (gx * p.inv_d);
-      const bool use = act[u] && inside;
-#pragma unroll
-      for (int j = 0; j < kVec; ++j) {
-        y[j] = r * (gw[j] - x[j] * coef);
-        const double dw = use ? dn[j] * x[j] * r : 0.0;
-        if (isq[u]) acc_q[j] += dw; else acc_k[j] += dw;
-      }
-      out[u] = inside ? pack_chunk<kDtype>(y) : g[u];
+    for (int u = 0; u < kTPT; ++u) {
+      const double coef = (r[u] * r[u]) * (gx[u] * p.inv_d);
+      u32x4 y;
+      if (bwd_chunk_dx<kDtype, false>(a[u], gw[u], r[u], coef, y)) bwd_chunk_dx<kDtype, true>(a[u], gw[u], r[u], coef, y);
+      out[u] = inside[u] ? y : g[u];
     }
   }
 #pragma unroll
@@ -362,77 +443,102 @@ __device__ __forceinline__ void norm_tile(const NormParams& p, uint32_t tile, in
     if (!st[u]) continue;
     __builtin_nontemporal_store(out[u], reinterpret_cast<gu32x4*>(optr[u]));
   }
+}
 
-  if constexpr (kBwd) {
-    // weight-gradient partial of the tile: lanes holding the same chunk, then the waves
-    for (int m = L; m < 64; m <<= 1) {
-      const int addr = (lane ^ m) << 2;
-#pragma unroll
-      for (int j = 0; j < kVec; ++j) {
-        acc_q[j] += lane_f64(acc_q[j], addr);
-        acc_k[j] += lane_f64(acc_k[j], addr);
-      }
-    }
-    const int wave = tid >> 6;
-    const int width = 2 * p.D;
-    if (lane < L) {
-#pragma unroll
-      for (int j = 0; j < kVec; ++j) {
-        s_dw[wave * width + cw + j] = acc_q[j];
-        s_dw[wave * width + p.D + cw + j] = acc_k[j];
-      }
-    }
-    __syncthreads();
-    double* dst = p.partial + static_cast<int64_t>(tile) * width;
-    for (int col = tid; col < width; col += kThreads) {
-      double s = s_dw[col];
-#pragma unroll
-      for (int wv2 = 1; wv2 < kWaves; ++wv2) s += s_dw[wv2 * width + col];
-      dst[col] = s;
-    }
+// LDS of the norm kernels after the table: weights [2 D] floats, then (backward)
+// the workgroup's weight-gradient sums [2 D] and one tile's per-wave sums [4][D], doubles.
+__device__ __forceinline__ float* lds_weights(double2* s_cs, const NormParams& p) {
+  return reinterpret_cast<float*>(reinterpret_cast<char*>(s_cs) + p.table_bytes);
+}
+
+// Both tensors' weights into LDS (a tensor without heads may have none).
+__device__ __forceinline__ void load_weights(const NormParams& p, float* s_w) {
+  for (int i = threadIdx.x; i < p.D / 2; i += kThreads) {  // float4s of the 2 D weights
+    const bool of_k = i * 4 >= p.D;
+    const float* base = p.ten[of_k ? 1 : 0].w;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (base != nullptr) v = *reinterpret_cast<const float4*>(base + (of_k ? i * 4 - p.D : i * 4));
+    reinterpret_cast<float4*>(s_w)[i] = v;
   }
 }
 
-template <int kDtype, bool kIl, bool kBwd, int kTPT>
-__global__ __launch_bounds__(kThreads) void rope_qk_norm_kernel(const NormParams p) {
+// Forward: one tile per workgroup.
+template <int kDtype, bool kIl, int kTPT>
+__global__ __launch_bounds__(kThreads) void rope_qk_norm_fwd_kernel(const NormParams p) {
   __shared__ int32_t s_pos[kMaxTileTokens];
-  extern __shared__ double2 s_dyn[];  // [table][weights 2D floats][backward: wave partials 4 x 2D doubles]
+  extern __shared__ double2 s_cs[];
   const uint32_t tile = blockIdx.y * gridDim.x + blockIdx.x;
   if (tile >= p.ntiles) return;
-  const int table_entries = kMaxTableBytes / 16;
-  double2* s_cs = s_dyn;
-  float* s_w = reinterpret_cast<float*>(s_dyn + table_entries);
-  double* s_dw = reinterpret_cast<double*>(s_dyn + table_entries) + p.D;  // after 2D floats = D doubles
-  norm_tile<kDtype, kIl, kBwd, kTPT>(p, tile, s_pos, s_cs, s_w, s_dw);
+  norm_tile<kDtype, kIl, false, kTPT>(p, tile, s_pos, s_cs, nullptr, nullptr);
 }
 
-// Stage 1 of the weight-gradient sum: column col of the tiles of slice
-// blockIdx.y, in tile order.
-__global__ __launch_bounds__(kThreads) void dw_slices_kernel(const double* __restrict__ partial, uint32_t ntiles,
-                                                            int32_t width, uint32_t slice,
-                                                            double* __restrict__ sums) {
-  const int col = blockIdx.x * kThreads + threadIdx.x;
-  if (col >= width) return;
-  const uint32_t a = blockIdx.y * slice;
-  const uint32_t b = min(a + slice, ntiles);
-  double acc = 0.0;
-  for (uint32_t t = a; t < b; ++t) acc += partial[static_cast<int64_t>(t) * width + col];
-  sums[static_cast<int64_t>(blockIdx.y) * width + col] = acc;
+// Backward: gridDim.x workgroups, each taking tiles blockIdx.x, + gridDim.x, ...
+template <int kDtype, bool kIl, int kTPT>
+__global__ __launch_bounds__(kThreads) void rope_qk_norm_bwd_kernel(const NormParams p) {
+  constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;
+  __shared__ int32_t s_pos[kMaxTileTokens];
+  extern __shared__ double2 s_cs[];
+  float* s_w = lds_weights(s_cs, p);
+  double* s_acc = reinterpret_cast<double*>(s_w + 2 * p.D);  // [2 D]
+  double* s_wave = s_acc + 2 * p.D;                          // [kWaves][D]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int L = p.L, D = p.D;
+  const int c = tid & (L - 1);
+  load_weights(p, s_w);
+  for (int i = tid; i < 2 * D; i += kThreads) s_acc[i] = 0.0;
+  __syncthreads();
+  for (uint32_t tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
+    double acc[kVec];
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) acc[j] = 0.0;
+    norm_tile<kDtype, kIl, true, kTPT>(p, tile, s_pos, s_cs, s_w, acc);
+    // lanes holding the same chunk, then the waves, into the workgroup's sums
+    for (int m = L; m < 64; m <<= 1) {
+      const int addr = (lane ^ m) << 2;
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) acc[j] += lane_f64(acc[j], addr);
+    }
+    if (lane < L) {
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) s_wave[wave * D + c * kVec + j] = acc[j];
+    }
+    __syncthreads();
+    const int sel = tile >= p.ten[0].ntiles ? 1 : 0;
+    for (int col = tid; col < D; col += kThreads) {
+      double s = s_wave[col];
+#pragma unroll
+      for (int wv = 1; wv < kWaves; ++wv) s += s_wave[wv * D + col];
+      s_acc[sel * D + col] += s;
+    }
+    __syncthreads();  // the table, positions and wave sums are rewritten by the next tile
+  }
+  double* dst = p.partial + static_cast<int64_t>(blockIdx.x) * 2 * D;
+  for (int i = tid; i < 2 * D; i += kThreads) dst[i] = s_acc[i];
 }
 
-// Stage 2: the slices in order, rounded once to float32.
-__global__ __launch_bounds__(kThreads) void dw_final_kernel(const double* __restrict__ sums, uint32_t nslices,
-                                                           int32_t D, float* __restrict__ dwq,
-                                                           float* __restrict__ dwk) {
-  const int col = blockIdx.x * kThreads + threadIdx.x;
-  if (col >= 2 * D) return;
+// The weight gradients: column blockIdx.x of the workgroups' sums, added in a
+// fixed tree order, rounded once to float32.
+__global__ __launch_bounds__(kThreads) void dw_reduce_kernel(const double* __restrict__ partial, uint32_t ngroups,
+                                                            int32_t D, float* __restrict__ dwq,
+                                                            float* __restrict__ dwk) {
+  __shared__ double s[kThreads];
+  const int col = blockIdx.x;
+  const int tid = threadIdx.x;
   double acc = 0.0;
-  for (uint32_t s = 0; s < nslices; ++s) acc += sums[static_cast<int64_t>(s) * 2 * D + col];
-  const float v = static_cast<float>(acc);
-  if (col < D) {
-    if (dwq != nullptr) dwq[col] = v;
-  } else if (dwk != nullptr) {
-    dwk[col - D] = v;
+  for (uint32_t i = tid; i < ngroups; i += kThreads) acc += partial[static_cast<int64_t>(i) * 2 * D + col];
+  s[tid] = acc;
+  __syncthreads();
+  for (int width = kThreads / 2; width > 0; width >>= 1) {
+    if (tid < width) s[tid] += s[tid + width];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const float v = static_cast<float>(s[0]);
+    if (col < D) {
+      if (dwq != nullptr) dwq[col] = v;
+    } else if (dwk != nullptr) {
+      dwk[col - D] = v;
+    }
   }
 }
 
@@ -445,42 +551,58 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) % 16)
 
 // Geometry shared by the forward, the backward and the workspace query.
 struct NormGeometry {
-  int64_t L = 0, tile_rows = 0, ntiles = 0, nslices = 0, span = 0;
+  int64_t L = 0;
+  int64_t tile_rows[2] = {0, 0};
+  int64_t ntiles[2] = {0, 0};
+  int64_t span = 0;    // most tokens one tile touches
+  int64_t table_bytes = 0;
+  int64_t groups = 0;  // backward workgroups
 };
 
-int norm_geometry(int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int dtype, NormGeometry* g) {
+int norm_geometry(int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int dtype, bool s_bwd, NormGeometry* g) {
   const int64_t esz = dtype == ROPE_QK_FP32 ? 4 : 2;
   const int64_t L = D * esz / 16;
   if ((D * esz) % 16 || L < 2 || L > 64 || (L & (L - 1))) return ROPE_QK_ERR_SHAPE;
-  const int64_t H = Hq + Hkv;
-  if (H > kMaxHeads) return ROPE_QK_ERR_SHAPE;
-  const int64_t half = D / 2;
-  int64_t cap_tokens = kMaxTableBytes / (half * 16);
+  if (Hq > kMaxHeads || Hkv > kMaxHeads) return ROPE_QK_ERR_SHAPE;
+  // table bytes per token: the backward keeps (cos, -sin) per pair, the
+  // forward (w cos, +-w' sin) per element
+  const int64_t per_token = s_bwd ? D / 2 * 16 : D * 16;
+  int64_t cap_tokens = (s_bwd ? kMaxTableBytes : kFwdTableBytes) / per_token;
   if (cap_tokens > kMaxTileTokens) cap_tokens = kMaxTileTokens;
-  int64_t tile_rows = int64_t(kNormTasks) * (kThreads / L);
-  if (H > 0 && tile_rows > (cap_tokens - 1) * H) tile_rows = (cap_tokens - 1) * H;
   g->L = L;
-  g->tile_rows = tile_rows;
-  g->ntiles = H > 0 ? (T * H + tile_rows - 1) / tile_rows : 0;
-  if (g->ntiles > INT32_MAX) return ROPE_QK_ERR_SHAPE;
-  g->nslices = g->ntiles < kReduceSlices ? g->ntiles : kReduceSlices;
-  g->span = H > 0 ? (tile_rows % H == 0 ? tile_rows / H : (H + tile_rows - 2) / H + 1) : 0;
+  g->span = 0;
+  const int64_t Hs[2] = {Hq, Hkv};
+  for (int s = 0; s < 2; ++s) {
+    const int64_t H = Hs[s];
+    int64_t rows = int64_t(s_bwd ? kBwdTasks : kFwdTasks) * (kThreads / L);
+    if (H > 0 && rows > (cap_tokens - 1) * H) rows = (cap_tokens - 1) * H;
+    g->tile_rows[s] = rows;
+    g->ntiles[s] = H > 0 ? (T * H + rows - 1) / rows : 0;
+    if (H > 0) {
+      const int64_t span = rows % H == 0 ? rows / H : (H + rows - 2) / H + 1;  // tokens one tile touches
+      if (span > g->span) g->span = span;
+    }
+  }
+  g->table_bytes = g->span * per_token;
+  const int64_t total = g->ntiles[0] + g->ntiles[1];
+  if (total > INT32_MAX) return ROPE_QK_ERR_SHAPE;
+  g->groups = total < kBwdGroups ? total : kBwdGroups;
   return ROPE_QK_OK;
 }
 
 int64_t workspace_bytes(const NormGeometry& g, int64_t D) {
-  return (g.ntiles + g.nslices) * 2 * D * static_cast<int64_t>(sizeof(double));
+  return g.groups * 2 * D * static_cast<int64_t>(sizeof(double));
 }
 
 // Everything both passes check: the shared call checks, the norm's own limits
 // (eps, full rotary dim, row shape) and each tensor's alignment and layout.
 int check_norm_call(int dtype, int64_t nseq, int64_t T, int64_t Hq, int64_t Hkv, int64_t D, double theta,
                     const rope_qk_options& o, double eps, const float* wq, const float* wk, const Tensor* ts,
-                    int nts, NormGeometry* g) {
+                    int nts, bool bwd, NormGeometry* g) {
   int status = check_call(dtype, nseq, T, Hq, Hkv, D, theta, o);
   if (status != ROPE_QK_OK) return status;
   if (!(eps > 0.0) || !isfinite(eps) || (o.rotary_dim != 0 && o.rotary_dim != D)) return ROPE_QK_ERR_OPTION;
-  status = norm_geometry(T, Hq, Hkv, D, dtype, g);
+  status = norm_geometry(T, Hq, Hkv, D, dtype, bwd, g);
   if (status != ROPE_QK_OK) return status;
   if (T == 0 || Hq + Hkv == 0) return ROPE_QK_OK;
   if ((Hq > 0 && wq == nullptr) || (Hkv > 0 && wk == nullptr)) return ROPE_QK_ERR_NULL;
@@ -497,24 +619,29 @@ int check_norm_call(int dtype, int64_t nseq, int64_t T, int64_t Hq, int64_t Hkv,
 }
 
 void fill_params(NormParams* p, const NormGeometry& g, const int32_t* cu, int64_t nseq, int64_t T, int64_t Hq,
-                 int64_t Hkv, int64_t D, double theta, double eps, int dtype, const rope_qk_options& o,
-                 const float* wq, const float* wk, double sign) {
-  const int64_t H = Hq + Hkv;
-  p->wq = wq;
-  p->wk = wk;
+                 int64_t Hkv, int64_t D, double theta, double eps, const rope_qk_options& o, const float* wq,
+                 const float* wk, double sign) {
+  const int64_t Hs[2] = {Hq, Hkv};
+  const float* ws[2] = {wq, wk};
+  for (int s = 0; s < 2; ++s) {
+    NormTensor& tn = p->ten[s];
+    const int64_t H = Hs[s] > 0 ? Hs[s] : 1;
+    tn.w = ws[s];
+    tn.magic_heads = ((uint64_t(1) << 40) + H - 1) / H;
+    tn.rcp_heads = 1.0 / static_cast<double>(H);
+    tn.H = static_cast<int32_t>(Hs[s]);
+    tn.tile_rows = static_cast<int32_t>(g.tile_rows[s]);
+    tn.ntiles = static_cast<uint32_t>(g.ntiles[s]);
+  }
   p->cu = cu;
   p->T = T;
-  p->magic_heads = ((uint64_t(1) << 40) + H - 1) / H;
   p->magic_half = ((uint64_t(1) << 32) + D / 2 - 1) / (D / 2);
-  p->rcp_heads = 1.0 / static_cast<double>(H);
   p->eps = eps;
   p->inv_d = 1.0 / static_cast<double>(D);
   p->sign = sign;
-  p->ntiles = static_cast<uint32_t>(g.ntiles);
-  p->tile_rows = static_cast<int32_t>(g.tile_rows);
+  p->ntiles = static_cast<uint32_t>(g.ntiles[0] + g.ntiles[1]);
+  p->table_bytes = static_cast<int32_t>(g.table_bytes);
   p->nseq = static_cast<int32_t>(nseq);
-  p->Hq = static_cast<int32_t>(Hq);
-  p->H = static_cast<int32_t>(H);
   p->D = static_cast<int32_t>(D);
   p->half = static_cast<int32_t>(D / 2);
   p->L = static_cast<int32_t>(g.L);
@@ -526,35 +653,35 @@ void fill_params(NormParams* p, const NormGeometry& g, const int32_t* cu, int64_
   fill_inv_freq(theta, D, o, p->inv_freq);
 }
 
+void set_tensor(NormTensor* tn, const void* x, const Tensor& tx, const void* gr, const Tensor* tg, void* o,
+                const Tensor& to, int64_t esz) {
+  tn->x = static_cast<const char*>(x);
+  tn->x_st = tx.st * esz;
+  tn->x_sh = tx.sh * esz;
+  tn->g = static_cast<const char*>(gr);
+  tn->g_st = tg ? tg->st * esz : 0;
+  tn->g_sh = tg ? tg->sh * esz : 0;
+  tn->o = static_cast<char*>(o);
+  tn->o_st = to.st * esz;
+  tn->o_sh = to.sh * esz;
+}
+
 bool same_tensor(const Tensor& a, const Tensor& b) { return a.base == b.base && a.st == b.st && a.sh == b.sh; }
 
-size_t norm_lds(int64_t D, bool bwd) {
-  return static_cast<size_t>(kMaxTableBytes) + static_cast<size_t>(2 * D) * sizeof(float) +
-         (bwd ? static_cast<size_t>(kWaves * 2 * D) * sizeof(double) : 0);
+const void* pick_fwd(int dtype, bool il) {
+#define ROPE_NF(DT) (il ? reinterpret_cast<const void*>(&rope_qk_norm_fwd_kernel<DT, true, kFwdTasks>) \
+                        : reinterpret_cast<const void*>(&rope_qk_norm_fwd_kernel<DT, false, kFwdTasks>))
+  return dtype == ROPE_QK_BF16 ? ROPE_NF(ROPE_QK_BF16) : dtype == ROPE_QK_FP16 ? ROPE_NF(ROPE_QK_FP16)
+                                                                               : ROPE_NF(ROPE_QK_FP32);
+#undef ROPE_NF
 }
 
-const void* pick_norm_kernel(int dtype, bool interleaved, bool bwd) {
-#define ROPE_NK(DT, IL, BW) reinterpret_cast<const void*>(&rope_qk_norm_kernel<DT, IL, BW, kNormTasks>)
-#define ROPE_NK_DT(DT) \
-  (interleaved ? (bwd ? ROPE_NK(DT, true, true) : ROPE_NK(DT, true, false)) \
-               : (bwd ? ROPE_NK(DT, false, true) : ROPE_NK(DT, false, false)))
-  return dtype == ROPE_QK_BF16 ? ROPE_NK_DT(ROPE_QK_BF16)
-         : dtype == ROPE_QK_FP16 ? ROPE_NK_DT(ROPE_QK_FP16)
-                                 : ROPE_NK_DT(ROPE_QK_FP32);
-#undef ROPE_NK_DT
-#undef ROPE_NK
-}
-
-int launch_norm(const NormParams& p, const NormGeometry& g, int64_t D, int dtype, bool interleaved, bool bwd,
-                hipStream_t stream) {
-  if (g.ntiles == 0) return ROPE_QK_OK;
-  const int64_t gx = g.ntiles < kGridX ? g.ntiles : kGridX;
-  const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>((g.ntiles + gx - 1) / gx));
-  NormParams pc = p;
-  void* args[] = {&pc};
-  const hipError_t err = hipLaunchKernel(pick_norm_kernel(dtype, interleaved, bwd), grid, dim3(kThreads), args,
-                                         norm_lds(D, bwd), stream);
-  return err == hipSuccess ? ROPE_QK_OK : ROPE_QK_ERR_LAUNCH;
+const void* pick_bwd(int dtype, bool il) {
+#define ROPE_NB(DT) (il ? reinterpret_cast<const void*>(&rope_qk_norm_bwd_kernel<DT, true, kBwdTasks>) \
+                        : reinterpret_cast<const void*>(&rope_qk_norm_bwd_kernel<DT, false, kBwdTasks>))
+  return dtype == ROPE_QK_BF16 ? ROPE_NB(ROPE_QK_BF16) : dtype == ROPE_QK_FP16 ? ROPE_NB(ROPE_QK_FP16)
+                                                                               : ROPE_NB(ROPE_QK_FP32);
+#undef ROPE_NB
 }
 
 }  // namespace
@@ -570,7 +697,7 @@ int rope_qk_norm_fwd(const void* q, const void* k, void* q_out, void* k_out, con
   const Tensor ts[4] = {{q, strides[0], strides[1]}, {k, strides[2], strides[3]},
                         {q_out, strides[4], strides[5]}, {k_out, strides[6], strides[7]}};
   NormGeometry g;
-  const int status = check_norm_call(dtype, nseq, T, Hq, Hkv, D, theta, o, eps, q_weight, k_weight, ts, 4, &g);
+  const int status = check_norm_call(dtype, nseq, T, Hq, Hkv, D, theta, o, eps, q_weight, k_weight, ts, 4, false, &g);
   if (status != ROPE_QK_OK) return status;
   if (T == 0 || Hq + Hkv == 0) return ROPE_QK_OK;
   const bool copy_q = Hq > 0 && !same_tensor(ts[0], ts[2]);
@@ -579,26 +706,27 @@ int rope_qk_norm_fwd(const void* q, const void* k, void* q_out, void* k_out, con
   if (cu_seqlens == nullptr) return ROPE_QK_ERR_NULL;
   const int64_t esz = dtype == ROPE_QK_FP32 ? 4 : 2;
   NormParams p;
-  fill_params(&p, g, cu_seqlens, nseq, T, Hq, Hkv, D, theta, eps, dtype, o, q_weight, k_weight, 1.0);
-  p.xq = static_cast<const char*>(q);
-  p.xk = static_cast<const char*>(k);
-  p.gq = p.gk = nullptr;
-  p.oq = static_cast<char*>(q_out);
-  p.ok = static_cast<char*>(k_out);
+  fill_params(&p, g, cu_seqlens, nseq, T, Hq, Hkv, D, theta, eps, o, q_weight, k_weight, 1.0);
+  set_tensor(&p.ten[0], q, ts[0], nullptr, nullptr, q_out, ts[2], esz);
+  set_tensor(&p.ten[1], k, ts[1], nullptr, nullptr, k_out, ts[3], esz);
+  p.ten[0].copy = copy_q;
+  p.ten[1].copy = copy_k;
   p.partial = nullptr;
-  p.xq_st = strides[0] * esz, p.xq_sh = strides[1] * esz, p.xk_st = strides[2] * esz, p.xk_sh = strides[3] * esz;
-  p.gq_st = p.gq_sh = p.gk_st = p.gk_sh = 0;
-  p.oq_st = strides[4] * esz, p.oq_sh = strides[5] * esz, p.ok_st = strides[6] * esz, p.ok_sh = strides[7] * esz;
-  p.copy_q = copy_q;
-  p.copy_k = copy_k;
-  return launch_norm(p, g, D, dtype, o.pairing == ROPE_QK_PAIR_INTERLEAVED, false, static_cast<hipStream_t>(stream));
+  const int64_t nt = p.ntiles;
+  const int64_t gx = nt < kGridX ? nt : kGridX;
+  const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>((nt + gx - 1) / gx));
+  const size_t lds = static_cast<size_t>(p.table_bytes) + static_cast<size_t>(2 * D) * sizeof(float);
+  void* args[] = {&p};
+  const hipError_t err = hipLaunchKernel(pick_fwd(dtype, o.pairing == ROPE_QK_PAIR_INTERLEAVED), grid,
+                                         dim3(kThreads), args, lds, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? ROPE_QK_OK : ROPE_QK_ERR_LAUNCH;
 }
 
 int64_t rope_qk_norm_bwd_workspace_bytes(int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int dtype) {
   if (dtype != ROPE_QK_FP32 && dtype != ROPE_QK_BF16 && dtype != ROPE_QK_FP16) return ROPE_QK_ERR_DTYPE;
   if (T < 0 || Hq < 0 || Hkv < 0 || D < 2 || (D & 1) || D > 2 * kMaxHalf || T > INT32_MAX) return ROPE_QK_ERR_SHAPE;
   NormGeometry g;
-  const int status = norm_geometry(T, Hq, Hkv, D, dtype, &g);
+  const int status = norm_geometry(T, Hq, Hkv, D, dtype, true, &g);
   if (status != ROPE_QK_OK) return status;
   return workspace_bytes(g, D);
 }
@@ -614,7 +742,7 @@ int rope_qk_norm_bwd(const void* dq_out, const void* dk_out, const void* q, cons
                         {q, strides[4], strides[5]},      {k, strides[6], strides[7]},
                         {dq, strides[8], strides[9]},     {dk, strides[10], strides[11]}};
   NormGeometry g;
-  const int status = check_norm_call(dtype, nseq, T, Hq, Hkv, D, theta, o, eps, q_weight, k_weight, ts, 6, &g);
+  const int status = check_norm_call(dtype, nseq, T, Hq, Hkv, D, theta, o, eps, q_weight, k_weight, ts, 6, true, &g);
   if (status != ROPE_QK_OK) return status;
   if ((Hq > 0 && dq_weight == nullptr) || (Hkv > 0 && dk_weight == nullptr)) return ROPE_QK_ERR_NULL;
   const int64_t need = workspace_bytes(g, D);
@@ -622,46 +750,32 @@ int rope_qk_norm_bwd(const void* dq_out, const void* dk_out, const void* q, cons
   if (workspace != nullptr && !aligned16(workspace)) return ROPE_QK_ERR_ALIGN;
   if (!(dq_weight == nullptr || aligned16(dq_weight)) || !(dk_weight == nullptr || aligned16(dk_weight)))
     return ROPE_QK_ERR_ALIGN;
-  if (g.ntiles > 0 && cu_seqlens == nullptr) return ROPE_QK_ERR_NULL;
+  if (g.groups > 0 && cu_seqlens == nullptr) return ROPE_QK_ERR_NULL;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t esz = dtype == ROPE_QK_FP32 ? 4 : 2;
   double* partial = static_cast<double*>(workspace);
-  double* sums = partial + g.ntiles * 2 * D;
-  if (g.ntiles > 0) {
+  if (g.groups > 0) {
     NormParams p;
-    fill_params(&p, g, cu_seqlens, nseq, T, Hq, Hkv, D, theta, eps, dtype, o, q_weight, k_weight, -1.0);
-    p.xq = static_cast<const char*>(q);
-    p.xk = static_cast<const char*>(k);
-    p.gq = static_cast<const char*>(dq_out);
-    p.gk = static_cast<const char*>(dk_out);
-    p.oq = static_cast<char*>(dq);
-    p.ok = static_cast<char*>(dk);
+    fill_params(&p, g, cu_seqlens, nseq, T, Hq, Hkv, D, theta, eps, o, q_weight, k_weight, -1.0);
+    set_tensor(&p.ten[0], q, ts[2], dq_out, &ts[0], dq, ts[4], esz);
+    set_tensor(&p.ten[1], k, ts[3], dk_out, &ts[1], dk, ts[5], esz);
+    p.ten[0].copy = Hq > 0 && !same_tensor(ts[0], ts[4]);
+    p.ten[1].copy = Hkv > 0 && !same_tensor(ts[1], ts[5]);
     p.partial = partial;
-    p.gq_st = strides[0] * esz, p.gq_sh = strides[1] * esz, p.gk_st = strides[2] * esz, p.gk_sh = strides[3] * esz;
-    p.xq_st = strides[4] * esz, p.xq_sh = strides[5] * esz, p.xk_st = strides[6] * esz, p.xk_sh = strides[7] * esz;
-    p.oq_st = strides[8] * esz, p.oq_sh = strides[9] * esz, p.ok_st = strides[10] * esz, p.ok_sh = strides[11] * esz;
-    p.copy_q = Hq > 0 && !same_tensor(ts[0], ts[4]);
-    p.copy_k = Hkv > 0 && !same_tensor(ts[1], ts[5]);
-    const int st = launch_norm(p, g, D, dtype, o.pairing == ROPE_QK_PAIR_INTERLEAVED, true, s);
-    if (st != ROPE_QK_OK) return st;
-    const uint32_t slice = static_cast<uint32_t>((g.ntiles + g.nslices - 1) / g.nslices);
-    const int32_t width = static_cast<int32_t>(2 * D);
-    uint32_t nt = static_cast<uint32_t>(g.ntiles);
-    void* a1[] = {&partial, &nt, const_cast<int32_t*>(&width), const_cast<uint32_t*>(&slice), &sums};
-    hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&dw_slices_kernel),
-                                     dim3(static_cast<uint32_t>((width + kThreads - 1) / kThreads),
-                                          static_cast<uint32_t>(g.nslices)),
-                                     dim3(kThreads), a1, 0, s);
+    const size_t lds = static_cast<size_t>(p.table_bytes) + static_cast<size_t>(2 * D) * sizeof(float) +
+                       static_cast<size_t>((2 + kWaves) * D) * sizeof(double);
+    void* args[] = {&p};
+    const hipError_t err = hipLaunchKernel(pick_bwd(dtype, o.pairing == ROPE_QK_PAIR_INTERLEAVED),
+                                           dim3(static_cast<uint32_t>(g.groups)), dim3(kThreads), args, lds, s);
     if (err != hipSuccess) return ROPE_QK_ERR_LAUNCH;
   }
   if (dq_weight == nullptr && dk_weight == nullptr) return ROPE_QK_OK;
-  uint32_t ns = static_cast<uint32_t>(g.nslices);
+  uint32_t ng = static_cast<uint32_t>(g.groups);
   int32_t d32 = static_cast<int32_t>(D);
-  const double* sums_c = sums;
-  void* a2[] = {const_cast<double**>(&sums_c), &ns, &d32, &dq_weight, &dk_weight};
-  const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&dw_final_kernel),
-                                         dim3(static_cast<uint32_t>((2 * D + kThreads - 1) / kThreads)),
-                                         dim3(kThreads), a2, 0, s);
+  const double* partial_c = partial;
+  void* args[] = {const_cast<double**>(&partial_c), &ng, &d32, &dq_weight, &dk_weight};
+  const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&dw_reduce_kernel),
+                                         dim3(static_cast<uint32_t>(2 * D)), dim3(kThreads), args, 0, s);
   return err == hipSuccess ? ROPE_QK_OK : ROPE_QK_ERR_LAUNCH;
 }
 
