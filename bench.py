@@ -367,6 +367,84 @@ def run_norm(args):
                       "peak": HBM_PEAK_GBS, **res}))
 
 
+def run_pack(args):
+    """The host packing pipeline: the native Best-Fit-Decreasing packer's
+    throughput (the oracle's on a bounded sample beside it), the
+    packed-metadata cache's miss and hit latency, and a 24-layer forward loop
+    over a BFD-packed batch (Qwen2.5-0.5B-shaped heads) that either looks the
+    batch's metadata up in the cache every layer or rebuilds and uploads
+    cu_seqlens every layer."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import packed_varlen_rotary_amd as P
+    import workloads as W
+
+    rng = np.random.default_rng(0)
+
+    def mixture(n):  # 80% U[32,512] / 20% U[2048,8192], the default workload's length mix
+        return np.where(rng.random(n) < 0.8, rng.integers(32, 513, size=n), rng.integers(2048, 8193, size=n))
+
+    cap = 16384
+    big = mixture(1_000_000)
+    best = min(_timed(lambda: P.pack_bfd(big, cap)) for _ in range(3))
+    sample = big[:4000]
+    t_or = _timed(lambda: oracle.bfd_pack(sample, cap))
+    log(f"[bench] pack: native BFD {big.size / best / 1e6:.2f} M lengths/s (1M lengths), "
+        f"oracle {sample.size / t_or / 1e3:.1f} K lengths/s (4000 lengths; quadratic)")
+    res = {"native_bfd": {"lengths": int(big.size), "s": best, "lengths_per_s": big.size / best},
+           "oracle_bfd": {"lengths": int(sample.size), "s": t_or, "lengths_per_s": sample.size / t_or}}
+    if torch.cuda.is_available():
+        dev = torch.device("cuda", 0)
+        torch.cuda.set_device(dev)
+        cache = P.PackCache(max_entries=8, device=dev)
+        cache.get(mixture(256), cap)  # the process's first pinned and device allocations: untimed
+        torch.cuda.synchronize()
+        batch = mixture(256)
+        t_miss = _timed(lambda: cache.get(batch, cap))
+        hits = 2000
+        t_hit = _timed(lambda: [cache.get(batch, cap) for _ in range(hits)]) / hits
+        plan = cache.get(batch, cap)
+        torch.cuda.synchronize()
+        layers, Hq, Hkv, D = 24, 14, 2, 64
+        q = W.randn((plan.T, Hq, D), "bf16", seed=1, device=dev)
+        k = W.randn((plan.T, Hkv, D), "bf16", seed=2, device=dev)
+
+        def cached_step():
+            for _ in range(layers):
+                P.rope_qk_fwd(q, k, cache.get(batch, cap).cu_seqlens, 1e6)
+
+        def rebuilt_step():
+            for _ in range(layers):
+                b, o, nb = P.pack_bfd(batch, cap)
+                cu = torch.as_tensor(P.packed_cu_seqlens(batch, b, o, nb, cap), device=dev)
+                P.rope_qk_fwd(q, k, cu, 1e6)
+
+        out = {}
+        for name, fn in (("cached", cached_step), ("rebuilt", rebuilt_step)):
+            fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+            out[name] = (time.perf_counter() - t0) / 10
+        log(f"[bench] pack cache: miss {t_miss * 1e6:.0f} us, hit {t_hit * 1e6:.2f} us; {layers}-layer forward loop "
+            f"over {plan.T} tokens: {out['cached'] * 1e3:.3f} ms cached vs {out['rebuilt'] * 1e3:.3f} ms rebuilt")
+        res["cache"] = {"miss_us": t_miss * 1e6, "hit_us": t_hit * 1e6, "batch_lengths": int(batch.size),
+                        "tokens": plan.T, "bins": plan.nbins}
+        res["layer_loop"] = {"layers": layers, "ms_cached": out["cached"] * 1e3, "ms_rebuilt": out["rebuilt"] * 1e3}
+        cache.close()
+    print(json.dumps({"metric": "host packing pipeline: BFD throughput and packed-metadata cache latency", **res}))
+
+
+def _timed(fn):
+    t0 = time.perf_counter()
+    fn()
+    return time.perf_counter() - t0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -380,6 +458,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of --copy-bytes (for HBM counter scaling)")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--pack", action="store_true",
+                    help="only time the BFD packer and the packed-metadata cache")
     ap.add_argument("--norm", action="store_true",
                     help="only time the fused RMSNorm + rotation kernels (forward and backward) on --workload")
     ap.add_argument("--copy-ceiling", action="store_true",
@@ -399,6 +479,9 @@ def main():
         return
     if args.norm:
         run_norm(args)
+        return
+    if args.pack:
+        run_pack(args)
         return
 
     w, r = run_gpu(args)

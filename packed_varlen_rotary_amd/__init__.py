@@ -20,8 +20,12 @@ from ._lib import (  # noqa: F401
     ROPE_QK_SCALING_NONE,
     RopeQKError,
     RopeQKOptions,
+    PackCache,
+    PackPlan,
     load,
     make_options,
+    pack_bfd,
+    packed_cu_seqlens,
     rope_qk_bwd,
     rope_qk_bwd_opt,
     rope_qk_fwd,
@@ -45,6 +49,10 @@ __all__ = [
     "make_options",
     "rope_qk_positions",
     "rope_qk_strerror",
+    "pack_bfd",
+    "packed_cu_seqlens",
+    "PackCache",
+    "PackPlan",
     "RopeQKError",
     "load",
     "LIB_PATH",

@@ -8,6 +8,7 @@ if the library is missing, every call raises.
 
 from __future__ import annotations
 
+import copy
 import ctypes
 import os
 import threading
@@ -27,7 +28,9 @@ ROPE_QK_FREQ_FP32 = 1
 
 # names exported by include/rope_qk.h
 EXPORTS = ("rope_qk_fwd", "rope_qk_bwd", "rope_qk_fwd_opt", "rope_qk_bwd_opt", "rope_qk_norm_fwd",
-           "rope_qk_norm_bwd", "rope_qk_norm_bwd_workspace_bytes", "rope_qk_positions", "rope_qk_strerror")
+           "rope_qk_norm_bwd", "rope_qk_norm_bwd_workspace_bytes", "rope_qk_positions", "rope_qk_strerror",
+           "rope_pack_bfd", "rope_pack_cu_seqlens", "rope_pack_cache_create", "rope_pack_cache_get",
+           "rope_pack_cache_stats", "rope_pack_cache_destroy")
 
 
 class RopeQKOptions(ctypes.Structure):
@@ -64,6 +67,23 @@ def make_options(pos_offset: int = 0, rotary_dim: int = 0, interleaved: bool = F
         o.high_freq_factor = float(llama3["high_freq_factor"])
         o.original_max_position = float(llama3["original_max_position"])
     return o
+
+class PackPlanStruct(ctypes.Structure):
+    """Mirror of ``rope_pack_plan`` (include/rope_pack.h)."""
+
+    _fields_ = [
+        ("cu_seqlens_device", ctypes.c_void_p),
+        ("cu_seqlens_host", ctypes.c_void_p),
+        ("bin_of", ctypes.c_void_p),
+        ("offset_of", ctypes.c_void_p),
+        ("n", ctypes.c_int64),
+        ("nseg", ctypes.c_int64),
+        ("nbins", ctypes.c_int64),
+        ("T", ctypes.c_int64),
+        ("max_seqlen", ctypes.c_int32),
+        ("hit", ctypes.c_int32),
+    ]
+
 
 _lock = threading.Lock()
 _lib = None
@@ -113,6 +133,18 @@ def load():
         lib.rope_qk_norm_bwd.restype = ctypes.c_int
         lib.rope_qk_norm_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         lib.rope_qk_norm_bwd_workspace_bytes.restype = ctypes.c_int64
+        lib.rope_pack_bfd.argtypes = [vp, i64, i64, vp, vp, ctypes.POINTER(i64)]
+        lib.rope_pack_bfd.restype = ctypes.c_int
+        lib.rope_pack_cu_seqlens.argtypes = [vp, vp, vp, i64, i64, i64, vp, ctypes.POINTER(i64)]
+        lib.rope_pack_cu_seqlens.restype = ctypes.c_int
+        lib.rope_pack_cache_create.argtypes = [i64, ctypes.c_int, ctypes.POINTER(vp)]
+        lib.rope_pack_cache_create.restype = ctypes.c_int
+        lib.rope_pack_cache_get.argtypes = [vp, vp, i64, i64, vp, ctypes.POINTER(PackPlanStruct)]
+        lib.rope_pack_cache_get.restype = ctypes.c_int
+        lib.rope_pack_cache_stats.argtypes = [vp, ctypes.POINTER(i64), ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        lib.rope_pack_cache_stats.restype = ctypes.c_int
+        lib.rope_pack_cache_destroy.argtypes = [vp]
+        lib.rope_pack_cache_destroy.restype = None
         lib.rope_qk_positions.argtypes = [vp, i64, i64, vp, vp]
         lib.rope_qk_positions.restype = ctypes.c_int
         lib.rope_qk_strerror.argtypes = [ctypes.c_int]
@@ -358,3 +390,153 @@ def rope_qk_norm_bwd(dq_out, dk_out, q, k, q_weight, k_weight, eps: float, cu_se
             float(theta), code, ctypes.byref(opts), _stream_ptr(q.device, stream))
     _check(status)
     return dq, dk, dq_weight, dk_weight
+
+
+# ---------------------------------------------------------------------------
+# Best-Fit-Decreasing packing and the packed-metadata cache (include/rope_pack.h)
+# ---------------------------------------------------------------------------
+
+def _lengths_i32(lengths):
+    import numpy as np
+
+    a = np.ascontiguousarray(np.asarray(lengths, dtype=np.int64))
+    if a.ndim != 1:
+        raise ValueError("lengths must be 1-D")
+    if a.size and (a.min() < -2 ** 31 or a.max() >= 2 ** 31):
+        raise ValueError("lengths must fit in int32")
+    return np.ascontiguousarray(a.astype(np.int32))
+
+
+def _host_ptr(a):
+    return ctypes.c_void_p(a.ctypes.data) if a.size else None
+
+
+def pack_bfd(lengths, capacity: int):
+    """Best-Fit-Decreasing packing (native): (bin_of, offset_of, nbins), int32 numpy arrays."""
+    import numpy as np
+
+    lib = load()
+    L = _lengths_i32(lengths)
+    bin_of = np.empty(L.size, dtype=np.int32)
+    offset_of = np.empty(L.size, dtype=np.int32)
+    nbins = ctypes.c_int64(0)
+    _check(lib.rope_pack_bfd(_host_ptr(L), L.size, int(capacity), _host_ptr(bin_of), _host_ptr(offset_of),
+                             ctypes.byref(nbins)))
+    return bin_of, offset_of, int(nbins.value)
+
+
+def packed_cu_seqlens(lengths, bin_of, offset_of, nbins: int, capacity: int):
+    """cu_seqlens (int32 numpy) of the packed batch over nbins * capacity tokens."""
+    import numpy as np
+
+    lib = load()
+    L = _lengths_i32(lengths)
+    b = np.ascontiguousarray(np.asarray(bin_of, dtype=np.int32))
+    o = np.ascontiguousarray(np.asarray(offset_of, dtype=np.int32))
+    if b.shape != L.shape or o.shape != L.shape:
+        raise ValueError("bin_of and offset_of must match lengths")
+    cu = np.empty(L.size + int(nbins) + 1, dtype=np.int32)
+    nseg = ctypes.c_int64(0)
+    _check(lib.rope_pack_cu_seqlens(_host_ptr(L), _host_ptr(b), _host_ptr(o), L.size, int(nbins), int(capacity),
+                                    _host_ptr(cu), ctypes.byref(nseg)))
+    return cu[: nseg.value + 1].copy()
+
+
+class _DeviceInt32:
+    """A device int32 vector owned by the native cache, shown to torch through
+    the CUDA array interface (zero copy)."""
+
+    def __init__(self, ptr: int, n: int):
+        self.__cuda_array_interface__ = {"shape": (n,), "typestr": "<i4", "data": (ptr, False), "version": 2,
+                                         "strides": None}
+
+
+class PackPlan:
+    """One packed batch from PackCache.get.  cu_seqlens: device int32 tensor
+    (a view of the cache's buffer; None for a host-only cache); the rest are
+    host copies.  The device view stays valid until the plan is evicted from
+    its cache (after max_entries other batches) or the cache is closed."""
+
+    def __init__(self, s: PackPlanStruct, device):
+        import numpy as np
+
+        nseg, n = int(s.nseg), int(s.n)
+        host = (ctypes.c_int32 * (nseg + 1)).from_address(s.cu_seqlens_host)
+        self.cu_seqlens_host = np.frombuffer(host, dtype=np.int32).copy()
+        self.bin_of = np.frombuffer((ctypes.c_int32 * n).from_address(s.bin_of), dtype=np.int32).copy() if n else \
+            np.empty(0, dtype=np.int32)
+        self.offset_of = np.frombuffer((ctypes.c_int32 * n).from_address(s.offset_of), dtype=np.int32).copy() \
+            if n else np.empty(0, dtype=np.int32)
+        self.n, self.nseg, self.nbins, self.T = n, nseg, int(s.nbins), int(s.T)
+        self.max_seqlen = int(s.max_seqlen)
+        self.hit = bool(s.hit)
+        self.cu_seqlens_ptr = int(s.cu_seqlens_device or 0)
+        self.cu_seqlens = None
+        if self.cu_seqlens_ptr:
+            import torch
+
+            self.cu_seqlens = torch.as_tensor(_DeviceInt32(self.cu_seqlens_ptr, nseg + 1), device=device)
+
+
+class PackCache:
+    """The native packed-metadata cache (rope_pack_cache_*): pack a batch once,
+    upload its cu_seqlens once, answer every later lookup on the host.
+
+    device: a torch device (default: the current CUDA device), or None with
+    host_only=True for a cache without device memory.
+    """
+
+    def __init__(self, max_entries: int = 64, device=None, host_only: bool = False):
+        lib = load()
+        self._lib = lib
+        self._ptr = None
+        self._max_entries = int(max_entries)
+        if host_only:
+            self.device, code = None, -1
+        else:
+            import torch
+
+            self.device = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+            code = self.device.index if self.device.index is not None else torch.cuda.current_device()
+        ptr = ctypes.c_void_p()
+        _check(lib.rope_pack_cache_create(int(max_entries), int(code), ctypes.byref(ptr)))
+        self._ptr = ptr
+        # Python views of the plans held, by their host cu_seqlens buffer: a hit
+        # returns the view made on that plan's miss (the native cache only
+        # answers a hit for a plan that this wrapper saw being created)
+        self._views = {}
+
+    def get(self, lengths, capacity: int, stream=None) -> PackPlan:
+        if self._ptr is None:
+            raise RuntimeError("the cache is closed")
+        L = _lengths_i32(lengths)
+        s = PackPlanStruct()
+        sp = _stream_ptr(self.device, stream) if self.device is not None else None
+        _check(self._lib.rope_pack_cache_get(self._ptr, _host_ptr(L), L.size, int(capacity), sp, ctypes.byref(s)))
+        key = int(s.cu_seqlens_host or 0)
+        view = self._views.get(key) if s.hit else None
+        if view is None:
+            view = PackPlan(s, self.device)
+            self._views[key] = view
+            if len(self._views) > 4 * self._max_entries:  # drop views of plans long evicted
+                self._views = {key: view}
+        out = copy.copy(view)  # shares the arrays and the device view; its own hit flag
+        out.hit = bool(s.hit)
+        return out
+
+    def stats(self):
+        """(hits, misses, entries)."""
+        h, m, e = ctypes.c_int64(0), ctypes.c_int64(0), ctypes.c_int64(0)
+        _check(self._lib.rope_pack_cache_stats(self._ptr, ctypes.byref(h), ctypes.byref(m), ctypes.byref(e)))
+        return int(h.value), int(m.value), int(e.value)
+
+    def close(self):
+        if self._ptr is not None:
+            self._lib.rope_pack_cache_destroy(self._ptr)
+            self._ptr = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -13,7 +13,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", n) for n in ("rope_qk.hip", "rope_qk_norm.hip")]
+SRCS = [os.path.join(PKG, "csrc", n) for n in ("rope_qk.hip", "rope_qk_norm.hip", "rope_pack.cpp")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librope_qk.so")
 

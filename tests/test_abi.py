@@ -20,9 +20,13 @@ HEADER = os.path.join(ROOT, "include", "rope_qk.h")
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(rope_qk_\w+)\s*\(", text)))
+    """Functions declared by every header under include/."""
+    names = set()
+    for name in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if name.endswith(".h"):
+            text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", name)).read(), flags=re.S)
+            names |= set(re.findall(r"\b(rope_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def header_constants():
@@ -57,7 +61,7 @@ def test_library_exports_every_declared_symbol():
     for name in declared_functions():
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", P.LIB_PATH], capture_output=True, text=True, check=True).stdout
-    exported = set(re.findall(r"\sT\s(rope_qk_\w+)$", out, flags=re.M))
+    exported = set(re.findall(r"\sT\s(rope_\w+)$", out, flags=re.M))
     assert exported == set(declared_functions())
 
 
