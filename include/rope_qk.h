@@ -31,7 +31,8 @@
  *
  * pos(t) = t - cu_seqlens[s], where s is the last index with cu_seqlens[s] <= t,
  * so positions restart at 0 at every sequence boundary.  Tokens t < cu_seqlens[0]
- * and t >= cu_seqlens[nseq] are not read and not written.  The rotation is
+ * and t >= cu_seqlens[nseq] are not written (a tile may read them while its
+ * positions are still being found).  The rotation is
  * evaluated in float64 and rounded once to the storage type (round to nearest,
  * ties to even): bf16 and fp16 results are the correctly rounded bf16 or fp16
  * of the float64 rotation, fp32 results the correctly rounded fp32.

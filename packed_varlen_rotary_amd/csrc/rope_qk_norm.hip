@@ -262,89 +262,96 @@ __device__ __forceinline__ bool bwd_chunk_dx(const u32x4& x, const double* gw, d
   return tie;
 }
 
-// One tile: tile_rows consecutive rows of one tensor.  s_w holds both
-// tensors' weights (q then k); acc (backward) receives this lane's
-// weight-gradient terms.
-template <int kDtype, bool kIl, bool kBwd, int kTPT>
-__device__ __forceinline__ void norm_tile(const NormParams& p, uint32_t tile, int32_t* s_pos, double2* s_cs,
-                                          const float* s_w, double* acc) {
-  constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;  // elements per chunk
-  constexpr int kPPC = kIl ? kVec / 2 : kVec;          // table pairs per chunk
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int L = p.L;
-  const int c = tid & (L - 1);  // the chunk of its rows this lane holds
-  const int hl = L >> 1;        // chunks per half row
-  const cu_ptr cu = (cu_ptr)p.cu;
-  const int32_t nseq = p.nseq;
-  const int sel = tile >= p.ten[0].ntiles ? 1 : 0;  // 0: q, 1: k (wave-uniform)
-  const NormTensor& tn = p.ten[sel];
-  const uint32_t lt = tile - (sel ? p.ten[0].ntiles : 0u);
-  const int32_t H = tn.H;
+// Scalar geometry of one tile: its tensor, first row n0 = t0 * H + r0, the
+// tokens [t0, t_end) it touches and its table entries (tokens x pairs).
+struct TileGeom {
+  int sel;  // 0: q, 1: k
+  uint32_t r0;
+  int ntok, nent;
+  int64_t n0, t0, n_end, t_end;
+};
 
-  // first row n0 = t0 * H + r0 (n0 < 2^47 is exact in float64; the rounded quotient is off by at most one)
-  const int64_t n0 = static_cast<int64_t>(lt) * tn.tile_rows;
-  int32_t t0i = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(static_cast<double>(n0) * tn.rcp_heads));
-  int64_t r0l = n0 - static_cast<int64_t>(t0i) * H;
+__device__ __forceinline__ TileGeom tile_geom(const NormParams& p, uint32_t tile) {
+  TileGeom gm;
+  gm.sel = tile >= p.ten[0].ntiles ? 1 : 0;  // wave-uniform
+  const NormTensor& tn = p.ten[gm.sel];
+  const uint32_t lt = tile - (gm.sel ? p.ten[0].ntiles : 0u);
+  const int32_t H = tn.H;
+  // n0 < 2^47 is exact in float64; the rounded quotient is off by at most one
+  gm.n0 = static_cast<int64_t>(lt) * tn.tile_rows;
+  int32_t t0i = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(static_cast<double>(gm.n0) * tn.rcp_heads));
+  int64_t r0l = gm.n0 - static_cast<int64_t>(t0i) * H;
   if (r0l < 0) { t0i -= 1; r0l += H; }
   if (r0l >= H) { t0i += 1; r0l -= H; }
-  const int64_t t0 = t0i;
-  const uint32_t r0 = static_cast<uint32_t>(r0l);
-  const int64_t n_end = min(n0 + tn.tile_rows, p.T * H);
-  const int ntok = static_cast<int>(div_tok(static_cast<uint32_t>(n_end - n0) + r0 - 1, tn.magic_heads)) + 1;
-  const int64_t t_end = t0 + ntok;
-  const int nent = ntok * p.half;
+  gm.t0 = t0i;
+  gm.r0 = static_cast<uint32_t>(r0l);
+  gm.n_end = min(gm.n0 + tn.tile_rows, p.T * H);
+  gm.ntok = static_cast<int>(div_tok(static_cast<uint32_t>(gm.n_end - gm.n0) + gm.r0 - 1, tn.magic_heads)) + 1;
+  gm.t_end = gm.t0 + gm.ntok;
+  gm.nent = gm.ntok * p.half;
+  return gm;
+}
 
-  // 1. inv_freq of this thread's table entries, before the data
-  double f[kEnt];
-  int tt_e[kEnt], i_e[kEnt];
-#pragma unroll
-  for (int v = 0; v < kEnt; ++v) {
-    const int e = tid + v * kThreads;
-    const int tt = e < nent ? static_cast<int>(div_small(static_cast<uint32_t>(e), p.magic_half)) : 0;
-    tt_e[v] = tt;
-    i_e[v] = e < nent ? e - tt * p.half : 0;
-    f[v] = (v == 0 || v * kThreads < nent) ? p.inv_freq[i_e[v]] : 0.0;
-  }
-  // forward: the weights of each table pair's two elements, folded into the table
-  float w1[kEnt], w2[kEnt];
-#pragma unroll
-  for (int v = 0; v < kEnt; ++v) {
-    w1[v] = w2[v] = 0.f;
-    if (!kBwd && (v == 0 || v * kThreads < nent)) {
-      w1[v] = tn.w[kIl ? 2 * i_e[v] : i_e[v]];
-      w2[v] = tn.w[kIl ? 2 * i_e[v] + 1 : i_e[v] + p.half];
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  // 2. every load of the tile (rows past the tile's end re-read its first row)
+// A lane's rows of one tile: the loaded chunks (x; backward also dy), where
+// its outputs go, and which tile token each row belongs to.
+template <int kTPT>
+struct TileData {
   u32x4 a[kTPT], g[kTPT];
   gchar* optr[kTPT];
   int tt_of[kTPT];
   bool act[kTPT];
+};
+
+// Issue every load of a tile (rows past the tile's end re-read its first row).
+template <bool kBwd, int kTPT>
+__device__ __forceinline__ void tile_loads(const NormParams& p, const TileGeom& gm, TileData<kTPT>& d) {
+  const int tid = threadIdx.x;
+  const NormTensor& tn = p.ten[gm.sel];
+  const int32_t H = tn.H;
   const int rows_per_step = kThreads >> p.lshift;
-  const int64_t off = static_cast<int64_t>(c) * 16;
+  const int64_t off = static_cast<int64_t>(tid & (p.L - 1)) * 16;
 #pragma unroll
   for (int u = 0; u < kTPT; ++u) {
     const int lr = u * rows_per_step + (tid >> p.lshift);
-    act[u] = n0 + lr < n_end;
-    const uint32_t l = act[u] ? r0 + static_cast<uint32_t>(lr) : r0;
+    d.act[u] = gm.n0 + lr < gm.n_end;
+    const uint32_t l = d.act[u] ? gm.r0 + static_cast<uint32_t>(lr) : gm.r0;
     const uint32_t tt = div_tok(l, tn.magic_heads);
     const int64_t h = static_cast<int64_t>(l - tt * static_cast<uint32_t>(H));
-    const int64_t t = t0 + tt;
-    a[u] = __builtin_nontemporal_load(
+    const int64_t t = gm.t0 + tt;
+    d.a[u] = __builtin_nontemporal_load(
         reinterpret_cast<const gu32x4*>((const gchar*)tn.x + t * tn.x_st + h * tn.x_sh + off));
     if constexpr (kBwd)
-      g[u] = __builtin_nontemporal_load(
+      d.g[u] = __builtin_nontemporal_load(
           reinterpret_cast<const gu32x4*>((const gchar*)tn.g + t * tn.g_st + h * tn.g_sh + off));
-    optr[u] = (gchar*)tn.o + t * tn.o_st + h * tn.o_sh + off;
-    tt_of[u] = static_cast<int>(tt);
+    d.optr[u] = (gchar*)tn.o + t * tn.o_st + h * tn.o_sh + off;
+    d.tt_of[u] = static_cast<int>(tt);
   }
-  __builtin_amdgcn_sched_barrier(0);
+}
 
-  // 3. positions and the table
-  const int32_t s0 = last_start_at_or_before(cu, nseq, t0);
+// This thread's table entries e = tid + v * 256 of a tile: token and pair.
+__device__ __forceinline__ void tile_entries(const NormParams& p, const TileGeom& gm, int* tt_e, int* i_e) {
+#pragma unroll
+  for (int v = 0; v < kEnt; ++v) {
+    const int e = threadIdx.x + v * kThreads;
+    const int tt = e < gm.nent ? static_cast<int>(div_small(static_cast<uint32_t>(e), p.magic_half)) : 0;
+    tt_e[v] = tt;
+    i_e[v] = e < gm.nent ? e - tt * p.half : 0;
+  }
+}
+
+// Positions and the table of a tile, from each entry's frequency f (and, for
+// the forward, the weights w1, w2 of the pair's two elements); ends with a
+// barrier.
+template <int kDtype, bool kIl, bool kBwd>
+__device__ __forceinline__ void tile_table(const NormParams& p, const TileGeom& gm, const int* tt_e, const int* i_e,
+                                           const double* f, const float* w1, const float* w2, int32_t* s_pos,
+                                           double2* s_cs) {
+  constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;
+  constexpr int kPPC = kIl ? kVec / 2 : kVec;
+  const int L = p.L, hl = p.L >> 1;
+  const cu_ptr cu = (cu_ptr)p.cu;
+  const int32_t nseq = p.nseq;
+  const int32_t s0 = last_start_at_or_before(cu, nseq, gm.t0);
   const int64_t cu_last = cu[nseq];
   const int64_t cu_first_end = nseq >= 1 ? static_cast<int64_t>(cu[1]) : INT64_MIN;  // cu[1] exists only then
   int64_t start[kEnt];
@@ -352,19 +359,19 @@ __device__ __forceinline__ void norm_tile(const NormParams& p, uint32_t tile, in
   for (int v = 0; v < kEnt; ++v) start[v] = s0 >= 0 ? static_cast<int64_t>(cu[s0]) : INT64_MIN;
   for (int32_t j = s0 + 1; j <= nseq; ++j) {
     const int64_t cv = cu[j];
-    if (cv >= t_end) break;
+    if (cv >= gm.t_end) break;
 #pragma unroll
-    for (int v = 0; v < kEnt; ++v) start[v] = cv <= t0 + tt_e[v] ? cv : start[v];
+    for (int v = 0; v < kEnt; ++v) start[v] = cv <= gm.t0 + tt_e[v] ? cv : start[v];
   }
 #pragma unroll
   for (int v = 0; v < kEnt; ++v) {
-    if (v > 0 && v * kThreads >= nent) break;
-    const int e = tid + v * kThreads;
-    const int64_t t = t0 + tt_e[v];
+    if (v > 0 && v * kThreads >= gm.nent) break;
+    const int e = threadIdx.x + v * kThreads;
+    const int64_t t = gm.t0 + tt_e[v];
     const bool inside = start[v] != INT64_MIN && t < cu_last;
     const int64_t pos64 = inside ? t - start[v] + (t < cu_first_end ? p.pos_offset : 0) : -1;
     const int32_t pos = pos64 <= INT32_MAX ? static_cast<int32_t>(pos64) : -1;
-    if (e < nent) {
+    if (e < gm.nent) {
       if (i_e[v] == 0) s_pos[tt_e[v]] = pos;
       if (pos >= 0) {
         double sn, cs;
@@ -385,9 +392,29 @@ __device__ __forceinline__ void norm_tile(const NormParams& p, uint32_t tile, in
     }
   }
   __syncthreads();
+}
 
-  // 4. every row of the tile: r for all rows (their lane sums together),
-  //    then the forward rows one at a time, or the backward in phases
+// Every row of a tile (after its table): r for all rows (their lane sums
+// together), then the forward rows one at a time, or the backward in phases;
+// then the stores.  s_w holds both tensors' weights (q then k); acc
+// (backward) receives this lane's weight-gradient terms.
+template <int kDtype, bool kIl, bool kBwd, int kTPT>
+__device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom& gm, const TileData<kTPT>& d,
+                                             const int32_t* s_pos, const double2* s_cs, const float* s_w,
+                                             double* acc) {
+  constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;  // elements per chunk
+  constexpr int kPPC = kIl ? kVec / 2 : kVec;          // table pairs per chunk
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int L = p.L;
+  const int c = tid & (L - 1);
+  const int hl = L >> 1;
+  const int sel = gm.sel;
+  const NormTensor& tn = p.ten[sel];
+  const u32x4* a = d.a;
+  const u32x4* g = d.g;
+  const int* tt_of = d.tt_of;
+  const bool* act = d.act;
   const int paddr = (lane ^ hl) << 2;  // rotate_half partner lane
   const bool first = c < hl;
   bool st[kTPT], inside[kTPT];
@@ -441,12 +468,38 @@ __device__ __forceinline__ void norm_tile(const NormParams& p, uint32_t tile, in
 #pragma unroll
   for (int u = 0; u < kTPT; ++u) {
     if (!st[u]) continue;
-    __builtin_nontemporal_store(out[u], reinterpret_cast<gu32x4*>(optr[u]));
+    __builtin_nontemporal_store(out[u], reinterpret_cast<gu32x4*>(d.optr[u]));
   }
 }
 
+
+// The forward tile: its frequencies and weights are loaded before its data.
+template <int kDtype, bool kIl, int kTPT>
+__device__ __forceinline__ void fwd_tile(const NormParams& p, uint32_t tile, int32_t* s_pos, double2* s_cs) {
+  const TileGeom gm = tile_geom(p, tile);
+  const NormTensor& tn = p.ten[gm.sel];
+  int tt_e[kEnt], i_e[kEnt];
+  tile_entries(p, gm, tt_e, i_e);
+  double f[kEnt];
+  float w1[kEnt], w2[kEnt];
+#pragma unroll
+  for (int v = 0; v < kEnt; ++v) {
+    const bool live = v == 0 || v * kThreads < gm.nent;
+    f[v] = live ? p.inv_freq[i_e[v]] : 0.0;
+    w1[v] = live ? tn.w[kIl ? 2 * i_e[v] : i_e[v]] : 0.f;
+    w2[v] = live ? tn.w[kIl ? 2 * i_e[v] + 1 : i_e[v] + p.half] : 0.f;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  TileData<kTPT> d;
+  tile_loads<false, kTPT>(p, gm, d);
+  __builtin_amdgcn_sched_barrier(0);
+  tile_table<kDtype, kIl, false>(p, gm, tt_e, i_e, f, w1, w2, s_pos, s_cs);
+  tile_compute<kDtype, kIl, false, kTPT>(p, gm, d, s_pos, s_cs, nullptr, nullptr);
+}
+
 // LDS of the norm kernels after the table: weights [2 D] floats, then (backward)
-// the workgroup's weight-gradient sums [2 D] and one tile's per-wave sums [4][D], doubles.
+// the workgroup's weight-gradient sums [2 D], one tile's per-wave sums [4][D]
+// and the frequencies [D / 2], doubles.
 __device__ __forceinline__ float* lds_weights(double2* s_cs, const NormParams& p) {
   return reinterpret_cast<float*>(reinterpret_cast<char*>(s_cs) + p.table_bytes);
 }
@@ -469,10 +522,14 @@ __global__ __launch_bounds__(kThreads) void rope_qk_norm_fwd_kernel(const NormPa
   extern __shared__ double2 s_cs[];
   const uint32_t tile = blockIdx.y * gridDim.x + blockIdx.x;
   if (tile >= p.ntiles) return;
-  norm_tile<kDtype, kIl, false, kTPT>(p, tile, s_pos, s_cs, nullptr, nullptr);
+  fwd_tile<kDtype, kIl, kTPT>(p, tile, s_pos, s_cs);
 }
 
-// Backward: gridDim.x workgroups, each taking tiles blockIdx.x, + gridDim.x, ...
+// Backward: gridDim.x workgroups, each taking tiles blockIdx.x, + gridDim.x,
+// ...; the weights and frequencies sit in LDS for all of a workgroup's tiles.
+// (Issuing the next tile's loads before the current tile's work measured no
+// faster: this kernel waits on its lane-exchange and barrier latencies, with
+// two waves per SIMD at its register count, more than on memory.)
 template <int kDtype, bool kIl, int kTPT>
 __global__ __launch_bounds__(kThreads) void rope_qk_norm_bwd_kernel(const NormParams p) {
   constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;
@@ -481,17 +538,29 @@ __global__ __launch_bounds__(kThreads) void rope_qk_norm_bwd_kernel(const NormPa
   float* s_w = lds_weights(s_cs, p);
   double* s_acc = reinterpret_cast<double*>(s_w + 2 * p.D);  // [2 D]
   double* s_wave = s_acc + 2 * p.D;                          // [kWaves][D]
+  double* s_freq = s_wave + kWaves * p.D;                    // [D / 2]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = p.L, D = p.D;
   const int c = tid & (L - 1);
   load_weights(p, s_w);
   for (int i = tid; i < 2 * D; i += kThreads) s_acc[i] = 0.0;
+  for (int i = tid; i < p.half; i += kThreads) s_freq[i] = p.inv_freq[i];
   __syncthreads();
   for (uint32_t tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
+    const TileGeom gm = tile_geom(p, tile);
+    TileData<kTPT> d;
+    tile_loads<true, kTPT>(p, gm, d);
+    __builtin_amdgcn_sched_barrier(0);
+    int tt_e[kEnt], i_e[kEnt];
+    double f[kEnt];
+    tile_entries(p, gm, tt_e, i_e);
+#pragma unroll
+    for (int v = 0; v < kEnt; ++v) f[v] = s_freq[i_e[v]];
+    tile_table<kDtype, kIl, true>(p, gm, tt_e, i_e, f, nullptr, nullptr, s_pos, s_cs);
     double acc[kVec];
 #pragma unroll
     for (int j = 0; j < kVec; ++j) acc[j] = 0.0;
-    norm_tile<kDtype, kIl, true, kTPT>(p, tile, s_pos, s_cs, s_w, acc);
+    tile_compute<kDtype, kIl, true, kTPT>(p, gm, d, s_pos, s_cs, s_w, acc);
     // lanes holding the same chunk, then the waves, into the workgroup's sums
     for (int m = L; m < 64; m <<= 1) {
       const int addr = (lane ^ m) << 2;
@@ -503,12 +572,11 @@ __global__ __launch_bounds__(kThreads) void rope_qk_norm_bwd_kernel(const NormPa
       for (int j = 0; j < kVec; ++j) s_wave[wave * D + c * kVec + j] = acc[j];
     }
     __syncthreads();
-    const int sel = tile >= p.ten[0].ntiles ? 1 : 0;
     for (int col = tid; col < D; col += kThreads) {
       double s = s_wave[col];
 #pragma unroll
       for (int wv = 1; wv < kWaves; ++wv) s += s_wave[wv * D + col];
-      s_acc[sel * D + col] += s;
+      s_acc[gm.sel * D + col] += s;
     }
     __syncthreads();  // the table, positions and wave sums are rewritten by the next tile
   }
@@ -763,7 +831,7 @@ int rope_qk_norm_bwd(const void* dq_out, const void* dk_out, const void* q, cons
     p.ten[1].copy = Hkv > 0 && !same_tensor(ts[1], ts[5]);
     p.partial = partial;
     const size_t lds = static_cast<size_t>(p.table_bytes) + static_cast<size_t>(2 * D) * sizeof(float) +
-                       static_cast<size_t>((2 + kWaves) * D) * sizeof(double);
+                       static_cast<size_t>((2 + kWaves) * D + D / 2) * sizeof(double);
     void* args[] = {&p};
     const hipError_t err = hipLaunchKernel(pick_bwd(dtype, o.pairing == ROPE_QK_PAIR_INTERLEAVED),
                                            dim3(static_cast<uint32_t>(g.groups)), dim3(kThreads), args, lds, s);
