@@ -291,3 +291,25 @@ def test_side_stream_and_binding_errors():
     with pytest.raises(P.RopeQKError) as e:
         P.rope_qk_fwd(odd, odd[:, :1], cu_dev([0, 8]), 1e4)
     assert e.value.status == -4
+
+
+@pytest.mark.parametrize("offset", [0, 2 ** 31 - 1 - 600])
+def test_chained_table_boundaries_and_large_positions(offset):
+    """Few heads at D = 64 and 32: each thread fills the cos/sin table for up to
+    four consecutive tokens by turning the previous entry; sequences of 1 to 5
+    tokens break the chains often; positions up to 2^31 - 2, where an angle's
+    float64 ulp is largest.  Every element exact against the oracle."""
+    rng = np.random.default_rng(77)
+    T = 600
+    lengths = rng.integers(1, 6, size=400)
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    cu = cu[cu <= T]
+    for D, Hq, Hkv in ((64, 2, 1), (32, 1, 1)):
+        q = W.randn((T, Hq, D), "bf16", seed=D, device=DEV)
+        k = W.randn((T, Hkv, D), "bf16", seed=D + 1, device=DEV)
+        xq, xk = f64(q), f64(k)
+        P.rope_qk_fwd(q, k, cu_dev(cu), 1e4, pos_offset=offset)
+        torch.cuda.synchronize()
+        for got, x in ((q, xq), (k, xk)):
+            s = check_against(got, oracle.rope(x, cu, 1e4, 1, pos_offset=offset), f"D{D}")
+            assert s["exact_fraction"] == 1.0, s
