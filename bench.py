@@ -439,6 +439,65 @@ def run_pack(args):
     print(json.dumps({"metric": "host packing pipeline: BFD throughput and packed-metadata cache latency", **res}))
 
 
+def run_eager_baseline(args):
+    """Context for the fusion: an unfused rotate_half RoPE written with PyTorch
+    eager ops (float32 cos/sin tables gathered by position, q and k rotated
+    separately, out of place) on the same workload and GPU, next to the fused
+    in-place kernel.  Not a parity path: only its time is reported."""
+    import torch
+
+    import packed_varlen_rotary_amd as P
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    w = W.make_workload(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cu = torch.as_tensor(w.cu_seqlens, device=dev)
+    nsets = max(1, min(16, -(-(1 << 30) // w.bytes_per_pass)))
+    sets = [W.make_tensors(w, ("q", "k"), device=dev, salt=s) for s in range(nsets)]
+    pos = P.rope_qk_positions(cu, w.T).clamp_min(0).long()
+    half = w.D // 2
+    inv = 1.0 / (w.theta ** (torch.arange(0, half, device=dev, dtype=torch.float32) * 2.0 / w.D))
+    max_pos = int(pos.max().item()) + 1
+    freqs = torch.outer(torch.arange(max_pos, device=dev, dtype=torch.float32), inv)
+    cos_t = torch.cat([freqs.cos(), freqs.cos()], -1).to(sets[0]["q"].dtype)
+    sin_t = torch.cat([freqs.sin(), freqs.sin()], -1).to(sets[0]["q"].dtype)
+
+    def rotate_half(x):
+        return torch.cat([-x[..., half:], x[..., :half]], -1)
+
+    def eager(i):
+        b = sets[i % nsets]
+        c = cos_t[pos][:, None, :]
+        s = sin_t[pos][:, None, :]
+        return b["q"] * c + rotate_half(b["q"]) * s, b["k"] * c + rotate_half(b["k"]) * s
+
+    def fused(i):
+        b = sets[i % nsets]
+        P.rope_qk_fwd(b["q"], b["k"], cu, w.theta)
+
+    res = {}
+    for name, fn in (("eager_unfused", eager), ("fused", fused)):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(args.steps):
+            fn(i)
+        b_.record()
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(b_) * 1e3 / args.steps
+    log(f"[bench] {w.name}: eager unfused RoPE {res['eager_unfused']:.1f} us, fused in place {res['fused']:.1f} us "
+        f"per forward ({res['eager_unfused'] / res['fused']:.1f}x)")
+    print(json.dumps({"metric": "forward RoPE of q and k: PyTorch eager (unfused) vs the fused kernel", "workload": w.name,
+                      "us_eager_unfused": res["eager_unfused"], "us_fused": res["fused"],
+                      "speedup": res["eager_unfused"] / res["fused"], "steps": args.steps,
+                      "note": "launched one by one (no graph) for both"}))
+
+
 def _timed(fn):
     t0 = time.perf_counter()
     fn()
@@ -458,6 +517,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain copy of --copy-bytes (for HBM counter scaling)")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
+    ap.add_argument("--eager-baseline", action="store_true",
+                    help="only time an unfused PyTorch-eager RoPE beside the fused kernel (context)")
     ap.add_argument("--pack", action="store_true",
                     help="only time the BFD packer and the packed-metadata cache")
     ap.add_argument("--norm", action="store_true",
@@ -482,6 +543,9 @@ def main():
         return
     if args.pack:
         run_pack(args)
+        return
+    if args.eager_baseline:
+        run_eager_baseline(args)
         return
 
     w, r = run_gpu(args)
