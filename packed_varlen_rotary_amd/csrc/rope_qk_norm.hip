@@ -29,11 +29,13 @@
 //    and one set of weight-gradient sums.
 //  * Backward: the rotation by -angle (the table holds -sin), then the RMSNorm
 //    gradient with a second row sum (sum_j g_j x_j).  A fixed number of
-//    workgroups loop over the tiles; each sums the weight gradient of its
-//    rows per lane, then across the lanes of a wave that hold the same chunk,
-//    then across the 4 waves, into float64 sums in LDS that it writes once at
-//    the end; a small kernel adds the workgroups' sums in a fixed tree order,
-//    so the result is deterministic.
+//    workgroups loop over the tiles, with one barrier per tile.  Each lane
+//    keeps the weight-gradient terms of its rows in registers while the
+//    tiles are of one tensor; then they are summed across the lanes of a
+//    wave that hold the same chunk and across the 4 waves, into float64 sums
+//    in LDS that the workgroup writes once at the end; a small kernel adds
+//    the workgroups' sums in a fixed tree order, so the result is
+//    deterministic.
 //  * Everything is evaluated in float64 and rounded once to the storage type.
 
 #include "rope_common.h"
@@ -41,7 +43,7 @@
 namespace {
 
 constexpr int kFwdTasks = 4;          // rows per lane per forward tile
-constexpr int kBwdTasks = 2;          // rows per lane per backward tile (register-bound: ~180 VGPRs)
+constexpr int kBwdTasks = 2;          // rows per lane per backward tile (register-bound: ~230 VGPRs)
 constexpr int64_t kMaxHeads = 65535;  // row -> (token, head) division limit
 constexpr int kWaves = kThreads / 64;
 constexpr int kFwdTableBytes = 32768;  // forward table per workgroup (one entry per element)
@@ -497,11 +499,12 @@ __device__ __forceinline__ void fwd_tile(const NormParams& p, uint32_t tile, int
   tile_compute<kDtype, kIl, false, kTPT>(p, gm, d, s_pos, s_cs, nullptr, nullptr);
 }
 
-// LDS of the norm kernels after the table: weights [2 D] floats, then (backward)
-// the workgroup's weight-gradient sums [2 D], one tile's per-wave sums [4][D]
-// and the frequencies [D / 2], doubles.
-__device__ __forceinline__ float* lds_weights(double2* s_cs, const NormParams& p) {
-  return reinterpret_cast<float*>(reinterpret_cast<char*>(s_cs) + p.table_bytes);
+// LDS of the norm kernels after the table (the forward's one, the backward's
+// two): weights [2 D] floats, then (backward) the workgroup's weight-gradient
+// sums [2 D], the per-wave sums of one flush [4][D] and the frequencies
+// [D / 2], doubles.
+__device__ __forceinline__ float* lds_weights(double2* s_cs, const NormParams& p, int ntables) {
+  return reinterpret_cast<float*>(reinterpret_cast<char*>(s_cs) + ntables * p.table_bytes);
 }
 
 // Both tensors' weights into LDS (a tensor without heads may have none).
@@ -525,29 +528,75 @@ __global__ __launch_bounds__(kThreads) void rope_qk_norm_fwd_kernel(const NormPa
   fwd_tile<kDtype, kIl, kTPT>(p, tile, s_pos, s_cs);
 }
 
-// Backward: gridDim.x workgroups, each taking tiles blockIdx.x, + gridDim.x,
-// ...; the weights and frequencies sit in LDS for all of a workgroup's tiles.
-// (Issuing the next tile's loads before the current tile's work measured no
-// faster: this kernel waits on its lane-exchange and barrier latencies, with
-// two waves per SIMD at its register count, more than on memory.)
-template <int kDtype, bool kIl, int kTPT>
-__global__ __launch_bounds__(kThreads) void rope_qk_norm_bwd_kernel(const NormParams p) {
-  constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;
-  __shared__ int32_t s_pos[kMaxTileTokens];
-  extern __shared__ double2 s_cs[];
-  float* s_w = lds_weights(s_cs, p);
-  double* s_acc = reinterpret_cast<double*>(s_w + 2 * p.D);  // [2 D]
-  double* s_wave = s_acc + 2 * p.D;                          // [kWaves][D]
-  double* s_freq = s_wave + kWaves * p.D;                    // [D / 2]
+// Adds this thread's weight-gradient terms of tensor `sel` into the
+// workgroup's sums: across the lanes of a wave that hold the same chunk, then
+// across the waves (in a fixed order); ends with a barrier.
+template <int kVec>
+__device__ __forceinline__ void flush_dw(const NormParams& p, int sel, const double* acc, double* s_wave,
+                                         double* s_acc) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int L = p.L, D = p.D;
   const int c = tid & (L - 1);
+  double v[kVec];
+#pragma unroll
+  for (int j = 0; j < kVec; ++j) v[j] = acc[j];
+  for (int m = L; m < 64; m <<= 1) {
+    const int addr = (lane ^ m) << 2;
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) v[j] += lane_f64(v[j], addr);
+  }
+  if (lane < L) {
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) s_wave[wave * D + c * kVec + j] = v[j];
+  }
+  __syncthreads();
+  for (int col = tid; col < D; col += kThreads) {
+    double s = s_wave[col];
+#pragma unroll
+    for (int wv = 1; wv < kWaves; ++wv) s += s_wave[wv * D + col];
+    s_acc[sel * D + col] += s;
+  }
+  __syncthreads();
+}
+
+// Backward: gridDim.x workgroups, each taking tiles blockIdx.x, + gridDim.x,
+// ...; the weights and frequencies sit in LDS for all of a workgroup's tiles.
+// Consecutive tiles alternate between two tables, so one barrier per tile
+// (after its table) suffices: a wave that writes table b for tile i has passed
+// tile i - 1's barrier, which every wave reaches only after its tile i - 2
+// work, the last reader of table b.  The weight-gradient terms stay in
+// registers while the tiles are of one tensor (q's tiles come first, so that
+// changes at most once) and are summed across the workgroup only then and at
+// the end.
+template <int kDtype, bool kIl, int kTPT>
+__global__ __launch_bounds__(kThreads) void rope_qk_norm_bwd_kernel(const NormParams p) {
+  constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;
+  __shared__ int32_t s_pos[2][kMaxTileTokens];
+  extern __shared__ double2 s_cs[];
+  const int tab_len = p.table_bytes / static_cast<int>(sizeof(double2));  // entries per table
+  float* s_w = lds_weights(s_cs, p, 2);
+  double* s_acc = reinterpret_cast<double*>(s_w + 2 * p.D);  // [2 D]
+  double* s_wave = s_acc + 2 * p.D;                          // [kWaves][D]
+  double* s_freq = s_wave + kWaves * p.D;                    // [D / 2]
+  const int tid = threadIdx.x;
+  const int D = p.D;
   load_weights(p, s_w);
   for (int i = tid; i < 2 * D; i += kThreads) s_acc[i] = 0.0;
   for (int i = tid; i < p.half; i += kThreads) s_freq[i] = p.inv_freq[i];
   __syncthreads();
+  double acc[kVec];
+#pragma unroll
+  for (int j = 0; j < kVec; ++j) acc[j] = 0.0;
+  int cur = -1;  // the tensor acc belongs to
+  int b = 0;     // this tile's table
   for (uint32_t tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
     const TileGeom gm = tile_geom(p, tile);
+    if (gm.sel != cur) {
+      if (cur >= 0) flush_dw<kVec>(p, cur, acc, s_wave, s_acc);
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) acc[j] = 0.0;
+      cur = gm.sel;
+    }
     TileData<kTPT> d;
     tile_loads<true, kTPT>(p, gm, d);
     __builtin_amdgcn_sched_barrier(0);
@@ -556,30 +605,11 @@ __global__ __launch_bounds__(kThreads) void rope_qk_norm_bwd_kernel(const NormPa
     tile_entries(p, gm, tt_e, i_e);
 #pragma unroll
     for (int v = 0; v < kEnt; ++v) f[v] = s_freq[i_e[v]];
-    tile_table<kDtype, kIl, true>(p, gm, tt_e, i_e, f, nullptr, nullptr, s_pos, s_cs);
-    double acc[kVec];
-#pragma unroll
-    for (int j = 0; j < kVec; ++j) acc[j] = 0.0;
-    tile_compute<kDtype, kIl, true, kTPT>(p, gm, d, s_pos, s_cs, s_w, acc);
-    // lanes holding the same chunk, then the waves, into the workgroup's sums
-    for (int m = L; m < 64; m <<= 1) {
-      const int addr = (lane ^ m) << 2;
-#pragma unroll
-      for (int j = 0; j < kVec; ++j) acc[j] += lane_f64(acc[j], addr);
-    }
-    if (lane < L) {
-#pragma unroll
-      for (int j = 0; j < kVec; ++j) s_wave[wave * D + c * kVec + j] = acc[j];
-    }
-    __syncthreads();
-    for (int col = tid; col < D; col += kThreads) {
-      double s = s_wave[col];
-#pragma unroll
-      for (int wv = 1; wv < kWaves; ++wv) s += s_wave[wv * D + col];
-      s_acc[gm.sel * D + col] += s;
-    }
-    __syncthreads();  // the table, positions and wave sums are rewritten by the next tile
+    tile_table<kDtype, kIl, true>(p, gm, tt_e, i_e, f, nullptr, nullptr, s_pos[b], s_cs + b * tab_len);
+    tile_compute<kDtype, kIl, true, kTPT>(p, gm, d, s_pos[b], s_cs + b * tab_len, s_w, acc);
+    b ^= 1;
   }
+  if (cur >= 0) flush_dw<kVec>(p, cur, acc, s_wave, s_acc);
   double* dst = p.partial + static_cast<int64_t>(blockIdx.x) * 2 * D;
   for (int i = tid; i < 2 * D; i += kThreads) dst[i] = s_acc[i];
 }
@@ -830,7 +860,7 @@ int rope_qk_norm_bwd(const void* dq_out, const void* dk_out, const void* q, cons
     p.ten[0].copy = Hq > 0 && !same_tensor(ts[0], ts[4]);
     p.ten[1].copy = Hkv > 0 && !same_tensor(ts[1], ts[5]);
     p.partial = partial;
-    const size_t lds = static_cast<size_t>(p.table_bytes) + static_cast<size_t>(2 * D) * sizeof(float) +
+    const size_t lds = static_cast<size_t>(2 * p.table_bytes) + static_cast<size_t>(2 * D) * sizeof(float) +
                        static_cast<size_t>((2 + kWaves) * D + D / 2) * sizeof(double);
     void* args[] = {&p};
     const hipError_t err = hipLaunchKernel(pick_bwd(dtype, o.pairing == ROPE_QK_PAIR_INTERLEAVED),
