@@ -200,11 +200,11 @@ __device__ __forceinline__ bool fwd_chunk(const u32x4& own, const u32x4& pr, dou
 // Backward of one chunk, first part: dn = rotation of the incoming gradient
 // by -angle (the table holds -sin; pr is the rotate_half partner chunk,
 // already negated in the first half), g = dn * w; adds sum_j g_j x_j to gx
-// and dn_j x_j r to acc (when `use`).
+// and dn_j x_j r to acc.
 template <int kDtype, bool kIl>
 __device__ __forceinline__ void bwd_chunk_grad(const u32x4& x, const u32x4& dy, const u32x4& pr, double r,
-                                               const float* w_own, const double2* cs, int step, bool use,
-                                               double* gw, double& gx, double* acc) {
+                                               const float* w_own, const double2* cs, int step, double* gw,
+                                               double& gx, double* acc) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const f64x2 xv = element_pair<kDtype>(x, d);
@@ -222,7 +222,7 @@ __device__ __forceinline__ void bwd_chunk_grad(const u32x4& x, const u32x4& dy, 
       }
       gw[d] = dn * static_cast<double>(w_own[d]);
       gx = fma(gw[d], xv.x, gx);
-      acc[d] += use ? dn * xv.x * r : 0.0;
+      acc[d] = fma(dn * xv.x, r, acc[d]);
     } else {
       double dn0, dn1;
       if constexpr (kIl) {
@@ -240,8 +240,8 @@ __device__ __forceinline__ void bwd_chunk_grad(const u32x4& x, const u32x4& dy, 
       gw[2 * d + 1] = dn1 * static_cast<double>(w_own[2 * d + 1]);
       gx = fma(gw[2 * d], xv.x, gx);
       gx = fma(gw[2 * d + 1], xv.y, gx);
-      acc[2 * d] += use ? dn0 * xv.x * r : 0.0;
-      acc[2 * d + 1] += use ? dn1 * xv.y * r : 0.0;
+      acc[2 * d] = fma(dn0 * xv.x, r, acc[2 * d]);
+      acc[2 * d + 1] = fma(dn1 * xv.y, r, acc[2 * d + 1]);
     }
   }
 }
@@ -413,19 +413,26 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
   const int hl = L >> 1;
   const int sel = gm.sel;
   const NormTensor& tn = p.ten[sel];
-  const u32x4* a = d.a;
-  const u32x4* g = d.g;
   const int* tt_of = d.tt_of;
   const bool* act = d.act;
   const int paddr = (lane ^ hl) << 2;  // rotate_half partner lane
   const bool first = c < hl;
+  const bool copy = tn.copy != 0;
   bool st[kTPT], inside[kTPT];
   u32x4 out[kTPT];
   double r[kTPT];
+  // backward: the rows that are in no sequence (or past the tile's end)
+  // enter as zeros, so they add exactly nothing to the weight gradient
+  // whatever they hold; their outputs are not computed from these
+  u32x4 a[kTPT], g[kTPT];
 #pragma unroll
   for (int u = 0; u < kTPT; ++u) {
     inside[u] = s_pos[tt_of[u]] >= 0;
-    st[u] = act[u] && (inside[u] || tn.copy);
+    st[u] = act[u] & (inside[u] | copy);
+    const bool use = !kBwd || (act[u] & inside[u]);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    a[u] = use ? d.a[u] : zero;
+    if constexpr (kBwd) g[u] = use ? d.g[u] : zero;
     r[u] = chunk_squares<kDtype>(a[u]);
   }
   row_sums<kTPT>(r, L, lane);
@@ -456,7 +463,7 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
       u32x4 pr = g[u];
       if constexpr (!kIl) pr = partner_chunk<kDtype>(g[u], paddr, first);
       gx[u] = 0.0;
-      bwd_chunk_grad<kDtype, kIl>(a[u], g[u], pr, r[u], w_own, cs, step, act[u] && inside[u], gw[u], gx[u], acc);
+      bwd_chunk_grad<kDtype, kIl>(a[u], g[u], pr, r[u], w_own, cs, step, gw[u], gx[u], acc);
     }
     row_sums<kTPT>(gx, L, lane);
 #pragma unroll
@@ -464,7 +471,7 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
       const double coef = (r[u] * r[u]) * (gx[u] * p.inv_d);
       u32x4 y;
       if (bwd_chunk_dx<kDtype, false>(a[u], gw[u], r[u], coef, y)) bwd_chunk_dx<kDtype, true>(a[u], gw[u], r[u], coef, y);
-      out[u] = inside[u] ? y : g[u];
+      out[u] = inside[u] ? y : d.g[u];
     }
   }
 #pragma unroll

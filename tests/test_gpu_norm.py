@@ -159,6 +159,43 @@ def test_norm_bwd_out_of_place_and_options(opts):
     run_bwd(700, 8, 2, 128, "bf16", [3, 100, 100, 620, 690], 5e5, seed=91, in_place=False, **opts)
 
 
+def test_norm_nonfinite_rows_outside_sequences():
+    """Rows of tokens outside every sequence may hold anything (say, a
+    gradient buffer that nothing wrote): NaN and infinities there pass through
+    to the outputs bit for bit and change neither the inside rows nor the
+    weight gradients, which match the oracle run on finite stand-ins."""
+    T, Hq, Hkv, D, dt = 300, 6, 2, 128, "bf16"
+    cu = [0, 1, 100, 100, 290]  # tokens 290.. lie outside
+    x = {nm: W.randn((T, H, D), dt, seed=s, device=DEV) for nm, H, s in (("q", Hq, 41), ("k", Hkv, 42))}
+    gy = {nm: W.randn((T, H, D), dt, seed=s, device=DEV) for nm, H, s in (("q", Hq, 43), ("k", Hkv, 44))}
+    bad = torch.tensor([float("nan"), float("inf"), -float("inf"), 1.0], dtype=torch.bfloat16, device=DEV)
+    for tns in list(x.values()) + list(gy.values()):
+        tail = tns[290:]
+        tail.copy_(bad.repeat(tail.numel() // 4 + 1)[: tail.numel()].view_as(tail))
+    wq, wk = weights(D, 45), weights(D, 46)
+    fin = {nm: f64(v) for nm, v in x.items()}
+    fing = {nm: f64(v) for nm, v in gy.items()}
+    for arr in list(fin.values()) + list(fing.values()):
+        arr[290:] = 0.0  # finite stand-ins: the oracle has no cross-token terms
+    yq, yk = torch.empty_like(x["q"]), torch.empty_like(x["k"])
+    P.rope_qk_norm_fwd(x["q"], x["k"], wq, wk, EPS, cu_dev(cu), 1e4, yq, yk)
+    dq, dk, dwq, dwk = P.rope_qk_norm_bwd(gy["q"].clone(), gy["k"].clone(), x["q"], x["k"], wq, wk, EPS,
+                                          cu_dev(cu), 1e4)
+    torch.cuda.synchronize()
+    o = oracle_opts({})
+    for nm, y, dx, dw, w in (("q", yq, dq, dwq, wq), ("k", yk, dk, dwk, wk)):
+        ry, _ = oracle.norm_rope(fin[nm], w64(w), EPS, cu, 1e4, **o)
+        s = check_against(y[:290], ry[:290], f"fwd {nm} inside")
+        assert s["exact_fraction"] == 1.0, s
+        assert torch.equal(y[290:].view(torch.int16), x[nm][290:].view(torch.int16))
+        rdx, rdw = oracle.norm_rope_bwd(fing[nm], fin[nm], w64(w), EPS, cu, 1e4, **o)
+        s = check_against(dx[:290], rdx[:290], f"bwd d{nm} inside")
+        assert s["exact_fraction"] == 1.0, s
+        assert torch.equal(dx[290:].view(torch.int16), gy[nm][290:].view(torch.int16))
+        assert torch.isfinite(dw).all()
+        check_dw(dw, rdw, dw_terms(fing[nm], fin[nm], w64(w), cu, 1e4, o), f"dw{nm} with non-finite outside rows")
+
+
 def test_norm_bwd_is_deterministic():
     T, Hq, Hkv, D = 3000, 16, 4, 128
     q = W.randn((T, Hq, D), "bf16", seed=1, device=DEV)
