@@ -187,6 +187,37 @@ def run_gpu(args):
     wall = time.perf_counter() - w0
     region_ms = t_start.elapsed_time(t_end)
 
+    # the forward and the backward on their own (K launches each, same replay)
+    def split_us(fn):
+        g = None
+        if args.graph:
+            side = torch.cuda.Stream(dev)
+            side.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.stream(side):
+                fn(0)
+            torch.cuda.current_stream(dev).wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(args.steps):
+                    fn(i)
+            g.replay()
+            torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        if g is not None:
+            g.replay()
+        else:
+            for i in range(args.steps):
+                fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / args.steps
+
+    fwd_us = split_us(lambda i: P.rope_qk_fwd(sets[i % nsets]["q"], sets[i % nsets]["k"], cu, w.theta))
+    bwd_us = split_us(lambda i: P.rope_qk_bwd(sets[i % nsets]["dq"], sets[i % nsets]["dk"], cu, w.theta))
+    log(f"[bench] {w.name}: forward {fwd_us:.2f} us, backward {bwd_us:.2f} us per launch")
+
     # parity of a fresh batch in the same run
     parity = check_parity(w, cu, dev)
 
@@ -199,6 +230,8 @@ def run_gpu(args):
         "launch_ms": launch_ms,
         "gbs": w.bytes_per_pass / (launch_ms * 1e-3) / 1e9,
         "traffic": measured_traffic(w.name),
+        "fwd_us": fwd_us,
+        "bwd_us": bwd_us,
         "parity": parity,
         "resident_batches": nsets,
         "device": torch.cuda.get_device_name(dev),
@@ -591,6 +624,8 @@ def main():
             "launches_per_step": 2,
             "algorithmic_bytes_per_launch": w.bytes_per_pass,
             "mean_launch_us": r["launch_ms"] * 1e3,
+            "fwd_launch_us": r["fwd_us"],
+            "bwd_launch_us": r["bwd_us"],
             "event_ms_per_step": r["event_ms_per_step"],
             "launch": "hip graph of the K steps" if args.graph else "stream launches",
         },

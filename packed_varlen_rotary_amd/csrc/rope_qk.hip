@@ -89,11 +89,8 @@ struct RopeParams {
   int32_t half_bytes;      // (D / 2) * element size
   int32_t pos_offset;      // added to the positions of segment 0
   int32_t freq_fp32;       // 1: angles as float32 tables form them (inv_freq already rounded to float32)
-  int32_t chain;           // > 1: each thread fills the table for `chain` consecutive tokens of one pair
-  int32_t lhalf;           // log2(half) when chain > 1
   double sign;             // +1 forward, -1 backward
   double inv_freq[kMaxHalf];
-  double2 step[kMaxHalf];  // chained tables: (cos, sin) of each frequency, from the same float64 sincos
 };
 
 // Rotate one task of 16-bit data: a holds x[i .. i+7], b holds x[i+D/2 .. i+D/2+7].
@@ -243,38 +240,16 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
 
     // 1. inv_freq of this thread's table entries.  Issued before the tile's
     //    data: the memory counter completes in order, so the table can be
-    //    built while the data loads are still in flight.  Chained tables
-    //    (half a power of two): thread tid fills pair tid % half for `chain`
-    //    consecutive tokens; otherwise entry e = tid + v * 256 is token
-    //    e / half, pair e % half.
-    // (not compiled into the interleaved instances, whose registers are at the limit)
-    const bool chained = kG != kInterleaved && p.chain > 1;  // wave-uniform
+    //    built while the data loads are still in flight.
     double f[kEnt];
     int tt_e[kEnt], i_e[kEnt];
-    bool ok_e[kEnt];
-    double2 stp = make_double2(1.0, 0.0);
-    if (chained) {
-      const int i = tid & (p.half - 1);
-      const int tt0 = (tid >> p.lhalf) * p.chain;
-      const double fi = p.inv_freq[i];
-      stp = p.step[i];
 #pragma unroll
-      for (int v = 0; v < kEnt; ++v) {
-        ok_e[v] = v < p.chain && tt0 + v < ntok;
-        tt_e[v] = ok_e[v] ? tt0 + v : 0;
-        i_e[v] = i;
-        f[v] = fi;
-      }
-    } else {
-#pragma unroll
-      for (int v = 0; v < kEnt; ++v) {
-        const int e = tid + v * kThreads;
-        ok_e[v] = e < nent;
-        const int tt = ok_e[v] ? static_cast<int>(div_small(static_cast<uint32_t>(e), p.magic_half)) : 0;
-        tt_e[v] = tt;
-        i_e[v] = ok_e[v] ? e - tt * p.half : 0;
-        f[v] = (v == 0 || v * kThreads < nent) ? p.inv_freq[i_e[v]] : 0.0;
-      }
+    for (int v = 0; v < kEnt; ++v) {
+      const int e = tid + v * kThreads;
+      const int tt = e < nent ? static_cast<int>(div_small(static_cast<uint32_t>(e), p.magic_half)) : 0;
+      tt_e[v] = tt;
+      i_e[v] = e < nent ? e - tt * p.half : 0;
+      f[v] = (v == 0 || v * kThreads < nent) ? p.inv_freq[i_e[v]] : 0.0;
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -341,47 +316,25 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
 #pragma unroll
       for (int v = 0; v < kEnt; ++v) start[v] = cv <= t0 + tt_e[v] ? cv : start[v];
     }
-    // A chained entry whose token follows the previous entry's in the same
-    // sequence is the previous (cos, sin) turned by the exact difference d of
-    // the two float64 angles (Sterbenz: both subtractions below are exact).
-    // d = f + eps with |eps| at most an ulp of the angle (< 2.5e-7 below
-    // position 2^31): cos d = cos f (1 - eps^2/2) - sin f eps and
-    // sin d = sin f (1 - eps^2/2) + cos f eps, up to eps^3 / 6 < 3e-21.  The
-    // entry then matches the directly evaluated sincos of the same rounded
-    // angle to a few float64 ulps.
-    double pc = 1.0, ps = 0.0, pang = 0.0;
-    int32_t ppos = -1;
 #pragma unroll
     for (int v = 0; v < kEnt; ++v) {
-      if (!chained && v > 0 && v * kThreads >= nent) break;
+      if (v > 0 && v * kThreads >= nent) break;
+      const int e = tid + v * kThreads;
       const int64_t t = t0 + tt_e[v];
       const bool inside = start[v] != INT64_MIN && t < cu_last;
       const int64_t pos64 = inside ? t - start[v] + (t < cu_first_end ? p.pos_offset : 0) : -1;
       const int32_t pos = pos64 <= INT32_MAX ? static_cast<int32_t>(pos64) : -1;
-      if (ok_e[v]) {
+      if (e < nent) {
         if (i_e[v] == 0) s_pos[tt_e[v]] = pos;
         if (pos >= 0) {
           double sn, cs;
           // float32 convention: float32 position times float32 frequency, one rounding
           const double ang = p.freq_fp32 ? static_cast<double>(static_cast<float>(pos) * static_cast<float>(f[v]))
                                          : static_cast<double>(pos) * f[v];
-          if (chained && ppos >= 0 && pos == ppos + 1) {
-            const double eps = (ang - pang) - f[v];
-            const double h = fma(-0.5 * eps, eps, 1.0);
-            const double cd = fma(-eps, stp.y, stp.x * h);
-            const double sd = fma(eps, stp.x, stp.y * h);
-            cs = fma(pc, cd, -(ps * sd));
-            sn = fma(ps, cd, pc * sd);
-          } else {
-            rope_sincos(ang, &sn, &cs);
-          }
+          rope_sincos(ang, &sn, &cs);
           s_cs[cs_slot(tt_e[v], i_e[v], kPPC, p.chunks)] = make_double2(cs, p.sign * sn);
-          pc = cs;
-          ps = sn;
-          pang = ang;
         }
       }
-      ppos = ok_e[v] ? pos : -1;
     }
     __syncthreads();
 
@@ -525,24 +478,6 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
   p.freq_fp32 = o.freq_precision == ROPE_QK_FREQ_FP32;
   p.sign = sign;
   fill_inv_freq(theta, r, o, p.inv_freq);
-  // chained tables: half a power of two (each pair owns kThreads / half
-  // threads), float64 angles, rotate_half pairing, and at least two tokens
-  // per thread
-  p.chain = 0;
-  p.lhalf = 0;
-  if ((half & (half - 1)) == 0 && o.freq_precision == ROPE_QK_FREQ_FP64 && !interleaved) {
-    const int64_t groups = kThreads / half;
-    const int64_t per_thread = (span + groups - 1) / groups;
-    if (per_thread >= 2 && per_thread <= kEnt) {
-      p.chain = static_cast<int32_t>(per_thread);
-      while ((int64_t(1) << p.lhalf) < half) ++p.lhalf;
-      for (int64_t i = 0; i < half; ++i) {
-        double s, c;
-        rope_sincos(p.inv_freq[i], &s, &c);
-        p.step[i] = make_double2(c, s);
-      }
-    }
-  }
 
   // LDS: the table of the tokens one tile touches; for pair tiles, padded so
   // that at most the measured best number of workgroups share a compute unit
