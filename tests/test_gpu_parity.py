@@ -294,11 +294,11 @@ def test_side_stream_and_binding_errors():
 
 
 @pytest.mark.parametrize("offset", [0, 2 ** 31 - 1 - 600])
-def test_chained_table_boundaries_and_large_positions(offset):
-    """Few heads at D = 64 and 32: each thread fills the cos/sin table for up to
-    four consecutive tokens by turning the previous entry; sequences of 1 to 5
-    tokens break the chains often; positions up to 2^31 - 2, where an angle's
-    float64 ulp is largest.  Every element exact against the oracle."""
+def test_short_sequences_and_large_positions(offset):
+    """Few heads at D = 64 and 32, so a tile's table spans many tokens;
+    sequences of 1 to 5 tokens put many boundaries inside each tile;
+    positions up to 2^31 - 2, where an angle's float64 ulp is largest.  Every
+    element exact against the oracle."""
     rng = np.random.default_rng(77)
     T = 600
     lengths = np.concatenate([[300], rng.integers(1, 6, size=200)])  # segment 0 carries the offset
