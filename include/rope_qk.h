@@ -272,8 +272,8 @@ int64_t rope_qk_norm_bwd_workspace_bytes(int64_t T, int64_t Hq, int64_t Hkv, int
  *                  dk, each (t, h)
  *
  * Everything else as rope_qk_norm_fwd (same eps, weights, options, theta).
- * Up to three launches on `stream`; with T == 0 or no heads only the weight
- * gradients are written (zeros).
+ * Two launches on `stream` (the rows, then the weight-gradient sums); with
+ * T == 0 or no heads only the second, which writes zero weight gradients.
  */
 int rope_qk_norm_bwd(const void* dq_out, const void* dk_out, const void* q, const void* k, void* dq, void* dk,
                      const float* q_weight, const float* k_weight, double eps, float* dq_weight, float* dk_weight,
