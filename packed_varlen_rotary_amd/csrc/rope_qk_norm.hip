@@ -341,29 +341,58 @@ __device__ __forceinline__ void tile_entries(const NormParams& p, const TileGeom
   }
 }
 
+// Where a tile's first token falls among the sequences: s0 is the last
+// sequence that starts at or before it (-1: none), start0 = cu[s0] and next =
+// cu[s0 + 1] (INT64_MIN / INT64_MAX past the ends).
+struct SeqCursor {
+  int32_t s0;
+  int64_t start0, next;
+};
+
+__device__ __forceinline__ SeqCursor seq_cursor(const NormParams& p, int32_t s0) {
+  const cu_ptr cu = (cu_ptr)p.cu;
+  SeqCursor c;
+  c.s0 = s0;
+  c.start0 = s0 >= 0 ? static_cast<int64_t>(cu[s0]) : INT64_MIN;
+  c.next = s0 < p.nseq ? static_cast<int64_t>(cu[s0 + 1]) : INT64_MAX;
+  return c;
+}
+
+// The cursor moved on to token t0 >= the token it was made for (cu_seqlens
+// non-decreasing): no memory read unless t0 has passed the next start.
+__device__ __forceinline__ void seq_advance(const NormParams& p, SeqCursor& c, int64_t t0) {
+  const cu_ptr cu = (cu_ptr)p.cu;
+  while (c.next <= t0) {
+    ++c.s0;
+    c.start0 = c.next;
+    c.next = c.s0 < p.nseq ? static_cast<int64_t>(cu[c.s0 + 1]) : INT64_MAX;
+  }
+}
+
 // Positions and the table of a tile, from each entry's frequency f (and, for
 // the forward, the weights w1, w2 of the pair's two elements); ends with a
 // barrier.
 template <int kDtype, bool kIl, bool kBwd>
 __device__ __forceinline__ void tile_table(const NormParams& p, const TileGeom& gm, const int* tt_e, const int* i_e,
-                                           const double* f, const float* w1, const float* w2, int32_t* s_pos,
-                                           double2* s_cs) {
+                                           const double* f, const float* w1, const float* w2,
+                                           const SeqCursor& sc, int32_t* s_pos, double2* s_cs) {
   constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;
   constexpr int kPPC = kIl ? kVec / 2 : kVec;
   const int L = p.L, hl = p.L >> 1;
   const cu_ptr cu = (cu_ptr)p.cu;
   const int32_t nseq = p.nseq;
-  const int32_t s0 = last_start_at_or_before(cu, nseq, gm.t0);
   const int64_t cu_last = cu[nseq];
   const int64_t cu_first_end = nseq >= 1 ? static_cast<int64_t>(cu[1]) : INT64_MIN;  // cu[1] exists only then
   int64_t start[kEnt];
 #pragma unroll
-  for (int v = 0; v < kEnt; ++v) start[v] = s0 >= 0 ? static_cast<int64_t>(cu[s0]) : INT64_MIN;
-  for (int32_t j = s0 + 1; j <= nseq; ++j) {
-    const int64_t cv = cu[j];
-    if (cv >= gm.t_end) break;
+  for (int v = 0; v < kEnt; ++v) start[v] = sc.start0;
+  // the sequence starts inside the tile
+  int64_t cv = sc.next;
+  for (int32_t j = sc.s0 + 1; cv < gm.t_end;) {
 #pragma unroll
     for (int v = 0; v < kEnt; ++v) start[v] = cv <= gm.t0 + tt_e[v] ? cv : start[v];
+    ++j;
+    cv = j <= nseq ? static_cast<int64_t>(cu[j]) : INT64_MAX;
   }
 #pragma unroll
   for (int v = 0; v < kEnt; ++v) {
@@ -502,7 +531,8 @@ __device__ __forceinline__ void fwd_tile(const NormParams& p, uint32_t tile, int
   TileData<kTPT> d;
   tile_loads<false, kTPT>(p, gm, d);
   __builtin_amdgcn_sched_barrier(0);
-  tile_table<kDtype, kIl, false>(p, gm, tt_e, i_e, f, w1, w2, s_pos, s_cs);
+  const SeqCursor sc = seq_cursor(p, last_start_at_or_before((cu_ptr)p.cu, p.nseq, gm.t0));
+  tile_table<kDtype, kIl, false>(p, gm, tt_e, i_e, f, w1, w2, sc, s_pos, s_cs);
   tile_compute<kDtype, kIl, false, kTPT>(p, gm, d, s_pos, s_cs, nullptr, nullptr);
 }
 
@@ -566,8 +596,8 @@ __device__ __forceinline__ void flush_dw(const NormParams& p, int sel, const dou
   __syncthreads();
 }
 
-// Backward: gridDim.x workgroups, each taking tiles blockIdx.x, + gridDim.x,
-// ...; the weights and frequencies sit in LDS for all of a workgroup's tiles.
+// Backward: gridDim.x workgroups, each taking a contiguous run of tiles; the
+// weights and frequencies sit in LDS for all of a workgroup's tiles.
 // Consecutive tiles alternate between two tables, so one barrier per tile
 // (after its table) suffices: a wave that writes table b for tile i has passed
 // tile i - 1's barrier, which every wave reaches only after its tile i - 2
@@ -596,9 +626,18 @@ __global__ __launch_bounds__(kThreads) void rope_qk_norm_bwd_kernel(const NormPa
   for (int j = 0; j < kVec; ++j) acc[j] = 0.0;
   int cur = -1;  // the tensor acc belongs to
   int b = 0;     // this tile's table
-  for (uint32_t tile = blockIdx.x; tile < p.ntiles; tile += gridDim.x) {
+  // a contiguous run of tiles per workgroup, so that each tile's first
+  // sequence is found by stepping on from the previous tile's (usually with
+  // no memory read: a search per tile is a chain of dependent reads that the
+  // tile's table, and so its barrier, would wait for)
+  const uint32_t per = p.ntiles / gridDim.x, extra = p.ntiles % gridDim.x;
+  const uint32_t first = blockIdx.x * per + min(blockIdx.x, extra);
+  const uint32_t end = first + per + (blockIdx.x < extra ? 1u : 0u);
+  SeqCursor sc = {-1, INT64_MIN, INT64_MAX};
+  for (uint32_t tile = first; tile < end; ++tile) {
     const TileGeom gm = tile_geom(p, tile);
-    if (gm.sel != cur) {
+    const bool fresh = gm.sel != cur;
+    if (fresh) {
       if (cur >= 0) flush_dw<kVec>(p, cur, acc, s_wave, s_acc);
 #pragma unroll
       for (int j = 0; j < kVec; ++j) acc[j] = 0.0;
@@ -607,12 +646,16 @@ __global__ __launch_bounds__(kThreads) void rope_qk_norm_bwd_kernel(const NormPa
     TileData<kTPT> d;
     tile_loads<true, kTPT>(p, gm, d);
     __builtin_amdgcn_sched_barrier(0);
+    if (fresh)
+      sc = seq_cursor(p, last_start_at_or_before((cu_ptr)p.cu, p.nseq, gm.t0));
+    else
+      seq_advance(p, sc, gm.t0);
     int tt_e[kEnt], i_e[kEnt];
     double f[kEnt];
     tile_entries(p, gm, tt_e, i_e);
 #pragma unroll
     for (int v = 0; v < kEnt; ++v) f[v] = s_freq[i_e[v]];
-    tile_table<kDtype, kIl, true>(p, gm, tt_e, i_e, f, nullptr, nullptr, s_pos[b], s_cs + b * tab_len);
+    tile_table<kDtype, kIl, true>(p, gm, tt_e, i_e, f, nullptr, nullptr, sc, s_pos[b], s_cs + b * tab_len);
     tile_compute<kDtype, kIl, true, kTPT>(p, gm, d, s_pos[b], s_cs + b * tab_len, s_w, acc);
     b ^= 1;
   }

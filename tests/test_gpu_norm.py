@@ -159,6 +159,29 @@ def test_norm_bwd_out_of_place_and_options(opts):
     run_bwd(700, 8, 2, 128, "bf16", [3, 100, 100, 620, 690], 5e5, seed=91, in_place=False, **opts)
 
 
+@pytest.mark.parametrize("shape", [(2000, 6, 2, 128, "bf16"), (1500, 1, 1, 64, "bf16"), (900, 40, 8, 128, "fp16"),
+                                   (1200, 3, 3, 32, "fp32")],
+                         ids=lambda s: f"T{s[0]}_H{s[1]}x{s[2]}_D{s[3]}_{s[4]}")
+def test_norm_many_short_sequences(shape):
+    """Hundreds of sequences of 0 to 7 tokens (empty ones included) after a
+    long first one, then tokens outside: tiles start and end inside
+    sequences, hold several boundaries, and the backward's workgroups step
+    through many boundaries in their runs of tiles.  Forward and backward
+    against the oracle."""
+    T, Hq, Hkv, D, dt = shape
+    rng = np.random.default_rng(T + Hq)
+    lengths = np.concatenate([[137], rng.integers(0, 8, size=T)])
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    cu = cu[cu <= T - 9]  # the last 9+ tokens lie outside
+    q = W.randn((T, Hq, D), dt, seed=T, device=DEV)
+    k = W.randn((T, Hkv, D), dt, seed=T + 1, device=DEV)
+    sq, sk = run_fwd(q, k, weights(D, 1), weights(D, 2), cu, 1e4, True)
+    s = run_bwd(T, Hq, Hkv, D, dt, cu, 1e4, seed=T + 2, in_place=False)
+    if dt != "fp32":
+        for r in (sq, sk, s["q"], s["k"]):
+            assert r["exact_fraction"] == 1.0, r
+
+
 def test_norm_nonfinite_rows_outside_sequences():
     """Rows of tokens outside every sequence may hold anything (say, a
     gradient buffer that nothing wrote): NaN and infinities there pass through
