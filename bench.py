@@ -42,8 +42,10 @@ sys.path.insert(0, ROOT)
 METRIC = "fused QK-RoPE fwd+bwd tokens/s and achieved HBM GB/s (% of MI355X peak)"
 HBM_PEAK_GBS = 8000.0
 # the sources the rotation kernels are compiled from
+# the rotation kernels' sources and the build script that holds their compile flags
 KERNEL_SRCS = [os.path.join(ROOT, "packed_varlen_rotary_amd", "csrc", n)
-               for n in ("rope_qk.hip", "rope_common.h", "rope_sincos.h")]
+               for n in ("rope_qk.hip", "rope_common.h", "rope_sincos.h")] + \
+              [os.path.join(ROOT, "packed_varlen_rotary_amd", "build.py")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rope_qk_kernel_traffic.md")
 
 
@@ -52,7 +54,7 @@ def log(*a):
 
 
 def kernel_sha() -> str:
-    """SHA-256 over the rotation kernels' sources, in a fixed order."""
+    """SHA-256 over the rotation kernels' sources and build script, in a fixed order."""
     h = hashlib.sha256()
     for path in KERNEL_SRCS:
         with open(path, "rb") as f:

@@ -28,6 +28,11 @@ FLAGS = [
     "-Wall",
     # no packed-fp32 VALU instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the SLP vectorizer packs the per-element rounding-tie flags of a chunk
+    # into a bit vector and reduces it with 16-bit vector ops; without it they
+    # stay lane masks OR-ed on the scalar unit (8% fewer vector instructions
+    # in the default workload's kernel, which runs ~5% faster)
+    "-fno-slp-vectorize",
 ]
 
 
