@@ -29,6 +29,20 @@
 #define ROPE_HD static inline
 #endif
 
+// a * b + c for a constant c.  On the GPU c is taken from scalar registers
+// by a three-operand FMA: the compiler's own choice, the two-operand form,
+// needs c in the destination and so copies every constant into vector
+// registers first (two moves per coefficient).  A plain fma on the host.
+ROPE_HD double rope_fma_k(double a, double b, double c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  double d;
+  __asm__("v_fma_f64 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "s"(c));
+  return d;
+#else
+  return fma(a, b, c);
+#endif
+}
+
 ROPE_HD void rope_sincos(double x, double* s_out, double* c_out) {
   const double kTwoOverPi = 0x1.45f306dc9c883p-1;
   const double kP1 = 0x1.921fb00000000p+0;   // pi/2, leading 21 bits
@@ -41,26 +55,26 @@ ROPE_HD void rope_sincos(double x, double* s_out, double* c_out) {
   const double z = r * r;
   // sin r = r (1 - z/3! + z^2/5! - ... - z^9/19!)
   double ps = -0x1.2f49b46814157p-57;             // -1/19!
-  ps = fma(ps, z, 0x1.952c77030ad4ap-49);         // +1/17!
-  ps = fma(ps, z, -0x1.ae7f3e733b81fp-41);        // -1/15!
-  ps = fma(ps, z, 0x1.6124613a86d09p-33);         // +1/13!
-  ps = fma(ps, z, -0x1.ae64567f544e4p-26);        // -1/11!
-  ps = fma(ps, z, 0x1.71de3a556c734p-19);         // +1/9!
-  ps = fma(ps, z, -0x1.a01a01a01a01ap-13);        // -1/7!
-  ps = fma(ps, z, 0x1.1111111111111p-7);          // +1/5!
-  ps = fma(ps, z, -0x1.5555555555555p-3);         // -1/3!
+  ps = rope_fma_k(ps, z, 0x1.952c77030ad4ap-49);         // +1/17!
+  ps = rope_fma_k(ps, z, -0x1.ae7f3e733b81fp-41);        // -1/15!
+  ps = rope_fma_k(ps, z, 0x1.6124613a86d09p-33);         // +1/13!
+  ps = rope_fma_k(ps, z, -0x1.ae64567f544e4p-26);        // -1/11!
+  ps = rope_fma_k(ps, z, 0x1.71de3a556c734p-19);         // +1/9!
+  ps = rope_fma_k(ps, z, -0x1.a01a01a01a01ap-13);        // -1/7!
+  ps = rope_fma_k(ps, z, 0x1.1111111111111p-7);          // +1/5!
+  ps = rope_fma_k(ps, z, -0x1.5555555555555p-3);         // -1/3!
   const double sr = fma(ps * z, r, r);
   // cos r = 1 - z/2! + z^2/4! - ... + z^10/20!
   double pc = 0x1.e542ba4020225p-62;              // +1/20!
-  pc = fma(pc, z, -0x1.6827863b97d97p-53);        // -1/18!
-  pc = fma(pc, z, 0x1.ae7f3e733b81fp-45);         // +1/16!
-  pc = fma(pc, z, -0x1.93974a8c07c9dp-37);        // -1/14!
-  pc = fma(pc, z, 0x1.1eed8eff8d898p-29);         // +1/12!
-  pc = fma(pc, z, -0x1.27e4fb7789f5cp-22);        // -1/10!
-  pc = fma(pc, z, 0x1.a01a01a01a01ap-16);         // +1/8!
-  pc = fma(pc, z, -0x1.6c16c16c16c17p-10);        // -1/6!
-  pc = fma(pc, z, 0x1.5555555555555p-5);          // +1/4!
-  pc = fma(pc, z, -0.5);                          // -1/2!
+  pc = rope_fma_k(pc, z, -0x1.6827863b97d97p-53);        // -1/18!
+  pc = rope_fma_k(pc, z, 0x1.ae7f3e733b81fp-45);         // +1/16!
+  pc = rope_fma_k(pc, z, -0x1.93974a8c07c9dp-37);        // -1/14!
+  pc = rope_fma_k(pc, z, 0x1.1eed8eff8d898p-29);         // +1/12!
+  pc = rope_fma_k(pc, z, -0x1.27e4fb7789f5cp-22);        // -1/10!
+  pc = rope_fma_k(pc, z, 0x1.a01a01a01a01ap-16);         // +1/8!
+  pc = rope_fma_k(pc, z, -0x1.6c16c16c16c17p-10);        // -1/6!
+  pc = rope_fma_k(pc, z, 0x1.5555555555555p-5);          // +1/4!
+  pc = rope_fma_k(pc, z, -0.5);                          // -1/2!
   const double cr = fma(pc, z, 1.0);
   // x = k pi/2 + r: rotate (cos r, sin r) by the quadrant k mod 4
   const int q = (int)((long long)k & 3);
