@@ -29,7 +29,8 @@
 //    and one set of weight-gradient sums.
 //  * Backward: the rotation by -angle (the table holds -sin), then the RMSNorm
 //    gradient with a second row sum (sum_j g_j x_j).  A fixed number of
-//    workgroups loop over the tiles, with one barrier per tile.  Each lane
+//    workgroups each take a contiguous run of tiles, carrying a cursor into
+//    cu_seqlens from tile to tile, with one barrier per tile.  Each lane
 //    keeps the weight-gradient terms of its rows in registers while the
 //    tiles are of one tensor; then they are summed across the lanes of a
 //    wave that hold the same chunk and across the 4 waves, into float64 sums
