@@ -65,6 +65,7 @@ struct NormTensor {
   int32_t tile_rows;     // rows per tile
   uint32_t ntiles;
   int32_t copy;          // 1: tokens outside every sequence are copied to a separate output
+  int32_t lin;           // 1: x, g and o are token-major (stride_t = H * stride_h), so row n sits at n * stride_h
 };
 
 struct NormParams {
@@ -313,6 +314,24 @@ __device__ __forceinline__ void tile_loads(const NormParams& p, const TileGeom& 
   const int32_t H = tn.H;
   const int rows_per_step = kThreads >> p.lshift;
   const int64_t off = static_cast<int64_t>(tid & (p.L - 1)) * 16;
+  if (tn.lin) {
+    // token-major rows: row n0 + lr at (n0 + lr) * stride_h, the tile's part
+    // of it once per tile
+    const gchar* xb = (const gchar*)tn.x + gm.n0 * tn.x_sh + off;
+    const gchar* gb = kBwd ? (const gchar*)tn.g + gm.n0 * tn.g_sh + off : nullptr;
+    gchar* ob = (gchar*)tn.o + gm.n0 * tn.o_sh + off;
+#pragma unroll
+    for (int u = 0; u < kTPT; ++u) {
+      const int lr = u * rows_per_step + (tid >> p.lshift);
+      d.act[u] = gm.n0 + lr < gm.n_end;
+      const int64_t r = d.act[u] ? lr : 0;
+      d.a[u] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4*>(xb + r * tn.x_sh));
+      if constexpr (kBwd) d.g[u] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4*>(gb + r * tn.g_sh));
+      d.optr[u] = ob + r * tn.o_sh;
+      d.tt_of[u] = static_cast<int>(div_tok(gm.r0 + static_cast<uint32_t>(r), tn.magic_heads));
+    }
+    return;
+  }
 #pragma unroll
   for (int u = 0; u < kTPT; ++u) {
     const int lr = u * rows_per_step + (tid >> p.lshift);
@@ -813,6 +832,8 @@ void set_tensor(NormTensor* tn, const void* x, const Tensor& tx, const void* gr,
   tn->o = static_cast<char*>(o);
   tn->o_st = to.st * esz;
   tn->o_sh = to.sh * esz;
+  const int64_t H = tn->H;
+  tn->lin = tx.st == H * tx.sh && (tg == nullptr || tg->st == H * tg->sh) && to.st == H * to.sh;
 }
 
 bool same_tensor(const Tensor& a, const Tensor& b) { return a.base == b.base && a.st == b.st && a.sh == b.sh; }

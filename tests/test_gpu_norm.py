@@ -182,6 +182,46 @@ def test_norm_many_short_sequences(shape):
             assert r["exact_fraction"] == 1.0, r
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_norm_strided_views(dt):
+    """q and k as views into fused QKV buffers (token stride (Hq + 2 Hkv) D,
+    so rows are not evenly spaced), outputs and gradients both contiguous and
+    strided: the general (token, head) addressing, against the oracle."""
+    T, Hq, Hkv, D = 400, 6, 2, 128
+    cu = [0, 3, 150, 150, 391]
+    W3 = Hq + 2 * Hkv
+    qkv = W.randn((T, W3, D), dt, seed=51, device=DEV)
+    gqkv = W.randn((T, W3, D), dt, seed=52, device=DEV)
+    q, k = qkv[:, :Hq], qkv[:, Hq:Hq + Hkv]
+    gq, gk = gqkv[:, :Hq], gqkv[:, Hq:Hq + Hkv]
+    assert q.stride(0) == W3 * D and not q.is_contiguous()
+    wq, wk = weights(D, 53), weights(D, 54)
+    o = oracle_opts({})
+    # forward: strided in, contiguous out; then contiguous in, strided out
+    yq, yk = torch.empty(T, Hq, D, dtype=q.dtype, device=DEV), torch.empty(T, Hkv, D, dtype=q.dtype, device=DEV)
+    P.rope_qk_norm_fwd(q, k, wq, wk, EPS, cu_dev(cu), 1e4, yq, yk)
+    out = torch.zeros_like(qkv)
+    P.rope_qk_norm_fwd(q.contiguous(), k.contiguous(), wq, wk, EPS, cu_dev(cu), 1e4, out[:, :Hq],
+                       out[:, Hq:Hq + Hkv])
+    torch.cuda.synchronize()
+    for got, x, w in ((yq, q, wq), (yk, k, wk), (out[:, :Hq], q, wq), (out[:, Hq:Hq + Hkv], k, wk)):
+        ry, _ = oracle.norm_rope(f64(x), w64(w), EPS, cu, 1e4, **o)
+        s = check_against(got, ry, "strided fwd")
+        if dt != "fp32":
+            assert s["exact_fraction"] == 1.0, s
+    # backward: strided dy and x, contiguous dx
+    dq, dk, dwq, dwk = P.rope_qk_norm_bwd(gq, gk, q, k, wq, wk, EPS, cu_dev(cu), 1e4,
+                                          torch.empty(T, Hq, D, dtype=q.dtype, device=DEV),
+                                          torch.empty(T, Hkv, D, dtype=q.dtype, device=DEV))
+    torch.cuda.synchronize()
+    for dx, dw, x, g, w in ((dq, dwq, q, gq, wq), (dk, dwk, k, gk, wk)):
+        rdx, rdw = oracle.norm_rope_bwd(f64(g), f64(x), w64(w), EPS, cu, 1e4, **o)
+        s = check_against(dx, rdx, "strided bwd")
+        if dt != "fp32":
+            assert s["exact_fraction"] == 1.0, s
+        check_dw(dw, rdw, dw_terms(f64(g), f64(x), w64(w), cu, 1e4, o), "strided dw")
+
+
 def test_norm_nonfinite_rows_outside_sequences():
     """Rows of tokens outside every sequence may hold anything (say, a
     gradient buffer that nothing wrote): NaN and infinities there pass through
