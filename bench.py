@@ -28,6 +28,7 @@ Workloads: 1 tiny fp32, 2 Qwen2.5-0.5B-shaped (default), 3 Qwen3-8B-shaped,
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import concurrent.futures as cf
 import hashlib
 import json
@@ -545,6 +546,71 @@ def run_eager_baseline(args):
                       "note": "launched one by one (no graph) for both"}))
 
 
+def run_variants(args):
+    """The rotation's options on one workload, forward only: each case timed
+    as a graph of K launches over resident batches (HIP events around the
+    replay).  Algorithmic bytes: read + write of the rotated elements (all of
+    each head, or the leading rotary_dim of it)."""
+    import torch
+
+    import packed_varlen_rotary_amd as P
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    w = W.make_workload(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    cu = torch.as_tensor(w.cu_seqlens, device=dev)
+    llama3 = dict(factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0, original_max_position=8192.0)
+    cases = [
+        ("plain", {}, w.dtype),
+        ("pos_offset=100000", dict(pos_offset=100000), w.dtype),
+        (f"rotary_dim={w.D // 2}", dict(rotary_dim=w.D // 2), w.dtype),
+        ("interleaved", dict(interleaved=True), w.dtype),
+        ("llama3", dict(llama3=llama3), w.dtype),
+        ("freq_fp32", dict(freq_fp32=True), w.dtype),
+        ("fp16", {}, "fp16"),
+        ("interleaved+llama3+freq_fp32+pos_offset", dict(interleaved=True, llama3=llama3, freq_fp32=True,
+                                                         pos_offset=77), w.dtype),
+    ]
+    res = []
+    for name, opts, dt in cases:
+        wd = dataclasses.replace(w, dtype=dt)
+        nsets = max(1, min(16, -(-(1 << 30) // wd.bytes_per_pass)))
+        sets = [W.make_tensors(wd, ("q", "k"), device=dev, salt=s) for s in range(nsets)]
+
+        def fwd(i):
+            b = sets[i % nsets]
+            P.rope_qk_fwd(b["q"], b["k"], cu, w.theta, **opts)
+
+        for i in range(args.warmup):
+            fwd(i)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(args.steps):
+                fwd(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        graph.replay()
+        b_.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b_) * 1e3 / args.steps
+        r = opts.get("rotary_dim", 0) or w.D
+        nbytes = wd.bytes_per_pass * r // w.D
+        gbs = nbytes / (us * 1e-6) / 1e9
+        log(f"[bench] {w.name} {name} ({dt}): {us:.2f} us, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
+        res.append({"case": name, "dtype": dt, "us_per_launch": us, "algorithmic_bytes": nbytes, "GB/s": gbs,
+                    "frac": gbs / HBM_PEAK_GBS})
+        del sets, graph
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "rope_qk_fwd with each option, per launch", "workload": w.name, "steps": args.steps,
+                      "peak": HBM_PEAK_GBS, "cases": res}))
+
+
 def _timed(fn):
     t0 = time.perf_counter()
     fn()
@@ -566,6 +632,8 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     ap.add_argument("--eager-baseline", action="store_true",
                     help="only time an unfused PyTorch-eager RoPE beside the fused kernel (context)")
+    ap.add_argument("--variants", action="store_true",
+                    help="only time the rotation's options (forward) on the workload")
     ap.add_argument("--pack", action="store_true",
                     help="only time the BFD packer and the packed-metadata cache")
     ap.add_argument("--norm", action="store_true",
@@ -593,6 +661,9 @@ def main():
         return
     if args.eager_baseline:
         run_eager_baseline(args)
+        return
+    if args.variants:
+        run_variants(args)
         return
 
     w, r = run_gpu(args)

@@ -24,7 +24,6 @@ constexpr int kMaxTableBytes = 16384;                 // cos/sin table per workg
 constexpr int kEnt = kMaxTableBytes / 16 / kThreads;  // table entries per thread, at most
 constexpr int64_t kGridX = 65536;                     // tiles per grid row
 constexpr int64_t kLdsPerCu = 163840;                 // MI355X: 160 KiB of LDS per compute unit
-constexpr uint32_t kF16MinNormalBits = 0x38800000u;  // fp32 bit pattern of 2^-14, the smallest normal fp16
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -98,10 +97,12 @@ __device__ __forceinline__ f64x2 unpack16(uint32_t w) {
 
 // Is an fp32 value one that the fp32 -> fp16 step may round differently from
 // a direct float64 -> fp16 rounding?  Midpoints of the fp16 grid in its normal
-// range (low 13 of 24 significant bits 1 followed by zeros), and every nonzero
-// value below 2^-14, where the grid of fp16 subnormals is coarser.
-__device__ __forceinline__ bool fp16_hard(uint32_t b) {
-  return (b & 0x1FFFu) == 0x1000u || (b & 0x7FFFFFFFu) - 1u < kF16MinNormalBits - 1u;
+// range (low 13 of 24 significant bits 1 followed by zeros), and every value
+// of magnitude below 2^-14, where the grid of fp16 subnormals is coarser
+// (zero included: it only sends an exact value down the exact path too).
+// The magnitude test is one float compare with an absolute-value operand.
+__device__ __forceinline__ bool fp16_hard(float f) {
+  return (__float_as_uint(f) & 0x1FFFu) == 0x1000u || fabsf(f) < 0x1p-14f;
 }
 
 // Fast rounding of two float64 values to a packed 16-bit pair: round each to
@@ -117,8 +118,8 @@ __device__ __forceinline__ uint32_t pack16_fast(double lo, double hi, bool& tie)
     tie |= (__float_as_uint(f.y) & 0xFFFFu) == 0x8000u;
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
   } else {
-    tie |= fp16_hard(__float_as_uint(f.x));
-    tie |= fp16_hard(__float_as_uint(f.y));
+    tie |= fp16_hard(f.x);
+    tie |= fp16_hard(f.y);
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
   }
 }
