@@ -44,11 +44,19 @@
 namespace {
 
 constexpr int kFwdTasks = 4;          // rows per lane per forward tile
-constexpr int kBwdTasks = 2;          // rows per lane per backward tile (register-bound: ~230 VGPRs)
+constexpr int kBwdTasks = 2;          // rows per lane per backward tile (register-bound)
 constexpr int64_t kMaxHeads = 65535;  // row -> (token, head) division limit
 constexpr int kWaves = kThreads / 64;
 constexpr int kFwdTableBytes = 32768;  // forward table per workgroup (one entry per element)
-constexpr int64_t kBwdGroups = 1024;  // backward workgroups (4 per compute unit), each looping over tiles
+// Backward workgroups, each looping over a contiguous run of tiles: four
+// times as many as the 256 compute units hold at once (3 per unit at the
+// 16-bit kernels' 168 VGPRs, 4 for float32).  Units that run ahead then take
+// more of the runs; with one run per resident slot the slowest unit sets the
+// end (MI355X, Qwen3-8B and Qwen3-32B shapes: 3072 workgroups 3-8% faster
+// than 768, level from 1536 to 6144).
+constexpr int kBwdWaves16 = 3;
+constexpr int64_t kBwdGroups16 = 4 * 256 * kBwdWaves16;
+constexpr int64_t kBwdGroups32 = 4 * 256 * 4;
 
 // One of the two tensors (q, k) of a call.
 struct NormTensor {
@@ -199,68 +207,79 @@ __device__ __forceinline__ bool fwd_chunk(const u32x4& own, const u32x4& pr, dou
   return tie;
 }
 
-// Backward of one chunk, first part: dn = rotation of the incoming gradient
-// by -angle (the table holds -sin; pr is the rotate_half partner chunk,
-// already negated in the first half), g = dn * w; adds sum_j g_j x_j to gx
-// and dn_j x_j r to acc.
+// The incoming gradient of one chunk rotated by -angle (the table holds
+// -sin; pr is the rotate_half partner chunk, already negated in the first
+// half): dn[j] for the chunk's elements j.
 template <int kDtype, bool kIl>
-__device__ __forceinline__ void bwd_chunk_grad(const u32x4& x, const u32x4& dy, const u32x4& pr, double r,
-                                               const float* w_own, const double2* cs, int step, double* gw,
-                                               double& gx, double* acc) {
+__device__ __forceinline__ void bwd_chunk_dn(const u32x4& dy, const u32x4& pr, const double2* cs, int step,
+                                             double* dn) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
-    const f64x2 xv = element_pair<kDtype>(x, d);
     const f64x2 dv = element_pair<kDtype>(dy, d);
     if constexpr (kDtype == ROPE_QK_FP32) {
-      double dn;
       if constexpr (kIl) {
         const f64x2 dz = element_pair<kDtype>(dy, d ^ 1);
         const double2 c = cs[(d >> 1) * step];
-        dn = (d & 1) ? fma(dv.x, c.x, dz.x * c.y) : fma(dv.x, c.x, -(dz.x * c.y));
+        dn[d] = (d & 1) ? fma(dv.x, c.x, dz.x * c.y) : fma(dv.x, c.x, -(dz.x * c.y));
       } else {
         const f64x2 pv = element_pair<kDtype>(pr, d);
         const double2 c = cs[d * step];
-        dn = fma(dv.x, c.x, pv.x * c.y);
+        dn[d] = fma(dv.x, c.x, pv.x * c.y);
       }
-      gw[d] = dn * static_cast<double>(w_own[d]);
-      gx = fma(gw[d], xv.x, gx);
-      acc[d] = fma(dn * xv.x, r, acc[d]);
     } else {
-      double dn0, dn1;
       if constexpr (kIl) {
         const double2 c = cs[d * step];
-        dn0 = fma(dv.x, c.x, -(dv.y * c.y));
-        dn1 = fma(dv.y, c.x, dv.x * c.y);
+        dn[2 * d] = fma(dv.x, c.x, -(dv.y * c.y));
+        dn[2 * d + 1] = fma(dv.y, c.x, dv.x * c.y);
       } else {
         const f64x2 pv = element_pair<kDtype>(pr, d);
         const double2 c0 = cs[(2 * d) * step];
         const double2 c1 = cs[(2 * d + 1) * step];
-        dn0 = fma(dv.x, c0.x, pv.x * c0.y);
-        dn1 = fma(dv.y, c1.x, pv.y * c1.y);
+        dn[2 * d] = fma(dv.x, c0.x, pv.x * c0.y);
+        dn[2 * d + 1] = fma(dv.y, c1.x, pv.y * c1.y);
       }
-      gw[2 * d] = dn0 * static_cast<double>(w_own[2 * d]);
-      gw[2 * d + 1] = dn1 * static_cast<double>(w_own[2 * d + 1]);
-      gx = fma(gw[2 * d], xv.x, gx);
-      gx = fma(gw[2 * d + 1], xv.y, gx);
-      acc[2 * d] = fma(dn0 * xv.x, r, acc[2 * d]);
-      acc[2 * d + 1] = fma(dn1 * xv.y, r, acc[2 * d + 1]);
     }
   }
 }
 
-// Backward of one chunk, second part: dx_j = r (g_j - x_j coef), rounded.
+// Backward of one chunk, first part: sum_j g_j x_j over its elements, with
+// g = dn * w.
+template <int kDtype>
+__device__ __forceinline__ double bwd_chunk_gx(const u32x4& x, const double* dn, const float* w_own) {
+  double gx = 0.0;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const f64x2 xv = element_pair<kDtype>(x, d);
+    if constexpr (kDtype == ROPE_QK_FP32) {
+      gx = fma(dn[d] * static_cast<double>(w_own[d]), xv.x, gx);
+    } else {
+      gx = fma(dn[2 * d] * static_cast<double>(w_own[2 * d]), xv.x, gx);
+      gx = fma(dn[2 * d + 1] * static_cast<double>(w_own[2 * d + 1]), xv.y, gx);
+    }
+  }
+  return gx;
+}
+
+// Backward of one chunk, second part: dx_j = r (g_j - x_j coef), rounded,
+// and (when acc is given) dn_j x_j r added to acc.
 template <int kDtype, bool kExact>
-__device__ __forceinline__ bool bwd_chunk_dx(const u32x4& x, const double* gw, double r, double coef, u32x4& out) {
+__device__ __forceinline__ bool bwd_chunk_dx(const u32x4& x, const double* dn, const float* w_own, double r,
+                                             double coef, double* acc, u32x4& out) {
   bool tie = false;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const f64x2 xv = element_pair<kDtype>(x, d);
     if constexpr (kDtype == ROPE_QK_FP32) {
-      out[d] = __float_as_uint(static_cast<float>(r * (gw[d] - xv.x * coef)));
+      out[d] = __float_as_uint(static_cast<float>(r * (dn[d] * static_cast<double>(w_own[d]) - xv.x * coef)));
+      if (acc) acc[d] = fma(dn[d] * xv.x, r, acc[d]);
     } else {
-      const double y0 = r * (gw[2 * d] - xv.x * coef);
-      const double y1 = r * (gw[2 * d + 1] - xv.y * coef);
+      const double y0 = r * (dn[2 * d] * static_cast<double>(w_own[2 * d]) - xv.x * coef);
+      const double y1 = r * (dn[2 * d + 1] * static_cast<double>(w_own[2 * d + 1]) - xv.y * coef);
       out[d] = kExact ? pack16_exact<kDtype>(y0, y1) : pack16_fast<kDtype>(y0, y1, tie);
+      if (acc) {
+        acc[2 * d] = fma(dn[2 * d] * xv.x, r, acc[2 * d]);
+        acc[2 * d + 1] = fma(dn[2 * d + 1] * xv.y, r, acc[2 * d + 1]);
+      }
     }
   }
   return tie;
@@ -503,23 +522,31 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
   } else {
     const float* w_own = s_w + sel * p.D + c * kVec;
     const int step = kIl ? L : hl;
-    double gw[kTPT][kVec];
+    // dn stays in registers from the first pass to the second; the
+    // weight-gradient terms are added in the second, where x is unpacked
+    // again anyway (in the first they kept x's float64 values live longer:
+    // 185 against 168 VGPRs, 2 against 3 waves per SIMD)
     double gx[kTPT];
+    double dn[kTPT][kVec];
 #pragma unroll
     for (int u = 0; u < kTPT; ++u) {
+      __builtin_amdgcn_sched_barrier(0);
       const int tt = tt_of[u];
       const double2* cs = kIl ? s_cs + tt * kPPC * L + c : s_cs + tt * kPPC * hl + (c & (hl - 1));
       u32x4 pr = g[u];
       if constexpr (!kIl) pr = partner_chunk<kDtype>(g[u], paddr, first);
-      gx[u] = 0.0;
-      bwd_chunk_grad<kDtype, kIl>(a[u], g[u], pr, r[u], w_own, cs, step, gw[u], gx[u], acc);
+      bwd_chunk_dn<kDtype, kIl>(g[u], pr, cs, step, dn[u]);
+      gx[u] = bwd_chunk_gx<kDtype>(a[u], dn[u], w_own);
     }
+    __builtin_amdgcn_sched_barrier(0);
     row_sums<kTPT>(gx, L, lane);
 #pragma unroll
     for (int u = 0; u < kTPT; ++u) {
+      __builtin_amdgcn_sched_barrier(0);
       const double coef = (r[u] * r[u]) * (gx[u] * p.inv_d);
       u32x4 y;
-      if (bwd_chunk_dx<kDtype, false>(a[u], gw[u], r[u], coef, y)) bwd_chunk_dx<kDtype, true>(a[u], gw[u], r[u], coef, y);
+      if (bwd_chunk_dx<kDtype, false>(a[u], dn[u], w_own, r[u], coef, acc, y))
+        bwd_chunk_dx<kDtype, true>(a[u], dn[u], w_own, r[u], coef, nullptr, y);
       out[u] = inside[u] ? y : d.g[u];
     }
   }
@@ -626,7 +653,8 @@ __device__ __forceinline__ void flush_dw(const NormParams& p, int sel, const dou
 // changes at most once) and are summed across the workgroup only then and at
 // the end.
 template <int kDtype, bool kIl, int kTPT>
-__global__ __launch_bounds__(kThreads) void rope_qk_norm_bwd_kernel(const NormParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBwdWaves16)))
+void rope_qk_norm_bwd_kernel(const NormParams p) {
   constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;
   __shared__ int32_t s_pos[2][kMaxTileTokens];
   extern __shared__ double2 s_cs[];
@@ -754,7 +782,8 @@ int norm_geometry(int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int dtype, bool
   g->table_bytes = g->span * per_token;
   const int64_t total = g->ntiles[0] + g->ntiles[1];
   if (total > INT32_MAX) return ROPE_QK_ERR_SHAPE;
-  g->groups = total < kBwdGroups ? total : kBwdGroups;
+  const int64_t groups = dtype == ROPE_QK_FP32 ? kBwdGroups32 : kBwdGroups16;
+  g->groups = total < groups ? total : groups;
   return ROPE_QK_OK;
 }
 

@@ -283,9 +283,11 @@ def test_norm_bwd_error_codes_and_workspace_size():
     assert lib.rope_qk_norm_bwd_workspace_bytes(256, 14, 2, 64, 9) == C["ROPE_QK_ERR_DTYPE"]
     assert lib.rope_qk_norm_bwd_workspace_bytes(256, 14, 2, 96, 1) == C["ROPE_QK_ERR_SHAPE"]
     assert lib.rope_qk_norm_bwd_workspace_bytes(0, 14, 2, 64, 1) == 0
-    # Qwen3-8B-shaped batch: 16 bytes per column for each of 1024 workgroups
+    # Qwen3-8B-shaped batch: 16 bytes per column for each workgroup, 3072 for
+    # 16-bit storage (4 x 3 per compute unit), 4096 for float32 (4 x 4)
     big = lib.rope_qk_norm_bwd_workspace_bytes(65536, 32, 8, 128, 1)
-    assert big == 1024 * 2 * 128 * 8
+    assert big == 3072 * 2 * 128 * 8
+    assert lib.rope_qk_norm_bwd_workspace_bytes(65536, 32, 8, 128, 0) == 4096 * 2 * 128 * 8
     assert norm_bwd(ws=0) == C["ROPE_QK_ERR_WORKSPACE"]
     assert norm_bwd(ws_size=need - 16) == C["ROPE_QK_ERR_WORKSPACE"]
     assert norm_bwd(ws=WS + 8) == C["ROPE_QK_ERR_ALIGN"]

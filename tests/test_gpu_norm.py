@@ -182,6 +182,21 @@ def test_norm_many_short_sequences(shape):
             assert r["exact_fraction"] == 1.0, r
 
 
+def test_norm_bwd_long_runs_of_tiles():
+    """Enough tiles (12,667) that each backward workgroup takes a run of about
+    four, over thousands of sequences of 0 to 7 tokens: the cursor into
+    cu_seqlens steps across many boundaries inside a run and from tile to
+    tile, and one run crosses from q's tiles to k's.  dx bit-exact, dw to the
+    oracle's sums."""
+    T, Hq, Hkv, D = 40000, 8, 2, 128
+    rng = np.random.default_rng(4242)
+    lengths = np.concatenate([[137], rng.integers(0, 8, size=T)])
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    cu = cu[cu <= T - 9]
+    s = run_bwd(T, Hq, Hkv, D, "bf16", cu, 1e4, seed=4243, in_place=True)
+    assert s["q"]["exact_fraction"] == 1.0 and s["k"]["exact_fraction"] == 1.0, s
+
+
 @pytest.mark.parametrize("dt", ["bf16", "fp32"])
 def test_norm_strided_views(dt):
     """q and k as views into fused QKV buffers (token stride (Hq + 2 Hkv) D,
