@@ -105,13 +105,14 @@ __device__ __forceinline__ double lane_f64(double v, int addr) {
   return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// 1 / sqrt(a) for finite a > 0: the hardware estimate refined by three
-// Newton steps y <- y + y (1 - a y^2) / 2 (each roughly squares the
-// relative error), which leaves an error of about one float64 ulp.
+// 1 / sqrt(a) for finite a > 0: the hardware estimate (relative error below
+// 2^-23) refined by two Newton steps y <- y + y (1 - a y^2) / 2; the first
+// leaves about 1.5 * 2^-46, the second ends at the float64 rounding, within
+// one ulp of the correctly rounded value (a third step changes nothing more).
 __device__ __forceinline__ double rsqrt_f64(double a) {
   double y = __builtin_amdgcn_rsq(a);
 #pragma unroll
-  for (int i = 0; i < 3; ++i) {
+  for (int i = 0; i < 2; ++i) {
     const double e = fma(-(a * y), y, 1.0);
     y = fma(0.5 * y, e, y);
   }
@@ -157,9 +158,10 @@ __device__ __forceinline__ double chunk_squares(const u32x4& a) {
 // Sums over the L consecutive lanes of a row for kN rows at once (xor
 // butterfly; a + b and b + a are the same float64, so every lane of a row
 // ends with the same bits), so that the lane exchanges of the rows overlap.
-template <int kN>
-__device__ __forceinline__ void row_sums(double* v, int L, int lane) {
-  for (int m = 1; m < L; m <<= 1) {
+template <int kN, int kL>
+__device__ __forceinline__ void row_sums(double* v, int lane) {
+#pragma unroll 1
+  for (int m = 1; m < kL; m <<= 1) {
     const int addr = (lane ^ m) << 2;
     double o[kN];
 #pragma unroll
@@ -326,13 +328,13 @@ struct TileData {
 };
 
 // Issue every load of a tile (rows past the tile's end re-read its first row).
-template <bool kBwd, int kTPT>
+template <bool kBwd, int kTPT, int kL>
 __device__ __forceinline__ void tile_loads(const NormParams& p, const TileGeom& gm, TileData<kTPT>& d) {
   const int tid = threadIdx.x;
   const NormTensor& tn = p.ten[gm.sel];
   const int32_t H = tn.H;
-  const int rows_per_step = kThreads >> p.lshift;
-  const int64_t off = static_cast<int64_t>(tid & (p.L - 1)) * 16;
+  constexpr int rows_per_step = kThreads / kL;
+  const int64_t off = static_cast<int64_t>(tid & (kL - 1)) * 16;
   if (tn.lin) {
     // token-major rows: row n0 + lr at (n0 + lr) * stride_h, the tile's part
     // of it once per tile
@@ -341,7 +343,7 @@ __device__ __forceinline__ void tile_loads(const NormParams& p, const TileGeom& 
     gchar* ob = (gchar*)tn.o + gm.n0 * tn.o_sh + off;
 #pragma unroll
     for (int u = 0; u < kTPT; ++u) {
-      const int lr = u * rows_per_step + (tid >> p.lshift);
+      const int lr = u * rows_per_step + tid / kL;
       d.act[u] = gm.n0 + lr < gm.n_end;
       const int64_t r = d.act[u] ? lr : 0;
       d.a[u] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4*>(xb + r * tn.x_sh));
@@ -353,7 +355,7 @@ __device__ __forceinline__ void tile_loads(const NormParams& p, const TileGeom& 
   }
 #pragma unroll
   for (int u = 0; u < kTPT; ++u) {
-    const int lr = u * rows_per_step + (tid >> p.lshift);
+    const int lr = u * rows_per_step + tid / kL;
     d.act[u] = gm.n0 + lr < gm.n_end;
     const uint32_t l = d.act[u] ? gm.r0 + static_cast<uint32_t>(lr) : gm.r0;
     const uint32_t tt = div_tok(l, tn.magic_heads);
@@ -411,13 +413,13 @@ __device__ __forceinline__ void seq_advance(const NormParams& p, SeqCursor& c, i
 // Positions and the table of a tile, from each entry's frequency f (and, for
 // the forward, the weights w1, w2 of the pair's two elements); ends with a
 // barrier.
-template <int kDtype, bool kIl, bool kBwd>
+template <int kDtype, bool kIl, bool kBwd, int kL>
 __device__ __forceinline__ void tile_table(const NormParams& p, const TileGeom& gm, const int* tt_e, const int* i_e,
                                            const double* f, const float* w1, const float* w2,
                                            const SeqCursor& sc, int32_t* s_pos, double2* s_cs) {
   constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;
   constexpr int kPPC = kIl ? kVec / 2 : kVec;
-  const int L = p.L, hl = p.L >> 1;
+  constexpr int L = kL, hl = kL / 2;
   const cu_ptr cu = (cu_ptr)p.cu;
   const int32_t nseq = p.nseq;
   const int64_t cu_last = cu[nseq];
@@ -458,6 +460,12 @@ __device__ __forceinline__ void tile_table(const NormParams& p, const TileGeom& 
           s_cs[(tt_e[v] * kVec + e1 % kVec) * L + e1 / kVec] = make_double2(a * cs, -(b * sn));
           s_cs[(tt_e[v] * kVec + e2 % kVec) * L + e2 / kVec] = make_double2(b * cs, a * sn);
         }
+      } else if constexpr (kBwd) {
+        // a token in no sequence: its rows enter the backward as zeros and
+        // must stay zeros through the rotation, so its entries are the
+        // identity rather than whatever an earlier kernel left in this LDS
+        // (0 times a stale NaN would reach the weight-gradient sums)
+        s_cs[cs_slot(tt_e[v], i_e[v], kPPC, kIl ? L : hl)] = make_double2(1.0, 0.0);
       }
     }
   }
@@ -468,7 +476,7 @@ __device__ __forceinline__ void tile_table(const NormParams& p, const TileGeom& 
 // together), then the forward rows one at a time, or the backward in phases;
 // then the stores.  s_w holds both tensors' weights (q then k); acc
 // (backward) receives this lane's weight-gradient terms.
-template <int kDtype, bool kIl, bool kBwd, int kTPT>
+template <int kDtype, bool kIl, bool kBwd, int kTPT, int kL>
 __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom& gm, const TileData<kTPT>& d,
                                              const int32_t* s_pos, const double2* s_cs, const float* s_w,
                                              double* acc) {
@@ -476,9 +484,8 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
   constexpr int kPPC = kIl ? kVec / 2 : kVec;          // table pairs per chunk
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int L = p.L;
+  constexpr int L = kL, hl = kL / 2;
   const int c = tid & (L - 1);
-  const int hl = L >> 1;
   const int sel = gm.sel;
   const NormTensor& tn = p.ten[sel];
   const int* tt_of = d.tt_of;
@@ -503,7 +510,7 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
     if constexpr (kBwd) g[u] = use ? d.g[u] : zero;
     r[u] = chunk_squares<kDtype>(a[u]);
   }
-  row_sums<kTPT>(r, L, lane);
+  row_sums<kTPT, kL>(r, lane);
 #pragma unroll
   for (int u = 0; u < kTPT; ++u) r[u] = rsqrt_f64(fma(r[u], p.inv_d, p.eps));
   if constexpr (!kBwd) {
@@ -520,7 +527,7 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
       out[u] = inside[u] ? y : a[u];
     }
   } else {
-    const float* w_own = s_w + sel * p.D + c * kVec;
+    const float* w_own = s_w + sel * (kL * kVec) + c * kVec;
     const int step = kIl ? L : hl;
     // dn stays in registers from the first pass to the second; the
     // weight-gradient terms are added in the second, where x is unpacked
@@ -539,7 +546,7 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
       gx[u] = bwd_chunk_gx<kDtype>(a[u], dn[u], w_own);
     }
     __builtin_amdgcn_sched_barrier(0);
-    row_sums<kTPT>(gx, L, lane);
+    row_sums<kTPT, kL>(gx, lane);
 #pragma unroll
     for (int u = 0; u < kTPT; ++u) {
       __builtin_amdgcn_sched_barrier(0);
@@ -559,7 +566,7 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
 
 
 // The forward tile: its frequencies and weights are loaded before its data.
-template <int kDtype, bool kIl, int kTPT>
+template <int kDtype, bool kIl, int kTPT, int kL>
 __device__ __forceinline__ void fwd_tile(const NormParams& p, uint32_t tile, int32_t* s_pos, double2* s_cs) {
   const TileGeom gm = tile_geom(p, tile);
   const NormTensor& tn = p.ten[gm.sel];
@@ -576,11 +583,11 @@ __device__ __forceinline__ void fwd_tile(const NormParams& p, uint32_t tile, int
   }
   __builtin_amdgcn_sched_barrier(0);
   TileData<kTPT> d;
-  tile_loads<false, kTPT>(p, gm, d);
+  tile_loads<false, kTPT, kL>(p, gm, d);
   __builtin_amdgcn_sched_barrier(0);
   const SeqCursor sc = seq_cursor(p, last_start_at_or_before((cu_ptr)p.cu, p.nseq, gm.t0));
-  tile_table<kDtype, kIl, false>(p, gm, tt_e, i_e, f, w1, w2, sc, s_pos, s_cs);
-  tile_compute<kDtype, kIl, false, kTPT>(p, gm, d, s_pos, s_cs, nullptr, nullptr);
+  tile_table<kDtype, kIl, false, kL>(p, gm, tt_e, i_e, f, w1, w2, sc, s_pos, s_cs);
+  tile_compute<kDtype, kIl, false, kTPT, kL>(p, gm, d, s_pos, s_cs, nullptr, nullptr);
 }
 
 // LDS of the norm kernels after the table (the forward's one, the backward's
@@ -603,23 +610,23 @@ __device__ __forceinline__ void load_weights(const NormParams& p, float* s_w) {
 }
 
 // Forward: one tile per workgroup.
-template <int kDtype, bool kIl, int kTPT>
+template <int kDtype, bool kIl, int kTPT, int kL>
 __global__ __launch_bounds__(kThreads) void rope_qk_norm_fwd_kernel(const NormParams p) {
   __shared__ int32_t s_pos[kMaxTileTokens];
   extern __shared__ double2 s_cs[];
   const uint32_t tile = blockIdx.y * gridDim.x + blockIdx.x;
   if (tile >= p.ntiles) return;
-  fwd_tile<kDtype, kIl, kTPT>(p, tile, s_pos, s_cs);
+  fwd_tile<kDtype, kIl, kTPT, kL>(p, tile, s_pos, s_cs);
 }
 
 // Adds this thread's weight-gradient terms of tensor `sel` into the
 // workgroup's sums: across the lanes of a wave that hold the same chunk, then
 // across the waves (in a fixed order); ends with a barrier.
-template <int kVec>
+template <int kVec, int kL>
 __device__ __forceinline__ void flush_dw(const NormParams& p, int sel, const double* acc, double* s_wave,
                                          double* s_acc) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int L = p.L, D = p.D;
+  constexpr int L = kL, D = kL * kVec;
   const int c = tid & (L - 1);
   double v[kVec];
 #pragma unroll
@@ -652,7 +659,7 @@ __device__ __forceinline__ void flush_dw(const NormParams& p, int sel, const dou
 // registers while the tiles are of one tensor (q's tiles come first, so that
 // changes at most once) and are summed across the workgroup only then and at
 // the end.
-template <int kDtype, bool kIl, int kTPT>
+template <int kDtype, bool kIl, int kTPT, int kL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBwdWaves16)))
 void rope_qk_norm_bwd_kernel(const NormParams p) {
   constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;
@@ -686,13 +693,13 @@ void rope_qk_norm_bwd_kernel(const NormParams p) {
     const TileGeom gm = tile_geom(p, tile);
     const bool fresh = gm.sel != cur;
     if (fresh) {
-      if (cur >= 0) flush_dw<kVec>(p, cur, acc, s_wave, s_acc);
+      if (cur >= 0) flush_dw<kVec, kL>(p, cur, acc, s_wave, s_acc);
 #pragma unroll
       for (int j = 0; j < kVec; ++j) acc[j] = 0.0;
       cur = gm.sel;
     }
     TileData<kTPT> d;
-    tile_loads<true, kTPT>(p, gm, d);
+    tile_loads<true, kTPT, kL>(p, gm, d);
     __builtin_amdgcn_sched_barrier(0);
     if (fresh)
       sc = seq_cursor(p, last_start_at_or_before((cu_ptr)p.cu, p.nseq, gm.t0));
@@ -703,11 +710,11 @@ void rope_qk_norm_bwd_kernel(const NormParams p) {
     tile_entries(p, gm, tt_e, i_e);
 #pragma unroll
     for (int v = 0; v < kEnt; ++v) f[v] = s_freq[i_e[v]];
-    tile_table<kDtype, kIl, true>(p, gm, tt_e, i_e, f, nullptr, nullptr, sc, s_pos[b], s_cs + b * tab_len);
-    tile_compute<kDtype, kIl, true, kTPT>(p, gm, d, s_pos[b], s_cs + b * tab_len, s_w, acc);
+    tile_table<kDtype, kIl, true, kL>(p, gm, tt_e, i_e, f, nullptr, nullptr, sc, s_pos[b], s_cs + b * tab_len);
+    tile_compute<kDtype, kIl, true, kTPT, kL>(p, gm, d, s_pos[b], s_cs + b * tab_len, s_w, acc);
     b ^= 1;
   }
-  if (cur >= 0) flush_dw<kVec>(p, cur, acc, s_wave, s_acc);
+  if (cur >= 0) flush_dw<kVec, kL>(p, cur, acc, s_wave, s_acc);
   double* dst = p.partial + static_cast<int64_t>(blockIdx.x) * 2 * D;
   for (int i = tid; i < 2 * D; i += kThreads) dst[i] = s_acc[i];
 }
@@ -867,20 +874,49 @@ void set_tensor(NormTensor* tn, const void* x, const Tensor& tx, const void* gr,
 
 bool same_tensor(const Tensor& a, const Tensor& b) { return a.base == b.base && a.st == b.st && a.sh == b.sh; }
 
-const void* pick_fwd(int dtype, bool il) {
-#define ROPE_NF(DT) (il ? reinterpret_cast<const void*>(&rope_qk_norm_fwd_kernel<DT, true, kFwdTasks>) \
-                        : reinterpret_cast<const void*>(&rope_qk_norm_fwd_kernel<DT, false, kFwdTasks>))
-  return dtype == ROPE_QK_BF16 ? ROPE_NF(ROPE_QK_BF16) : dtype == ROPE_QK_FP16 ? ROPE_NF(ROPE_QK_FP16)
-                                                                               : ROPE_NF(ROPE_QK_FP32);
+// The kernel instance for a call: storage type, pairing and row width L (a
+// compile-time constant, so that the table offsets of a row's elements are
+// immediate offsets of its LDS reads and the lane sums unroll).
+template <int kDtype, bool kIl>
+const void* fwd_for_width(int64_t L) {
+#define ROPE_NF(W) reinterpret_cast<const void*>(&rope_qk_norm_fwd_kernel<kDtype, kIl, kFwdTasks, W>)
+  switch (L) {
+    case 2: return ROPE_NF(2);
+    case 4: return ROPE_NF(4);
+    case 8: return ROPE_NF(8);
+    case 16: return ROPE_NF(16);
+    case 32: return ROPE_NF(32);
+    case 64: return ROPE_NF(64);
+    default: return nullptr;
+  }
 #undef ROPE_NF
 }
 
-const void* pick_bwd(int dtype, bool il) {
-#define ROPE_NB(DT) (il ? reinterpret_cast<const void*>(&rope_qk_norm_bwd_kernel<DT, true, kBwdTasks>) \
-                        : reinterpret_cast<const void*>(&rope_qk_norm_bwd_kernel<DT, false, kBwdTasks>))
-  return dtype == ROPE_QK_BF16 ? ROPE_NB(ROPE_QK_BF16) : dtype == ROPE_QK_FP16 ? ROPE_NB(ROPE_QK_FP16)
-                                                                               : ROPE_NB(ROPE_QK_FP32);
+template <int kDtype, bool kIl>
+const void* bwd_for_width(int64_t L) {
+#define ROPE_NB(W) reinterpret_cast<const void*>(&rope_qk_norm_bwd_kernel<kDtype, kIl, kBwdTasks, W>)
+  switch (L) {
+    case 2: return ROPE_NB(2);
+    case 4: return ROPE_NB(4);
+    case 8: return ROPE_NB(8);
+    case 16: return ROPE_NB(16);
+    case 32: return ROPE_NB(32);
+    case 64: return ROPE_NB(64);
+    default: return nullptr;
+  }
 #undef ROPE_NB
+}
+
+const void* pick_fwd(int dtype, bool il, int64_t L) {
+  if (dtype == ROPE_QK_BF16) return il ? fwd_for_width<ROPE_QK_BF16, true>(L) : fwd_for_width<ROPE_QK_BF16, false>(L);
+  if (dtype == ROPE_QK_FP16) return il ? fwd_for_width<ROPE_QK_FP16, true>(L) : fwd_for_width<ROPE_QK_FP16, false>(L);
+  return il ? fwd_for_width<ROPE_QK_FP32, true>(L) : fwd_for_width<ROPE_QK_FP32, false>(L);
+}
+
+const void* pick_bwd(int dtype, bool il, int64_t L) {
+  if (dtype == ROPE_QK_BF16) return il ? bwd_for_width<ROPE_QK_BF16, true>(L) : bwd_for_width<ROPE_QK_BF16, false>(L);
+  if (dtype == ROPE_QK_FP16) return il ? bwd_for_width<ROPE_QK_FP16, true>(L) : bwd_for_width<ROPE_QK_FP16, false>(L);
+  return il ? bwd_for_width<ROPE_QK_FP32, true>(L) : bwd_for_width<ROPE_QK_FP32, false>(L);
 }
 
 }  // namespace
@@ -916,8 +952,9 @@ int rope_qk_norm_fwd(const void* q, const void* k, void* q_out, void* k_out, con
   const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>((nt + gx - 1) / gx));
   const size_t lds = static_cast<size_t>(p.table_bytes) + static_cast<size_t>(2 * D) * sizeof(float);
   void* args[] = {&p};
-  const hipError_t err = hipLaunchKernel(pick_fwd(dtype, o.pairing == ROPE_QK_PAIR_INTERLEAVED), grid,
-                                         dim3(kThreads), args, lds, static_cast<hipStream_t>(stream));
+  const void* kernel = pick_fwd(dtype, o.pairing == ROPE_QK_PAIR_INTERLEAVED, g.L);
+  if (kernel == nullptr) return ROPE_QK_ERR_SHAPE;
+  const hipError_t err = hipLaunchKernel(kernel, grid, dim3(kThreads), args, lds, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? ROPE_QK_OK : ROPE_QK_ERR_LAUNCH;
 }
 
@@ -964,8 +1001,10 @@ int rope_qk_norm_bwd(const void* dq_out, const void* dk_out, const void* q, cons
     const size_t lds = static_cast<size_t>(2 * p.table_bytes) + static_cast<size_t>(2 * D) * sizeof(float) +
                        static_cast<size_t>((2 + kWaves) * D + D / 2) * sizeof(double);
     void* args[] = {&p};
-    const hipError_t err = hipLaunchKernel(pick_bwd(dtype, o.pairing == ROPE_QK_PAIR_INTERLEAVED),
-                                           dim3(static_cast<uint32_t>(g.groups)), dim3(kThreads), args, lds, s);
+    const void* kernel = pick_bwd(dtype, o.pairing == ROPE_QK_PAIR_INTERLEAVED, g.L);
+    if (kernel == nullptr) return ROPE_QK_ERR_SHAPE;
+    const hipError_t err =
+        hipLaunchKernel(kernel, dim3(static_cast<uint32_t>(g.groups)), dim3(kThreads), args, lds, s);
     if (err != hipSuccess) return ROPE_QK_ERR_LAUNCH;
   }
   if (dq_weight == nullptr && dk_weight == nullptr) return ROPE_QK_OK;

@@ -237,6 +237,24 @@ def test_norm_strided_views(dt):
         check_dw(dw, rdw, dw_terms(f64(g), f64(x), w64(w), cu, 1e4, o), "strided dw")
 
 
+def test_norm_bwd_outside_tokens_after_nan_tables():
+    """The backward's rows of tokens in no sequence enter as zeros; their
+    cos/sin entries must not come from whatever an earlier kernel left in LDS.
+    A forward with NaN weights first fills the LDS of every compute unit with
+    NaN table entries; the backward that follows, on a batch whose tail and
+    empty sequences lie outside, must still give finite weight gradients equal
+    to the oracle's."""
+    T, Hq, Hkv, D, dt = 900, 40, 8, 128, "fp16"
+    nan_w = torch.full((D,), float("nan"), dtype=torch.float32, device=DEV)
+    xq = W.randn((8192, Hq, D), dt, seed=71, device=DEV)
+    xk = W.randn((8192, Hkv, D), dt, seed=72, device=DEV)
+    cu_big = cu_dev([0, 8192])
+    for _ in range(3):
+        P.rope_qk_norm_fwd(xq, xk, nan_w, nan_w, EPS, cu_big, 1e4, torch.empty_like(xq), torch.empty_like(xk))
+        cu = [0, 1, 300, 300, 300, 651, 890]  # tokens 890.. lie outside
+        run_bwd(T, Hq, Hkv, D, dt, cu, 1e4, seed=73, in_place=False)
+
+
 def test_norm_nonfinite_rows_outside_sequences():
     """Rows of tokens outside every sequence may hold anything (say, a
     gradient buffer that nothing wrote): NaN and infinities there pass through
