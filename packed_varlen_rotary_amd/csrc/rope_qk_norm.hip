@@ -327,6 +327,11 @@ struct TileData {
   bool act[kTPT];
 };
 
+// a * b for b < 2^32 (its low word), as one 32 x 32 -> 64-bit multiply.
+__device__ __forceinline__ int64_t mul_u32_wide(uint32_t a, int64_t b) {
+  return static_cast<int64_t>(static_cast<uint64_t>(a) * static_cast<uint32_t>(b));
+}
+
 // Issue every load of a tile (rows past the tile's end re-read its first row).
 template <bool kBwd, int kTPT, int kL>
 __device__ __forceinline__ void tile_loads(const NormParams& p, const TileGeom& gm, TileData<kTPT>& d) {
@@ -345,11 +350,14 @@ __device__ __forceinline__ void tile_loads(const NormParams& p, const TileGeom& 
     for (int u = 0; u < kTPT; ++u) {
       const int lr = u * rows_per_step + tid / kL;
       d.act[u] = gm.n0 + lr < gm.n_end;
-      const int64_t r = d.act[u] ? lr : 0;
-      d.a[u] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4*>(xb + r * tn.x_sh));
-      if constexpr (kBwd) d.g[u] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4*>(gb + r * tn.g_sh));
-      d.optr[u] = ob + r * tn.o_sh;
-      d.tt_of[u] = static_cast<int>(div_tok(gm.r0 + static_cast<uint32_t>(r), tn.magic_heads));
+      const uint32_t r = d.act[u] ? static_cast<uint32_t>(lr) : 0u;
+      // head strides below 2^32 bytes (checked on the host for this form):
+      // each row offset is one 32 x 32 -> 64-bit multiply
+      d.a[u] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4*>(xb + mul_u32_wide(r, tn.x_sh)));
+      if constexpr (kBwd)
+        d.g[u] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4*>(gb + mul_u32_wide(r, tn.g_sh)));
+      d.optr[u] = ob + mul_u32_wide(r, tn.o_sh);
+      d.tt_of[u] = static_cast<int>(div_tok(gm.r0 + r, tn.magic_heads));
     }
     return;
   }
@@ -869,7 +877,11 @@ void set_tensor(NormTensor* tn, const void* x, const Tensor& tx, const void* gr,
   tn->o_st = to.st * esz;
   tn->o_sh = to.sh * esz;
   const int64_t H = tn->H;
-  tn->lin = tx.st == H * tx.sh && (tg == nullptr || tg->st == H * tg->sh) && to.st == H * to.sh;
+  // token-major with head strides below 2^32 bytes: the kernels address rows
+  // as n * head stride, with 32 x 32 -> 64-bit products
+  const int64_t kSh = int64_t(1) << 32;
+  tn->lin = tx.st == H * tx.sh && (tg == nullptr || tg->st == H * tg->sh) && to.st == H * to.sh &&
+            tn->x_sh < kSh && tn->g_sh < kSh && tn->o_sh < kSh;
 }
 
 bool same_tensor(const Tensor& a, const Tensor& b) { return a.base == b.base && a.st == b.st && a.sh == b.sh; }

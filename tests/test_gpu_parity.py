@@ -313,3 +313,38 @@ def test_short_sequences_and_large_positions(offset):
         for got, x in ((q, xq), (k, xk)):
             s = check_against(got, oracle.rope(x, cu, 1e4, 1, pos_offset=offset), f"D{D}")
             assert s["exact_fraction"] == 1.0, s
+
+
+@pytest.mark.parametrize("delta", [1, 4097, 500_000])
+def test_scores_depend_only_on_relative_position(delta):
+    """The property that makes the rotation a relative position encoding: the
+    score <f(q, m), f(k, n)> is the same when every position moves by delta.
+    fp32 q and k (GQA, 4 q heads per k head) rotated at positions 0..S-1 and
+    again, from fresh copies, at delta..delta+S-1 (pos_offset); every (m, n)
+    score of every head, in float64 from the stored fp32 outputs, agrees
+    within 1e-5 of |q_m| |k_n| (each output element carries one fp32 rounding,
+    the angles one float64 rounding)."""
+    S, Hq, Hkv, D = 96, 8, 2, 64
+    q = W.randn((S, Hq, D), "fp32", seed=delta, device=DEV)
+    k = W.randn((S, Hkv, D), "fp32", seed=delta + 1, device=DEV)
+    cu = cu_dev([0, S])
+    q0, k0, q1, k1 = q.clone(), k.clone(), q.clone(), k.clone()
+    P.rope_qk_fwd(q0, k0, cu, 1e4)
+    P.rope_qk_fwd(q1, k1, cu, 1e4, pos_offset=delta)
+    torch.cuda.synchronize()
+    g = Hq // Hkv
+    for a, b in ((q0, k0), (q1, k1)):
+        assert torch.isfinite(a).all() and torch.isfinite(b).all()
+
+    def scores(qr, kr):  # [Hq, S(m), S(n)] in float64, each q head against its k head
+        qh = f64(qr).transpose(1, 0, 2)
+        kh = np.repeat(f64(kr), g, axis=1).transpose(1, 2, 0)
+        return qh @ kh
+
+    s0, s1 = scores(q0, k0), scores(q1, k1)
+    qn = np.linalg.norm(f64(q), axis=-1).T[:, :, None]
+    kn = np.repeat(np.linalg.norm(f64(k), axis=-1), g, axis=1).T[:, None, :]
+    err = np.abs(s0 - s1) / (qn * kn)
+    assert float(err.max()) <= 1e-5, float(err.max())
+    # and the positions did move: the rotated tensors themselves differ
+    assert not torch.equal(q0, q1)
