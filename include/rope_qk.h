@@ -240,7 +240,8 @@ int rope_qk_norm_fwd(const void* q, const void* k, void* q_out, void* k_out, con
  * Bytes of device workspace rope_qk_norm_bwd needs for these sizes (>= 0), or
  * a negative status (ROPE_QK_ERR_DTYPE, ROPE_QK_ERR_SHAPE): 16 * D bytes for
  * each of the backward's workgroups, of which there are at most 3072 for
- * bf16 and fp16 and 4096 for fp32 (6 MiB at D = 128 in bf16; at most 32 MiB).
+ * bf16 and fp16 and 4096 for fp32 (6 MiB at D = 128 in bf16; at most 24 MiB,
+ * at D = 512 in bf16 or fp16).
  */
 int64_t rope_qk_norm_bwd_workspace_bytes(int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int dtype);
 

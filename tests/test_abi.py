@@ -288,8 +288,11 @@ def test_norm_bwd_error_codes_and_workspace_size():
     big = lib.rope_qk_norm_bwd_workspace_bytes(65536, 32, 8, 128, 1)
     assert big == 3072 * 2 * 128 * 8
     assert lib.rope_qk_norm_bwd_workspace_bytes(65536, 32, 8, 128, 0) == 4096 * 2 * 128 * 8
-    # the largest: D = 512 in float32, 32 MiB as the header states
-    assert lib.rope_qk_norm_bwd_workspace_bytes(10 ** 6, 8, 8, 512, 0) == 32 << 20
+    # the largest, as the header states: D = 512 in bf16, 24 MiB (float32
+    # rows stop at D = 256: 16 MiB)
+    assert lib.rope_qk_norm_bwd_workspace_bytes(10 ** 6, 8, 8, 512, 1) == 24 << 20
+    assert lib.rope_qk_norm_bwd_workspace_bytes(10 ** 6, 8, 8, 256, 0) == 16 << 20
+    assert lib.rope_qk_norm_bwd_workspace_bytes(10 ** 6, 8, 8, 512, 0) == C["ROPE_QK_ERR_SHAPE"]
     assert norm_bwd(ws=0) == C["ROPE_QK_ERR_WORKSPACE"]
     assert norm_bwd(ws_size=need - 16) == C["ROPE_QK_ERR_WORKSPACE"]
     assert norm_bwd(ws=WS + 8) == C["ROPE_QK_ERR_ALIGN"]
