@@ -90,8 +90,6 @@ struct NormParams {
   int32_t nseq;
   int32_t D;
   int32_t half;          // D / 2
-  int32_t L;             // chunks per row
-  int32_t lshift;        // log2(L)
   int32_t pos_offset;
   int32_t freq_fp32;
   double inv_freq[kMaxHalf];
@@ -856,10 +854,6 @@ void fill_params(NormParams* p, const NormGeometry& g, const int32_t* cu, int64_
   p->nseq = static_cast<int32_t>(nseq);
   p->D = static_cast<int32_t>(D);
   p->half = static_cast<int32_t>(D / 2);
-  p->L = static_cast<int32_t>(g.L);
-  int s = 0;
-  while ((int64_t(1) << s) < g.L) ++s;
-  p->lshift = s;
   p->pos_offset = static_cast<int32_t>(o.pos_offset);
   p->freq_fp32 = o.freq_precision == ROPE_QK_FREQ_FP32;
   fill_inv_freq(theta, D, o, p->inv_freq);
