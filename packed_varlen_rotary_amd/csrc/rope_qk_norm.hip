@@ -21,7 +21,7 @@
 //    inside a token.
 //  * Per row: the sum of squares in float64, summed over the row's lanes by
 //    a xor butterfly (ds_bpermute; every lane ends with the same bits),
-//    r = 1/sqrt(mean + eps) from v_rsq_f64 and three Newton steps, then the
+//    r = 1/sqrt(mean + eps) from v_rsq_f64 and two Newton steps, then the
 //    rotation exactly as in the rotation kernels: the rotate_half partner
 //    chunk comes from lane l ^ L/2 (negated in the first half), interleaved
 //    pairs sit inside a chunk; the cos/sin table is built once per tile.
@@ -37,6 +37,10 @@
 //    in LDS that the workgroup writes once at the end; a small kernel adds
 //    the workgroups' sums in a fixed tree order, so the result is
 //    deterministic.
+//  * Rows of tokens in no sequence pass through unchanged; in the backward
+//    they enter the arithmetic as zeros, with identity table entries.
+//  * The kernels are instantiated per row width L, so the table offsets of a
+//    row's elements are immediate offsets of its LDS reads.
 //  * Everything is evaluated in float64 and rounded once to the storage type.
 
 #include "rope_common.h"
