@@ -377,3 +377,39 @@ def test_norm_qwen3_8b_shape_full_size():
         check_dw(dw, ref, S, f"dw{nm} full size")
     del t, make
     torch.cuda.empty_cache()
+
+
+def test_norm_long_context_full_size():
+    """The 524,288-token single sequence (32 + 8 heads, D = 128, bf16; q has
+    2^31 elements, so row offsets pass 2^32 bytes): forward out of place and
+    backward in place at full size, outputs of sampled tokens (every head and
+    element, the last token included) against the oracle, bit for bit; the
+    weight gradients finite (their sum over every token is checked against
+    the oracle on the Qwen3-8B shape)."""
+    w = W.make_workload(5)
+    T, Hq, Hkv, D = w.T, w.Hq, w.Hkv, w.D
+    assert T * Hq * D == 2 ** 31
+    t = W.make_tensors(w, ("q", "k", "dq", "dk"), device=DEV)
+    wq, wk = weights(D, 61), weights(D, 62)
+    cu = cu_dev(w.cu_seqlens)
+    idx = np.unique(np.concatenate([sample_tokens(w.cu_seqlens, T, 256, seed=5), [T - 1]]))
+    idx_d = torch.as_tensor(idx, device=DEV)
+    pos = oracle.segment_positions(w.cu_seqlens, T)[idx]
+    qo, ko = torch.empty_like(t["q"]), torch.empty_like(t["k"])
+    P.rope_qk_norm_fwd(t["q"], t["k"], wq, wk, EPS, cu, w.theta, qo, ko)
+    for x, y, wt, nm in ((t["q"], qo, wq, "q"), (t["k"], ko, wk, "k")):
+        n, _ = oracle.rms_norm(f64(x.index_select(0, idx_d)), w64(wt), EPS)
+        s = check_against(y.index_select(0, idx_d), oracle.rotate(n, pos, w.theta, 1), f"fwd {nm}")
+        assert s["exact_fraction"] == 1.0, s
+    del qo, ko
+    g_s = {nm: f64(t["d" + nm].index_select(0, idx_d)) for nm in ("q", "k")}
+    dq, dk, dwq, dwk = P.rope_qk_norm_bwd(t["dq"], t["dk"], t["q"], t["k"], wq, wk, EPS, cu, w.theta)
+    torch.cuda.synchronize()
+    for x, dx, wt, nm in ((t["q"], dq, wq, "q"), (t["k"], dk, wk, "k")):
+        dn = oracle.rotate(g_s[nm], pos, w.theta, -1)
+        rdx, _ = oracle.rms_norm_bwd(dn, f64(x.index_select(0, idx_d)), w64(wt), EPS)
+        s = check_against(dx.index_select(0, idx_d), rdx, f"bwd d{nm}")
+        assert s["exact_fraction"] == 1.0, s
+    assert torch.isfinite(dwq).all() and torch.isfinite(dwk).all()
+    del t, dq, dk
+    torch.cuda.empty_cache()
