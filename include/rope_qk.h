@@ -39,8 +39,9 @@
  *
  * Memory, ownership, ordering
  * ---------------------------
- * All tensor pointers are device memory owned by the caller; the library keeps
- * no state and allocates nothing.  q is [T, Hq, D] and k is [T, Hkv, D] with
+ * All tensor pointers are device memory owned by the caller; the library
+ * allocates nothing, and its only state is the static scratch array of
+ * rope_qk_norm_bwd_noalloc (part of its code object).  q is [T, Hq, D] and k is [T, Hkv, D] with
  * element strides (stride_t, stride_h) and a unit stride along D; the two
  * tensors must not overlap each other and each must not overlap itself
  * (checked from the strides; q/k views into one fused QKV buffer are fine).
@@ -81,6 +82,7 @@ extern "C" {
 #define ROPE_QK_ERR_LAYOUT -7    /* negative strides, or a tensor whose rows overlap */
 #define ROPE_QK_ERR_OPTION -8    /* a field of rope_qk_options out of range (or eps, for the norm calls) */
 #define ROPE_QK_ERR_WORKSPACE -9 /* workspace NULL or smaller than rope_qk_norm_bwd_workspace_bytes */
+#define ROPE_QK_ERR_SCRATCH -10  /* rope_qk_norm_bwd_noalloc: the call needs more than its static scratch */
 
 /* pairing of the rotated elements of a head (rope_qk_options.pairing) */
 #define ROPE_QK_PAIR_HALF 0         /* element i with element i + r/2 ("rotate_half"; the default) */
@@ -281,6 +283,29 @@ int rope_qk_norm_bwd(const void* dq_out, const void* dk_out, const void* q, cons
                      void* workspace, int64_t workspace_size, const int32_t* cu_seqlens, int64_t nseq, int64_t T,
                      int64_t Hq, int64_t Hkv, int64_t D, const int64_t* strides, double theta, int dtype,
                      const rope_qk_options* options, void* stream);
+
+/*
+ * rope_qk_norm_bwd for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as rope_qk_norm_bwd without the
+ * workspace: the weight-gradient sums go to a static device array of 24 MiB
+ * per GPU (the largest workspace any accepted shape needs, so every call the
+ * workspace form accepts fits; ROPE_QK_ERR_SCRATCH would report one that
+ * does not).  The array is part of the library's code object: each GPU the
+ * library runs on holds its own copy until the process ends, and its address
+ * is looked up once per device, on the first call for that device (the
+ * device of `stream`, or the current device for the NULL stream).  The call
+ * makes no hipMalloc, hipFree or other allocation.  Every call on one GPU
+ * shares that GPU's array: calls that may overlap on one GPU (different
+ * streams, host threads or processes sharing the code object) race and must
+ * be ordered by the caller, e.g. by one stream.  Nothing in the array needs
+ * to start at any value: each call writes every sum it reads.
+ */
+int rope_qk_norm_bwd_noalloc(const void* dq_out, const void* dk_out, const void* q, const void* k, void* dq,
+                             void* dk, const float* q_weight, const float* k_weight, double eps, float* dq_weight,
+                             float* dk_weight, const int32_t* cu_seqlens, int64_t nseq, int64_t T, int64_t Hq,
+                             int64_t Hkv, int64_t D, const int64_t* strides, double theta, int dtype,
+                             const rope_qk_options* options, void* stream);
 
 /*
  * The positions the rotation kernels use, for inspection: writes, for every

@@ -31,6 +31,7 @@ from ._lib import (  # noqa: F401
     rope_qk_fwd,
     rope_qk_fwd_opt,
     rope_qk_norm_bwd,
+    rope_qk_norm_bwd_noalloc,
     rope_qk_norm_bwd_workspace_bytes,
     rope_qk_norm_fwd,
     rope_qk_positions,
@@ -44,6 +45,7 @@ __all__ = [
     "rope_qk_bwd_opt",
     "rope_qk_norm_fwd",
     "rope_qk_norm_bwd",
+    "rope_qk_norm_bwd_noalloc",
     "rope_qk_norm_bwd_workspace_bytes",
     "RopeQKOptions",
     "make_options",

@@ -28,7 +28,8 @@ ROPE_QK_FREQ_FP32 = 1
 
 # names exported by include/rope_qk.h
 EXPORTS = ("rope_qk_fwd", "rope_qk_bwd", "rope_qk_fwd_opt", "rope_qk_bwd_opt", "rope_qk_norm_fwd",
-           "rope_qk_norm_bwd", "rope_qk_norm_bwd_workspace_bytes", "rope_qk_positions", "rope_qk_strerror",
+           "rope_qk_norm_bwd", "rope_qk_norm_bwd_workspace_bytes", "rope_qk_norm_bwd_noalloc", "rope_qk_positions",
+           "rope_qk_strerror",
            "rope_pack_bfd", "rope_pack_cu_seqlens", "rope_pack_cache_create", "rope_pack_cache_get",
            "rope_pack_cache_stats", "rope_pack_cache_destroy")
 
@@ -131,6 +132,9 @@ def load():
         lib.rope_qk_norm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, dbl, vp, vp, vp, i64, vp, i64, i64, i64,
                                          i64, i64, i64p, dbl, ctypes.c_int, optp, vp]
         lib.rope_qk_norm_bwd.restype = ctypes.c_int
+        lib.rope_qk_norm_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, dbl, vp, vp, vp, i64, i64, i64,
+                                                 i64, i64, i64p, dbl, ctypes.c_int, optp, vp]
+        lib.rope_qk_norm_bwd_noalloc.restype = ctypes.c_int
         lib.rope_qk_norm_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
         lib.rope_qk_norm_bwd_workspace_bytes.restype = ctypes.c_int64
         lib.rope_pack_bfd.argtypes = [vp, i64, i64, vp, vp, ctypes.POINTER(i64)]
@@ -349,6 +353,35 @@ def rope_qk_norm_bwd_workspace_bytes(T: int, Hq: int, Hkv: int, D: int, dtype_co
     if n < 0:
         _check(int(n))
     return int(n)
+
+
+def rope_qk_norm_bwd_noalloc(dq_out, dk_out, q, k, q_weight, k_weight, eps: float, cu_seqlens, theta: float,
+                             dq, dk, dq_weight, dk_weight, stream=None, *, pos_offset: int = 0,
+                             interleaved: bool = False, llama3=None, freq_fp32: bool = False):
+    """rope_qk_norm_bwd without a workspace: the library's static per-GPU
+    scratch holds the weight-gradient sums, so the call allocates nothing
+    (every output is the caller's; pass dq is dq_out for in place).  Calls
+    that may overlap on one GPU share that scratch and must be ordered."""
+    import torch
+
+    lib = load()
+    for name, t in (("dk_out", dk_out), ("k", k), ("dq", dq), ("dk", dk), ("dq_out", dq_out)):
+        _check_rows(name, t, q)
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor")
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    opts = make_options(pos_offset, 0, interleaved, llama3, freq_fp32)
+    with torch.cuda.device(q.device):
+        status = lib.rope_qk_norm_bwd_noalloc(
+            _ptr(dq_out), _ptr(dk_out), _ptr(q), _ptr(k), _ptr(dq), _ptr(dk),
+            _check_weight("q_weight", q_weight, D, q.device), _check_weight("k_weight", k_weight, D, q.device),
+            float(eps), _check_weight("dq_weight", dq_weight, D, q.device),
+            _check_weight("dk_weight", dk_weight, D, q.device), _ptr(cu_seqlens), cu_seqlens.numel() - 1, T, Hq,
+            Hkv, D, _strides(dq_out, dk_out, q, k, dq, dk), float(theta), _dtype_code(q), ctypes.byref(opts),
+            _stream_ptr(q.device, stream))
+    _check(status)
+    return dq, dk, dq_weight, dk_weight
 
 
 def rope_qk_norm_bwd(dq_out, dk_out, q, k, q_weight, k_weight, eps: float, cu_seqlens, theta: float, dq=None,

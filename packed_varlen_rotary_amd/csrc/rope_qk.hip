@@ -568,6 +568,8 @@ const char* rope_qk_strerror(int status) {
     case ROPE_QK_ERR_OPTION:
       return "an option is out of range (pos_offset, rotary_dim, pairing, scaling, freq_precision, reserved or eps)";
     case ROPE_QK_ERR_WORKSPACE: return "workspace missing or smaller than rope_qk_norm_bwd_workspace_bytes";
+    case ROPE_QK_ERR_SCRATCH:
+      return "the call needs more weight-gradient scratch than rope_qk_norm_bwd_noalloc's static 24 MiB";
     default: return "unknown status";
   }
 }

@@ -45,6 +45,8 @@
 
 #include "rope_common.h"
 
+#include <mutex>
+
 namespace {
 
 constexpr int kFwdTasks = 4;          // rows per lane per forward tile
@@ -929,6 +931,108 @@ const void* pick_bwd(int dtype, bool il, int64_t L) {
   return il ? bwd_for_width<ROPE_QK_FP32, true>(L) : bwd_for_width<ROPE_QK_FP32, false>(L);
 }
 
+// Weight-gradient scratch of rope_qk_norm_bwd_noalloc: one array per GPU the
+// library runs on, held until the process ends.  Its size is the largest
+// workspace any accepted shape needs (bf16 or fp16 at D = 512: 3072
+// workgroups x 2 D float64 sums), so every call the workspace form accepts
+// fits.  In host code `scratch` names a host-side stand-in; its device
+// address comes from hipGetSymbolAddress, per device.
+constexpr int64_t kScratchBytes = kBwdGroups16 * 2 * (2 * kMaxHalf) * static_cast<int64_t>(sizeof(double));
+static_assert(kScratchBytes == 24 << 20, "scratch size stated in include/rope_qk.h");
+static_assert(kBwdGroups32 * 2 * kMaxHalf * static_cast<int64_t>(sizeof(double)) <= kScratchBytes,
+              "float32 rows (D <= 256) fit too");
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on `device`, looked up once per device
+// with that device current (each GPU holds its own copy of the array).
+int scratch_address(int device, void** out) {
+  if (device < 0 || device >= kMaxDevices) return ROPE_QK_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device] == nullptr) {
+    int current = -1;
+    if (hipGetDevice(&current) != hipSuccess) return ROPE_QK_ERR_LAUNCH;
+    if (current != device && hipSetDevice(device) != hipSuccess) return ROPE_QK_ERR_LAUNCH;
+    void* ptr = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (current != device && hipSetDevice(current) != hipSuccess) return ROPE_QK_ERR_LAUNCH;
+    if (err != hipSuccess || ptr == nullptr) return ROPE_QK_ERR_LAUNCH;
+    g_scratch_ptr[device] = ptr;
+  }
+  *out = g_scratch_ptr[device];
+  return ROPE_QK_OK;
+}
+
+// The backward's checks and launches.  use_scratch: the no-allocation form,
+// whose sums go to this device's `scratch` (looked up after every host
+// check, so its errors come in the workspace form's order) instead of the
+// caller's workspace.
+int norm_bwd_impl(const void* dq_out, const void* dk_out, const void* q, const void* k, void* dq, void* dk,
+                  const float* q_weight, const float* k_weight, double eps, float* dq_weight, float* dk_weight,
+                  void* workspace, int64_t workspace_size, const int32_t* cu_seqlens, int64_t nseq, int64_t T,
+                  int64_t Hq, int64_t Hkv, int64_t D, const int64_t* strides, double theta, int dtype,
+                  const rope_qk_options* options, void* stream, bool use_scratch) {
+  const rope_qk_options o = options ? *options : rope_qk_options{};
+  if (strides == nullptr) return ROPE_QK_ERR_NULL;
+  const Tensor ts[6] = {{dq_out, strides[0], strides[1]}, {dk_out, strides[2], strides[3]},
+                        {q, strides[4], strides[5]},      {k, strides[6], strides[7]},
+                        {dq, strides[8], strides[9]},     {dk, strides[10], strides[11]}};
+  NormGeometry g;
+  const int status = check_norm_call(dtype, nseq, T, Hq, Hkv, D, theta, o, eps, q_weight, k_weight, ts, 6, true, &g);
+  if (status != ROPE_QK_OK) return status;
+  if ((Hq > 0 && dq_weight == nullptr) || (Hkv > 0 && dk_weight == nullptr)) return ROPE_QK_ERR_NULL;
+  const int64_t need = workspace_bytes(g, D);
+  if (use_scratch) {
+    if (need > kScratchBytes) return ROPE_QK_ERR_SCRATCH;
+  } else {
+    if (need > 0 && (workspace == nullptr || workspace_size < need)) return ROPE_QK_ERR_WORKSPACE;
+    if (workspace != nullptr && !aligned16(workspace)) return ROPE_QK_ERR_ALIGN;
+  }
+  if (!(dq_weight == nullptr || aligned16(dq_weight)) || !(dk_weight == nullptr || aligned16(dk_weight)))
+    return ROPE_QK_ERR_ALIGN;
+  if (g.groups > 0 && cu_seqlens == nullptr) return ROPE_QK_ERR_NULL;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (use_scratch) {
+    // the device the kernels run on: the stream's, or the current one for the NULL stream
+    int device = -1;
+    if (s != nullptr ? hipStreamGetDevice(s, &device) != hipSuccess : hipGetDevice(&device) != hipSuccess)
+      return ROPE_QK_ERR_LAUNCH;
+    const int found = scratch_address(device, &workspace);
+    if (found != ROPE_QK_OK) return found;
+  }
+  const int64_t esz = dtype == ROPE_QK_FP32 ? 4 : 2;
+  double* partial = static_cast<double*>(workspace);
+  if (g.groups > 0) {
+    NormParams p;
+    fill_params(&p, g, cu_seqlens, nseq, T, Hq, Hkv, D, theta, eps, o, q_weight, k_weight, -1.0);
+    set_tensor(&p.ten[0], q, ts[2], dq_out, &ts[0], dq, ts[4], esz);
+    set_tensor(&p.ten[1], k, ts[3], dk_out, &ts[1], dk, ts[5], esz);
+    p.ten[0].copy = Hq > 0 && !same_tensor(ts[0], ts[4]);
+    p.ten[1].copy = Hkv > 0 && !same_tensor(ts[1], ts[5]);
+    p.partial = partial;
+    const size_t lds = static_cast<size_t>(2 * p.table_bytes) + static_cast<size_t>(2 * D) * sizeof(float) +
+                       static_cast<size_t>((2 + kWaves) * D + D / 2) * sizeof(double);
+    void* args[] = {&p};
+    const void* kernel = pick_bwd(dtype, o.pairing == ROPE_QK_PAIR_INTERLEAVED, g.L);
+    if (kernel == nullptr) return ROPE_QK_ERR_SHAPE;
+    const hipError_t err =
+        hipLaunchKernel(kernel, dim3(static_cast<uint32_t>(g.groups)), dim3(kThreads), args, lds, s);
+    if (err != hipSuccess) return ROPE_QK_ERR_LAUNCH;
+  }
+  if (dq_weight == nullptr && dk_weight == nullptr) return ROPE_QK_OK;
+  uint32_t ng = static_cast<uint32_t>(g.groups);
+  int32_t d32 = static_cast<int32_t>(D);
+  const double* partial_c = partial;
+  void* args[] = {const_cast<double**>(&partial_c), &ng, &d32, &dq_weight, &dk_weight};
+  const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&dw_reduce_kernel),
+                                         dim3(static_cast<uint32_t>(2 * D)), dim3(kThreads), args, 0, s);
+  return err == hipSuccess ? ROPE_QK_OK : ROPE_QK_ERR_LAUNCH;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -982,49 +1086,18 @@ int rope_qk_norm_bwd(const void* dq_out, const void* dk_out, const void* q, cons
                      void* workspace, int64_t workspace_size, const int32_t* cu_seqlens, int64_t nseq, int64_t T,
                      int64_t Hq, int64_t Hkv, int64_t D, const int64_t* strides, double theta, int dtype,
                      const rope_qk_options* options, void* stream) {
-  const rope_qk_options o = options ? *options : rope_qk_options{};
-  if (strides == nullptr) return ROPE_QK_ERR_NULL;
-  const Tensor ts[6] = {{dq_out, strides[0], strides[1]}, {dk_out, strides[2], strides[3]},
-                        {q, strides[4], strides[5]},      {k, strides[6], strides[7]},
-                        {dq, strides[8], strides[9]},     {dk, strides[10], strides[11]}};
-  NormGeometry g;
-  const int status = check_norm_call(dtype, nseq, T, Hq, Hkv, D, theta, o, eps, q_weight, k_weight, ts, 6, true, &g);
-  if (status != ROPE_QK_OK) return status;
-  if ((Hq > 0 && dq_weight == nullptr) || (Hkv > 0 && dk_weight == nullptr)) return ROPE_QK_ERR_NULL;
-  const int64_t need = workspace_bytes(g, D);
-  if (need > 0 && (workspace == nullptr || workspace_size < need)) return ROPE_QK_ERR_WORKSPACE;
-  if (workspace != nullptr && !aligned16(workspace)) return ROPE_QK_ERR_ALIGN;
-  if (!(dq_weight == nullptr || aligned16(dq_weight)) || !(dk_weight == nullptr || aligned16(dk_weight)))
-    return ROPE_QK_ERR_ALIGN;
-  if (g.groups > 0 && cu_seqlens == nullptr) return ROPE_QK_ERR_NULL;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t esz = dtype == ROPE_QK_FP32 ? 4 : 2;
-  double* partial = static_cast<double*>(workspace);
-  if (g.groups > 0) {
-    NormParams p;
-    fill_params(&p, g, cu_seqlens, nseq, T, Hq, Hkv, D, theta, eps, o, q_weight, k_weight, -1.0);
-    set_tensor(&p.ten[0], q, ts[2], dq_out, &ts[0], dq, ts[4], esz);
-    set_tensor(&p.ten[1], k, ts[3], dk_out, &ts[1], dk, ts[5], esz);
-    p.ten[0].copy = Hq > 0 && !same_tensor(ts[0], ts[4]);
-    p.ten[1].copy = Hkv > 0 && !same_tensor(ts[1], ts[5]);
-    p.partial = partial;
-    const size_t lds = static_cast<size_t>(2 * p.table_bytes) + static_cast<size_t>(2 * D) * sizeof(float) +
-                       static_cast<size_t>((2 + kWaves) * D + D / 2) * sizeof(double);
-    void* args[] = {&p};
-    const void* kernel = pick_bwd(dtype, o.pairing == ROPE_QK_PAIR_INTERLEAVED, g.L);
-    if (kernel == nullptr) return ROPE_QK_ERR_SHAPE;
-    const hipError_t err =
-        hipLaunchKernel(kernel, dim3(static_cast<uint32_t>(g.groups)), dim3(kThreads), args, lds, s);
-    if (err != hipSuccess) return ROPE_QK_ERR_LAUNCH;
-  }
-  if (dq_weight == nullptr && dk_weight == nullptr) return ROPE_QK_OK;
-  uint32_t ng = static_cast<uint32_t>(g.groups);
-  int32_t d32 = static_cast<int32_t>(D);
-  const double* partial_c = partial;
-  void* args[] = {const_cast<double**>(&partial_c), &ng, &d32, &dq_weight, &dk_weight};
-  const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&dw_reduce_kernel),
-                                         dim3(static_cast<uint32_t>(2 * D)), dim3(kThreads), args, 0, s);
-  return err == hipSuccess ? ROPE_QK_OK : ROPE_QK_ERR_LAUNCH;
+  return norm_bwd_impl(dq_out, dk_out, q, k, dq, dk, q_weight, k_weight, eps, dq_weight, dk_weight, workspace,
+                       workspace_size, cu_seqlens, nseq, T, Hq, Hkv, D, strides, theta, dtype, options, stream,
+                       false);
+}
+
+int rope_qk_norm_bwd_noalloc(const void* dq_out, const void* dk_out, const void* q, const void* k, void* dq,
+                             void* dk, const float* q_weight, const float* k_weight, double eps, float* dq_weight,
+                             float* dk_weight, const int32_t* cu_seqlens, int64_t nseq, int64_t T, int64_t Hq,
+                             int64_t Hkv, int64_t D, const int64_t* strides, double theta, int dtype,
+                             const rope_qk_options* options, void* stream) {
+  return norm_bwd_impl(dq_out, dk_out, q, k, dq, dk, q_weight, k_weight, eps, dq_weight, dk_weight, nullptr, 0,
+                       cu_seqlens, nseq, T, Hq, Hkv, D, strides, theta, dtype, options, stream, true);
 }
 
 }  // extern "C"

@@ -302,3 +302,37 @@ def test_norm_bwd_error_codes_and_workspace_size():
     assert norm_bwd(wq=0) == C["ROPE_QK_ERR_NULL"]
     assert norm_bwd(cu=0) == C["ROPE_QK_ERR_NULL"]
     assert norm_bwd(dtype=5) == C["ROPE_QK_ERR_DTYPE"]
+
+
+def norm_bwd_noalloc(dwq=0x70000, dwk=0x80000, wq=W_Q, eps=1e-6, T=256, Hq=14, Hkv=2, D=64, dtype=1, cu=CU,
+                     opts=None, theta=1e6, strides="default"):
+    st = None if strides is None else (ctypes.c_int64 * 12)(*([Hq * D, D, Hkv * D, D] * 3))
+    return lib.rope_qk_norm_bwd_noalloc(ctypes.c_void_p(Q), ctypes.c_void_p(K), ctypes.c_void_p(Q + (1 << 24)),
+                                        ctypes.c_void_p(K + (1 << 24)), ctypes.c_void_p(Q), ctypes.c_void_p(K),
+                                        ctypes.c_void_p(wq), ctypes.c_void_p(W_K), eps, ctypes.c_void_p(dwq),
+                                        ctypes.c_void_p(dwk), ctypes.c_void_p(cu), 4, T, Hq, Hkv, D, st, theta, dtype,
+                                        ctypes.byref(opts) if opts is not None else None, None)
+
+
+def test_norm_bwd_noalloc_checks_before_any_hip_call():
+    """The no-allocation backward runs every host check of the workspace form,
+    in the same order, before it looks up its scratch (the first HIP call)."""
+    assert norm_bwd_noalloc(dtype=5) == C["ROPE_QK_ERR_DTYPE"]
+    assert norm_bwd_noalloc(D=96) == C["ROPE_QK_ERR_SHAPE"]
+    assert norm_bwd_noalloc(D=1024) == C["ROPE_QK_ERR_SHAPE"]
+    assert norm_bwd_noalloc(theta=float("nan")) == C["ROPE_QK_ERR_THETA"]
+    assert norm_bwd_noalloc(eps=0.0) == C["ROPE_QK_ERR_OPTION"]
+    assert norm_bwd_noalloc(opts=P.make_options(rotary_dim=32)) == C["ROPE_QK_ERR_OPTION"]
+    assert norm_bwd_noalloc(strides=None) == C["ROPE_QK_ERR_NULL"]
+    assert norm_bwd_noalloc(wq=0) == C["ROPE_QK_ERR_NULL"]
+    assert norm_bwd_noalloc(dwq=0) == C["ROPE_QK_ERR_NULL"]
+    assert norm_bwd_noalloc(dwq=0x70004) == C["ROPE_QK_ERR_ALIGN"]
+    assert norm_bwd_noalloc(cu=0) == C["ROPE_QK_ERR_NULL"]
+    # the same calls give the same codes in the workspace form
+    assert norm_bwd(dtype=5) == C["ROPE_QK_ERR_DTYPE"] and norm_bwd(D=96) == C["ROPE_QK_ERR_SHAPE"]
+    assert norm_bwd(eps=0.0) == C["ROPE_QK_ERR_OPTION"] and norm_bwd(cu=0) == C["ROPE_QK_ERR_NULL"]
+    # every shape the workspace form accepts fits the 24 MiB static scratch
+    assert max(lib.rope_qk_norm_bwd_workspace_bytes(10 ** 6, 8, 8, 512, 1),
+               lib.rope_qk_norm_bwd_workspace_bytes(10 ** 6, 8, 8, 512, 2),
+               lib.rope_qk_norm_bwd_workspace_bytes(10 ** 6, 8, 8, 256, 0)) == 24 << 20
+    assert "24 MiB" in P.rope_qk_strerror(C["ROPE_QK_ERR_SCRATCH"])
