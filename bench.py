@@ -1,6 +1,6 @@
 """Benchmark: fused QK-RoPE forward + backward over a packed variable-length batch.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--table 2,3,4]
 
 One step = the whole hot path over one packed batch: rope_qk_fwd on (q, k)
 then rope_qk_bwd on (dq, dk), each one kernel launch through the C ABI.
@@ -8,21 +8,28 @@ Inputs are resident in HBM before timing starts; consecutive steps rotate
 over enough independent batches (>= 1 GiB in total) that every launch reads
 cold HBM rather than the 256 MB Infinity Cache.
 
+The headline workload (default 5: the Llama-3.1-8B-shaped 524,288-token
+context, the largest) gives `value` and `roofline`; the other model-shaped
+workloads (--table, default 2,3,4) are measured in the same run and listed
+under `workloads`, each with its forward and backward launch times and the
+plain in-place stream of the same bytes (libstream_ceiling.so) beside them.
+
 Prints ONE JSON line on stdout (progress goes to stderr) with:
   value        tokens/s of the whole step (fwd + bwd), wall clock over K steps
                (replayed as one HIP graph unless --no-graph)
   roofline     the rotation kernel's achieved HBM bandwidth: algorithmic bytes
                per launch (read + write of q and k) / mean launch duration,
                from HIP events bracketing the K steps (2 launches each) on the
-               launch stream,
-               against MI355X's 8 TB/s; `traffic` is the measured HBM bytes per
-               launch from committed rocprofv3 counters when they were taken
-               on the current kernel source, else null
-  cpu_baseline the fp64 numpy oracle on a bounded sample of the same
-               workload, on the host cores
+               launch stream, against MI355X's 8 TB/s; `traffic` is the
+               measured HBM bytes per launch from committed rocprofv3 counters
+               when they were taken on the current kernel source, else null
+  workloads    per workload: forward and backward us per launch and fraction
+               of 8 TB/s, the stream ceiling of the same traffic, traffic
+  cpu_baseline the fp64 numpy oracle on a bounded sample of the headline
+               workload, on the host cores (threads used, host cores, CPU)
   parity       a fresh batch checked against the oracle in the same run
-Workloads: 1 tiny fp32, 2 Qwen2.5-0.5B-shaped (default), 3 Qwen3-8B-shaped,
-4 Qwen3-32B-shaped, 5 Llama-3.1-8B-shaped 524,288-token context.
+Workloads: 1 tiny fp32, 2 Qwen2.5-0.5B-shaped, 3 Qwen3-8B-shaped,
+4 Qwen3-32B-shaped, 5 Llama-3.1-8B-shaped 524,288-token context (default).
 """
 
 from __future__ import annotations
@@ -32,6 +39,7 @@ import dataclasses
 import concurrent.futures as cf
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -42,12 +50,23 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fused QK-RoPE fwd+bwd tokens/s and achieved HBM GB/s (% of MI355X peak)"
 HBM_PEAK_GBS = 8000.0
-# the sources the rotation kernels are compiled from
 # the rotation kernels' sources and the build script that holds their compile flags
 KERNEL_SRCS = [os.path.join(ROOT, "packed_varlen_rotary_amd", "csrc", n)
                for n in ("rope_qk.hip", "rope_common.h", "rope_sincos.h")] + \
               [os.path.join(ROOT, "packed_varlen_rotary_amd", "build.py")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "rope_qk_kernel_traffic.md")
+# the machine's CPU share for one GPU: the oracle's thread pool stops there
+CPU_SHARE = 16
+# a timed graph holds at least this much kernel time, so that the events'
+# own overhead (a few microseconds) stays under ~0.2% of the region
+MIN_REGION_S = 4e-3
+# plain in-place stream variants timed for the ceiling: (chunks per lane,
+# persistent workgroups or 0 for one tile per workgroup, non-temporal,
+# resident workgroups per compute unit or 0 for as many as fit)
+CEILING_VARIANTS = [(1, 0, 1, 0), (2, 0, 1, 0), (4, 0, 1, 0), (8, 0, 1, 0), (16, 0, 1, 0), (4, 0, 0, 0),
+                    (1, 0, 1, 4), (1, 0, 1, 6), (2, 0, 1, 2), (2, 0, 1, 3), (2, 0, 1, 4), (2, 0, 1, 6),
+                    (4, 0, 1, 1), (4, 0, 1, 2), (4, 0, 1, 3), (8, 0, 1, 1), (8, 0, 1, 2),
+                    (4, 1024, 1, 0), (8, 1024, 1, 0), (16, 1024, 1, 0)]
 
 
 def log(*a):
@@ -78,6 +97,16 @@ def measured_traffic(workload_name: str):
     return None
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle as it stands, on a bounded sample
 # ---------------------------------------------------------------------------
@@ -92,10 +121,11 @@ def cpu_baseline(w, budget_s: float = 12.0, chunk: int = 1024, single_s: float =
 
     import oracle
 
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    host_cores = len(os.sched_getaffinity(0))
+    threads = min(host_cores, CPU_SHARE)
     pos_all = oracle.segment_positions(w.cu_seqlens, w.T)
     rng = np.random.default_rng(0)
-    starts = list(range(0, w.T, chunk))[:cores]
+    starts = list(range(0, w.T, chunk))[:threads]
     inputs = {}
     for s in starts:
         n = min(s + chunk, w.T) - s
@@ -119,7 +149,7 @@ def cpu_baseline(w, budget_s: float = 12.0, chunk: int = 1024, single_s: float =
 
     t0 = time.perf_counter()
     tokens = 0
-    with cf.ThreadPoolExecutor(max_workers=cores) as ex:
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
         while time.perf_counter() - t0 < budget_s:
             tokens += sum(ex.map(one_chunk, starts))
     dt = time.perf_counter() - t0
@@ -131,10 +161,14 @@ def cpu_baseline(w, budget_s: float = 12.0, chunk: int = 1024, single_s: float =
     return {
         "value": tokens / dt,
         "unit": "tokens/s",
-        "cores": cores,
+        "cores": threads,
         "kind": "oracle",
         "sample": f"{tokens} tokens of the workload ({chunk}-token chunks, q and k, fwd and bwd, "
-                  f"positions+fp64 rotation+bf16 rounding; inputs drawn beforehand) in {dt:.1f} s on {cores} threads",
+                  f"positions+fp64 rotation+bf16 rounding; inputs drawn beforehand) in {dt:.1f} s on {threads} threads",
+        "host_cores": host_cores,
+        "threads": threads,
+        "cpu_model": cpu_model(),
+        "thread_cap": f"the pool stops at {CPU_SHARE} threads, the host CPU share one GPU's jobs get",
         "single_thread_value": tokens1 / dt1,
     }
 
@@ -142,6 +176,135 @@ def cpu_baseline(w, budget_s: float = 12.0, chunk: int = 1024, single_s: float =
 # ---------------------------------------------------------------------------
 # GPU timing
 # ---------------------------------------------------------------------------
+
+def resident_sets(w, names, dev, per_set_bytes, max_sets=64):
+    """Enough independent batches (>= 1 GiB together) that each launch reads cold HBM."""
+    import workloads as W
+
+    nsets = max(1, min(max_sets, -(-(1 << 30) // per_set_bytes)))
+    return [W.make_tensors(w, names, device=dev, salt=s) for s in range(nsets)]
+
+
+def timed_us(fn, n, graph, warmup=2, warm_s=0.1, region_s=0.02):
+    """Mean microseconds per call of fn(i), HIP events on the launch stream
+    around R passes of n calls (R passes make up >= region_s), each pass one
+    HIP graph replay (or n launches one by one).  Passes totalling >= warm_s
+    run untimed first, so that the GPU is at its working clocks whatever ran
+    (or did not run) before."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    g = None
+    if graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            fn(0)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+
+    def one_pass():
+        if g is not None:
+            g.replay()
+        else:
+            for i in range(n):
+                fn(i)
+
+    start = time.perf_counter()
+    one_pass()  # upload and first replay
+    torch.cuda.synchronize()
+    per_pass = time.perf_counter() - start
+    while time.perf_counter() - start < warm_s:
+        t = time.perf_counter()
+        one_pass()
+        torch.cuda.synchronize()
+        per_pass = time.perf_counter() - t
+    reps = max(1, math.ceil(region_s / max(per_pass, 1e-6)))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        one_pass()
+    b.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) * 1e3 / (n * reps)
+
+
+def launches_for(nbytes, steps):
+    """Calls per timed region: at least `steps`, and enough for MIN_REGION_S at ~6 TB/s."""
+    return max(steps, min(4000, math.ceil(MIN_REGION_S / (nbytes / 6e12))))
+
+
+def stream_ceiling(nbytes, dev, steps, graph=True, variants=CEILING_VARIANTS):
+    """The plain in-place 16-byte stream (libstream_ceiling.so) over buffers of
+    nbytes // 2 bytes (read + write = nbytes of traffic), rotating over
+    >= 1 GiB, each variant timed like the rotation; returns the fastest."""
+    import torch
+
+    from packed_varlen_rotary_amd import stream_ceiling as SC
+
+    half = nbytes // 2
+    nb = max(1, min(64, -(-(1 << 30) // half)))
+    bufs = [torch.zeros(half, dtype=torch.uint8, device=dev) for _ in range(nb)]
+    n = launches_for(nbytes, steps)
+    rows = []
+    for tpl, groups, nt, cap in variants:
+        try:
+            us = timed_us(lambda i: SC.stream_ceiling_launch(bufs[i % nb], tpl, groups, nt, cap), n, graph)
+        except RuntimeError as e:  # a launch configuration this part does not take
+            log(f"[bench] stream {tpl} chunks/lane, groups {groups}, per CU {cap}: {e}")
+            torch.cuda.synchronize()
+            continue
+        gbs = nbytes / (us * 1e-6) / 1e9
+        rows.append({"chunks_per_lane": tpl, "groups": groups, "nontemporal": bool(nt), "groups_per_cu": cap,
+                     "us": us, "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS})
+    del bufs
+    torch.cuda.empty_cache()
+    best = min(rows, key=lambda r: r["us"])
+    keys = ("chunks_per_lane", "groups", "nontemporal", "groups_per_cu")
+    return {"us": best["us"], "frac": best["frac"], "variant": {k: best[k] for k in keys}, "launches_timed": n,
+            "variants": rows}
+
+
+def measure_workload(cfg, dev, steps, graph, with_ceiling=True):
+    """Forward and backward launch times of one workload (graph-replayed
+    launches over resident batches), its stream ceiling and its traffic."""
+    import torch
+
+    import packed_varlen_rotary_amd as P
+    import workloads as W
+
+    w = W.make_workload(cfg)
+    cu = torch.as_tensor(w.cu_seqlens, device=dev)
+    sets = resident_sets(w, ("q", "k"), dev, w.bytes_per_pass // 2)
+    ns = len(sets)
+    n = launches_for(w.bytes_per_pass, steps)
+    fwd_us = timed_us(lambda i: P.rope_qk_fwd(sets[i % ns]["q"], sets[i % ns]["k"], cu, w.theta), n, graph)
+    bwd_us = timed_us(lambda i: P.rope_qk_bwd(sets[i % ns]["q"], sets[i % ns]["k"], cu, w.theta), n, graph)
+    del sets
+    torch.cuda.empty_cache()
+    gbs = lambda us: w.bytes_per_pass / (us * 1e-6) / 1e9  # noqa: E731
+    row = {"workload": w.name, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "nseq": w.nseq,
+           "bytes_per_launch": w.bytes_per_pass, "launches_timed": n, "resident_batches": ns,
+           "fwd_us": fwd_us, "bwd_us": bwd_us, "fwd_frac": gbs(fwd_us) / HBM_PEAK_GBS,
+           "bwd_frac": gbs(bwd_us) / HBM_PEAK_GBS, "traffic": measured_traffic(w.name)}
+    if with_ceiling:
+        c = stream_ceiling(w.bytes_per_pass, dev, steps, graph)
+        row["stream_ceiling"] = {k: c[k] for k in ("us", "frac", "variant")}
+        row["fwd_of_ceiling"] = c["us"] / fwd_us
+        row["bwd_of_ceiling"] = c["us"] / bwd_us
+    log(f"[bench] {w.name}: fwd {fwd_us:.2f} us ({100 * row['fwd_frac']:.1f}%), bwd {bwd_us:.2f} us "
+        f"({100 * row['bwd_frac']:.1f}%)" + (f"; stream ceiling {row['stream_ceiling']['us']:.2f} us "
+                                              f"({100 * row['stream_ceiling']['frac']:.1f}%)" if with_ceiling else ""))
+    return row
+
 
 def run_gpu(args):
     import torch
@@ -156,9 +319,9 @@ def run_gpu(args):
     torch.cuda.set_device(dev)
     cu = torch.as_tensor(w.cu_seqlens, device=dev)
     set_bytes = w.bytes_per_pass  # q, k, dq, dk of one batch: (Hq+Hkv)*D*s*T bytes per pair
-    nsets = max(1, min(64, -(-(1 << 30) // set_bytes)))
+    sets = resident_sets(w, ("q", "k", "dq", "dk"), dev, set_bytes)
+    nsets = len(sets)
     log(f"[bench] {w.name}: {nsets} resident batches of {set_bytes / 2**20:.1f} MiB")
-    sets = [W.make_tensors(w, ("q", "k", "dq", "dk"), device=dev, salt=s) for s in range(nsets)]
 
     def step(i):
         b = sets[i % nsets]
@@ -201,55 +364,49 @@ def run_gpu(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     region_ms = t_start.elapsed_time(t_end)
+    del graph
 
-    # the forward and the backward on their own (K launches each, same replay)
-    def split_us(fn):
-        g = None
-        if args.graph:
-            side = torch.cuda.Stream(dev)
-            side.wait_stream(torch.cuda.current_stream(dev))
-            with torch.cuda.stream(side):
-                fn(0)
-            torch.cuda.current_stream(dev).wait_stream(side)
-            torch.cuda.synchronize()
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(args.steps):
-                    fn(i)
-            g.replay()
-            torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        if g is not None:
-            g.replay()
-        else:
-            for i in range(args.steps):
-                fn(i)
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / args.steps
-
-    fwd_us = split_us(lambda i: P.rope_qk_fwd(sets[i % nsets]["q"], sets[i % nsets]["k"], cu, w.theta))
-    bwd_us = split_us(lambda i: P.rope_qk_bwd(sets[i % nsets]["dq"], sets[i % nsets]["dk"], cu, w.theta))
-    log(f"[bench] {w.name}: forward {fwd_us:.2f} us, backward {bwd_us:.2f} us per launch")
+    # the forward and the backward on their own (same replay, enough launches
+    # for a region of MIN_REGION_S)
+    n = launches_for(w.bytes_per_pass, args.steps)
+    fwd_us = timed_us(lambda i: P.rope_qk_fwd(sets[i % nsets]["q"], sets[i % nsets]["k"], cu, w.theta), n,
+                      args.graph)
+    bwd_us = timed_us(lambda i: P.rope_qk_bwd(sets[i % nsets]["dq"], sets[i % nsets]["dk"], cu, w.theta), n,
+                      args.graph)
+    log(f"[bench] {w.name}: forward {fwd_us:.2f} us, backward {bwd_us:.2f} us per launch ({n} launches each)")
+    del sets
+    torch.cuda.empty_cache()
 
     # parity of a fresh batch in the same run
     parity = check_parity(w, cu, dev)
+    torch.cuda.empty_cache()
 
     launch_ms = region_ms / (2 * args.steps)  # HIP events around the K steps, on the launch stream
     ms_per_step = wall * 1e3 / args.steps
+    gbs = lambda us: w.bytes_per_pass / (us * 1e-6) / 1e9  # noqa: E731
+    row = {"workload": w.name, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "nseq": w.nseq,
+           "bytes_per_launch": w.bytes_per_pass, "launches_timed": n, "resident_batches": nsets,
+           "fwd_us": fwd_us, "bwd_us": bwd_us, "fwd_frac": gbs(fwd_us) / HBM_PEAK_GBS,
+           "bwd_frac": gbs(bwd_us) / HBM_PEAK_GBS, "traffic": measured_traffic(w.name)}
+    if args.ceiling:
+        c = stream_ceiling(w.bytes_per_pass, dev, args.steps, args.graph)
+        row["stream_ceiling"] = {k: c[k] for k in ("us", "frac", "variant")}
+        row["fwd_of_ceiling"] = c["us"] / fwd_us
+        row["bwd_of_ceiling"] = c["us"] / bwd_us
+        log(f"[bench] {w.name}: stream ceiling {c['us']:.2f} us ({100 * c['frac']:.1f}%), variant {c['variant']}")
     return w, {
         "ms_per_step": ms_per_step,
         "tokens_per_s": w.T / (ms_per_step * 1e-3),
         "event_ms_per_step": region_ms / args.steps,
         "launch_ms": launch_ms,
         "gbs": w.bytes_per_pass / (launch_ms * 1e-3) / 1e9,
-        "traffic": measured_traffic(w.name),
+        "traffic": row["traffic"],
         "fwd_us": fwd_us,
         "bwd_us": bwd_us,
         "parity": parity,
         "resident_batches": nsets,
         "device": torch.cuda.get_device_name(dev),
+        "row": row,
     }
 
 
@@ -611,6 +768,27 @@ def run_variants(args):
                       "peak": HBM_PEAK_GBS, "cases": res}))
 
 
+def run_stream_ceiling(args):
+    """Every plain in-place stream variant with one launch's HBM traffic of
+    --workload (read + write of q and k), timed like the rotation."""
+    import torch
+
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    w = W.make_workload(args.workload)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    c = stream_ceiling(w.bytes_per_pass, dev, args.steps, args.graph)
+    for v in c["variants"]:
+        log(f"[bench] stream {v['chunks_per_lane']} chunks/lane, groups {v['groups']}, nt {v['nontemporal']}, "
+            f"per CU {v['groups_per_cu']}: {v['us']:.2f} us ({100 * v['frac']:.1f}%)")
+    print(json.dumps({"metric": "plain in-place 16-byte stream with one launch's HBM traffic", "workload": w.name,
+                      "traffic_bytes": w.bytes_per_pass, "launches_timed": c["launches_timed"], "best_us": c["us"],
+                      "best_frac": c["frac"], "best_variant": c["variant"], "variants": c["variants"]}))
+
+
 def _timed(fn):
     t0 = time.perf_counter()
     fn()
@@ -620,9 +798,16 @@ def _timed(fn):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5],
+                    help="the headline workload (default 5: the 524,288-token Llama-3.1-8B-shaped context)")
+    ap.add_argument("--table", default="2,3,4",
+                    help="other workloads measured in the same run (comma-separated; empty: none)")
+    ap.add_argument("--no-ceiling", dest="ceiling", action="store_false",
+                    help="skip the plain-stream ceiling beside each workload")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="only time every plain in-place stream variant with one launch's traffic of --workload")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="launch the timed steps one by one on the stream instead of replaying a HIP graph")
@@ -665,10 +850,19 @@ def main():
     if args.variants:
         run_variants(args)
         return
+    if args.stream_ceiling:
+        run_stream_ceiling(args)
+        return
 
     w, r = run_gpu(args)
     log(f"[bench] gpu done: {r['ms_per_step']:.4f} ms/step, mean launch {r['launch_ms'] * 1e3:.2f} us, "
         f"{r['gbs']:.0f} GB/s, parity {r['parity']}")
+    import torch
+
+    rows = [r["row"]]
+    for cfg in [int(c) for c in args.table.split(",") if c.strip()]:
+        if cfg != args.workload:
+            rows.append(measure_workload(cfg, torch.device("cuda", 0), args.steps, args.graph, args.ceiling))
     cpu = None
     if args.workload and not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
@@ -714,6 +908,7 @@ def main():
             "event_ms_per_step": r["event_ms_per_step"],
             "launch": "hip graph of the K steps" if args.graph else "stream launches",
         },
+        "workloads": rows,
         "parity": r["parity"],
         "device": r["device"],
     }

@@ -1,4 +1,5 @@
-"""Build librope_qk.so (the HIP kernels and their C ABI) in-tree for gfx950.
+"""Build librope_qk.so (the HIP kernels and their C ABI) and libstream_ceiling.so
+(the plain stream the bench measures against) in-tree for gfx950.
 
     python -m packed_varlen_rotary_amd.build
 
@@ -16,6 +17,10 @@ ROOT = os.path.dirname(PKG)
 SRCS = [os.path.join(PKG, "csrc", n) for n in ("rope_qk.hip", "rope_qk_norm.hip", "rope_pack.cpp")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librope_qk.so")
+# the plain in-place stream that the bench measures the rotation against
+# (include/stream_ceiling.h): a measurement aid in a library of its own
+CEILING_SRCS = [os.path.join(PKG, "csrc", "stream_ceiling.hip")]
+CEILING_LIB = os.path.join(PKG, "libstream_ceiling.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -36,8 +41,8 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
-    cmd = [HIPCC, *FLAGS, *extra_flags, "-I", INCLUDE, "-o", out + ".tmp", *SRCS]
+def build(verbose: bool = False, extra_flags=(), out: str = LIB, srcs=None) -> str:
+    cmd = [HIPCC, *FLAGS, *extra_flags, "-I", INCLUDE, "-o", out + ".tmp", *(SRCS if srcs is None else srcs)]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,6 +56,11 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
     return out
 
 
+def build_all(verbose: bool = False) -> list:
+    """Both libraries: the rotation library and the stream-ceiling probe."""
+    return [build(verbose), build(verbose, out=CEILING_LIB, srcs=CEILING_SRCS)]
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print("\n".join(build_all(verbose=True)))
     sys.exit(0)
