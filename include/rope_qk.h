@@ -43,8 +43,12 @@
  * allocates nothing, and its only state is the static scratch array of
  * rope_qk_norm_bwd_noalloc (part of its code object).  q is [T, Hq, D] and k is [T, Hkv, D] with
  * element strides (stride_t, stride_h) and a unit stride along D; the two
- * tensors must not overlap each other and each must not overlap itself
- * (checked from the strides; q/k views into one fused QKV buffer are fine).
+ * tensors must not overlap each other and each must not overlap itself.
+ * Both are checked from the pointers and strides (ROPE_QK_ERR_LAYOUT): q and
+ * k pass when their byte ranges do not meet, or when they share one token
+ * stride, each token's rows fit in it, and k's rows of a token lie in a gap
+ * of q's (views into one fused QKV buffer); any other meeting of the two
+ * ranges is refused.
  * Calls are asynchronous on `stream` (a hipStream_t; NULL = the legacy default
  * stream of the current device) and never synchronise with the host:
  * cu_seqlens is read only on the device.  cu_seqlens must be int32, with
@@ -79,7 +83,7 @@ extern "C" {
 #define ROPE_QK_ERR_ALIGN -4     /* base, stride*elem or (D/2)*elem not a multiple of 16 bytes */
 #define ROPE_QK_ERR_THETA -5     /* theta not finite or <= 0 */
 #define ROPE_QK_ERR_LAUNCH -6    /* the HIP launch itself failed */
-#define ROPE_QK_ERR_LAYOUT -7    /* negative strides, or a tensor whose rows overlap */
+#define ROPE_QK_ERR_LAYOUT -7    /* negative strides, a tensor whose rows overlap, or tensors that share memory */
 #define ROPE_QK_ERR_OPTION -8    /* a field of rope_qk_options out of range (or eps, for the norm calls) */
 #define ROPE_QK_ERR_WORKSPACE -9 /* workspace NULL or smaller than rope_qk_norm_bwd_workspace_bytes */
 #define ROPE_QK_ERR_SCRATCH -10  /* rope_qk_norm_bwd_noalloc: the call needs more than its static scratch */
@@ -216,8 +220,9 @@ int rope_qk_bwd_opt(void* dq, void* dk, const int32_t* cu_seqlens, int64_t nseq,
  *
  *   q, k           inputs [T, Hq, D], [T, Hkv, D] (device; NULL only without heads)
  *   q_out, k_out   outputs of the same shapes; each may be exactly its input
- *                  (same pointer and strides: in place) or must not overlap
- *                  any input
+ *                  (same pointer and strides: in place) or must share no
+ *                  memory with any other tensor of the call (checked like q
+ *                  against k in rope_qk_fwd: ROPE_QK_ERR_LAYOUT)
  *   q_weight, k_weight
  *                  device float32 [D], 16-byte aligned (NULL only without heads)
  *   eps            finite, > 0 (else ROPE_QK_ERR_OPTION; Qwen3 uses 1e-6)
@@ -251,7 +256,8 @@ int64_t rope_qk_norm_bwd_workspace_bytes(int64_t T, int64_t Hq, int64_t Hkv, int
  * Backward of rope_qk_norm_fwd.  Inputs: dq_out, dk_out (the gradients of the
  * forward's outputs) and q, k (the forward's INPUTS, which the caller keeps);
  * outputs: dq, dk (gradients of the inputs; each may be exactly its dq_out /
- * dk_out, i.e. in place, or must not overlap any input) and dq_weight,
+ * dk_out, i.e. in place, or must share no memory with any other tensor of
+ * the call, ROPE_QK_ERR_LAYOUT otherwise) and dq_weight,
  * dk_weight (device float32 [D], 16-byte aligned, overwritten with the
  * gradient of q_weight / k_weight summed over every normalised head; NULL
  * only without heads).  With n, r as in the forward and dn = rope^T(dy) (the
@@ -308,14 +314,54 @@ int rope_qk_norm_bwd_noalloc(const void* dq_out, const void* dk_out, const void*
                              const rope_qk_options* options, void* stream);
 
 /*
- * The positions the rotation kernels use, for inspection: writes, for every
- * t < T, pos(t) as defined above, or -1 for tokens outside
- * [cu_seqlens[0], cu_seqlens[nseq]) (no pos_offset).  pos_out: device int32[T], caller-owned.  Asynchronous on
- * `stream`.  Returns ROPE_QK_OK, ROPE_QK_ERR_NULL, ROPE_QK_ERR_SHAPE or
- * ROPE_QK_ERR_LAUNCH.
+ * Per-token positions, for inspection: writes, for every t < T, pos(t) as
+ * defined above, or -1 for tokens outside [cu_seqlens[0], cu_seqlens[nseq])
+ * (no pos_offset).  Computed by the rotation kernels' own tile code (the
+ * search of cu_seqlens for a tile's first token and the scan of the sequence
+ * starts inside it), on tiles of 64 whole tokens.  pos_out: device
+ * int32[T], caller-owned.  Asynchronous on `stream`.  Returns ROPE_QK_OK,
+ * ROPE_QK_ERR_NULL, ROPE_QK_ERR_SHAPE or ROPE_QK_ERR_LAUNCH.
  */
 int rope_qk_positions(const int32_t* cu_seqlens, int64_t nseq, int64_t T, int32_t* pos_out,
                       void* stream);
+
+/*
+ * Test hook: the positions each tile of a rotation call computes, in that
+ * call's own tile decomposition and through the rotation kernels' own
+ * geometry and position code (the auto-packing paragraph of the Unsloth
+ * article: length metadata keeps packed samples apart).  The call is
+ * described by cu_seqlens, nseq, T, Hq, Hkv, D, dtype and options as for
+ * rope_qk_fwd_opt (q, k, their strides and theta play no part in it).
+ *
+ *   out       device int32[out_len], caller-owned, or NULL to ask only for
+ *             the geometry; row i (row_len entries from out + i * row_len)
+ *             receives tile i's first token, then the position of each token
+ *             the tile touches, in order (-1: a token in no sequence); the
+ *             rest of the row is not written
+ *   ntiles, row_len
+ *             host int64 outputs: the call's tile count, and 1 + the most
+ *             tokens one tile touches (0 and 0 when the call launches nothing)
+ *
+ * Errors as rope_qk_fwd_opt (shape, dtype, options, ROPE_QK_ERR_NULL for a
+ * NULL cu_seqlens, ntiles or row_len), and ROPE_QK_ERR_SHAPE when out_len <
+ * ntiles * row_len.  One launch on `stream` when out is not NULL.
+ */
+int rope_qk_tile_positions(const int32_t* cu_seqlens, int64_t nseq, int64_t T, int64_t Hq, int64_t Hkv,
+                           int64_t D, int dtype, const rope_qk_options* options, int32_t* out,
+                           int64_t out_len, int64_t* ntiles, int64_t* row_len, void* stream);
+
+/*
+ * The same hook for the fused RMSNorm + rotation: backward == 0 runs the
+ * forward's tiles (one per workgroup, each searching cu_seqlens), backward
+ * != 0 the backward's runs of tiles with the sequence cursor each workgroup
+ * carries from tile to tile.  Arguments, output rows and errors as
+ * rope_qk_tile_positions, with the norm's shape limits; nseq == 0 is
+ * allowed (every position -1).
+ */
+int rope_qk_norm_tile_positions(const int32_t* cu_seqlens, int64_t nseq, int64_t T, int64_t Hq, int64_t Hkv,
+                                int64_t D, int dtype, const rope_qk_options* options, int backward,
+                                int32_t* out, int64_t out_len, int64_t* ntiles, int64_t* row_len,
+                                void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* rope_qk_strerror(int status);

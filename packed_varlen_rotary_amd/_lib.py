@@ -29,7 +29,7 @@ ROPE_QK_FREQ_FP32 = 1
 # names exported by include/rope_qk.h
 EXPORTS = ("rope_qk_fwd", "rope_qk_bwd", "rope_qk_fwd_opt", "rope_qk_bwd_opt", "rope_qk_norm_fwd",
            "rope_qk_norm_bwd", "rope_qk_norm_bwd_workspace_bytes", "rope_qk_norm_bwd_noalloc", "rope_qk_positions",
-           "rope_qk_strerror",
+           "rope_qk_tile_positions", "rope_qk_norm_tile_positions", "rope_qk_strerror",
            "rope_pack_bfd", "rope_pack_cu_seqlens", "rope_pack_cache_create", "rope_pack_cache_get",
            "rope_pack_cache_stats", "rope_pack_cache_destroy")
 
@@ -151,6 +151,12 @@ def load():
         lib.rope_pack_cache_destroy.restype = None
         lib.rope_qk_positions.argtypes = [vp, i64, i64, vp, vp]
         lib.rope_qk_positions.restype = ctypes.c_int
+        lib.rope_qk_tile_positions.argtypes = [vp, i64, i64, i64, i64, i64, ctypes.c_int, optp, vp, i64,
+                                               ctypes.POINTER(i64), ctypes.POINTER(i64), vp]
+        lib.rope_qk_tile_positions.restype = ctypes.c_int
+        lib.rope_qk_norm_tile_positions.argtypes = [vp, i64, i64, i64, i64, i64, ctypes.c_int, optp, ctypes.c_int,
+                                                    vp, i64, ctypes.POINTER(i64), ctypes.POINTER(i64), vp]
+        lib.rope_qk_norm_tile_positions.restype = ctypes.c_int
         lib.rope_qk_strerror.argtypes = [ctypes.c_int]
         lib.rope_qk_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -264,7 +270,8 @@ def rope_qk_bwd_opt(dq, dk, cu_seqlens, theta: float, options=None, stream=None)
 
 
 def rope_qk_positions(cu_seqlens, T: int, out=None, stream=None):
-    """Per-token positions the kernels use (int32 [T], -1 outside every sequence)."""
+    """Per-token positions (int32 [T], -1 outside every sequence), computed by
+    the rotation kernels' own tile code on tiles of 64 whole tokens."""
     import torch
 
     lib = load()
@@ -281,6 +288,45 @@ def rope_qk_positions(cu_seqlens, T: int, out=None, stream=None):
         )
     _check(status)
     return out
+
+
+TILE_ROW_UNWRITTEN = -(2 ** 31)  # what the hooks' output rows hold where a tile wrote nothing
+
+
+def _tile_positions(entry, cu_seqlens, T, Hq, Hkv, D, dtype_code, options, stream, extra=()):
+    import torch
+
+    lib = load()
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor")
+    nt, rl = ctypes.c_int64(0), ctypes.c_int64(0)
+    opts = ctypes.byref(options) if options is not None else None
+    head = [ctypes.c_void_p(cu_seqlens.data_ptr()), cu_seqlens.numel() - 1, int(T), int(Hq), int(Hkv), int(D),
+            int(dtype_code), opts, *extra]
+    _check(getattr(lib, entry)(*head, None, 0, ctypes.byref(nt), ctypes.byref(rl), None))
+    out = torch.full((max(nt.value, 0), max(rl.value, 0)), TILE_ROW_UNWRITTEN, dtype=torch.int32,
+                     device=cu_seqlens.device)
+    if out.numel():
+        with torch.cuda.device(cu_seqlens.device):
+            _check(getattr(lib, entry)(*head, ctypes.c_void_p(out.data_ptr()), out.numel(), ctypes.byref(nt),
+                                       ctypes.byref(rl), _stream_ptr(cu_seqlens.device, stream)))
+    return out
+
+
+def rope_qk_tile_positions(cu_seqlens, T: int, Hq: int, Hkv: int, D: int, dtype_code: int, options=None,
+                           stream=None):
+    """Test hook: [ntiles, row_len] int32 device tensor; row i = tile i's first
+    token, then the positions of the tokens it touches (TILE_ROW_UNWRITTEN
+    after them), computed by the rotation kernels' own tile code for a call
+    of these sizes and options (a RopeQKOptions or None)."""
+    return _tile_positions("rope_qk_tile_positions", cu_seqlens, T, Hq, Hkv, D, dtype_code, options, stream)
+
+
+def rope_qk_norm_tile_positions(cu_seqlens, T: int, Hq: int, Hkv: int, D: int, dtype_code: int, backward: bool,
+                                options=None, stream=None):
+    """The same hook for the fused RMSNorm + rotation's forward or backward tiles."""
+    return _tile_positions("rope_qk_norm_tile_positions", cu_seqlens, T, Hq, Hkv, D, dtype_code, options, stream,
+                           extra=(1 if backward else 0,))
 
 
 # ---------------------------------------------------------------------------

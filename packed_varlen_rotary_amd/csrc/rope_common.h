@@ -12,6 +12,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "rope_layout.h"
 #include "rope_qk.h"
 #include "rope_sincos.h"
 
@@ -155,17 +156,6 @@ __device__ __forceinline__ uint32_t pack16_exact(double lo, double hi) {
 }
 
 // ---- host side ----
-
-// Rows of D elements at t * st + h * sh (t < T, h < H), all strides >= 0: do any two overlap?
-bool rows_overlap(int64_t T, int64_t H, int64_t D, int64_t st, int64_t sh) {
-  if (T <= 1 && H <= 1) return false;
-  if (T <= 1) return sh < D;
-  if (H <= 1) return st < D;
-  const int64_t s_small = st < sh ? st : sh, n_small = st < sh ? T : H;
-  const int64_t s_big = st < sh ? sh : st;
-  if (s_small < D) return true;
-  return s_big / s_small < n_small;  // s_big < n_small * s_small, without overflow
-}
 
 // Frequencies of a head of size r (pairs i < r/2), optionally with the Llama
 // 3.1 rescaling (the rule is documented with rope_qk_options in rope_qk.h).

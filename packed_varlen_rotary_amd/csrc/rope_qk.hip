@@ -214,8 +214,12 @@ __device__ __forceinline__ void rotate_pairs_f32(const u32x4& own, const double2
 // kG away.
 // kG = kInterleaved: interleaved pairing; a task is one 16-byte chunk of whole
 // pairs, consecutive lanes on consecutive chunks.
-template <int kDtype, int kG, int kTPT>
-__device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, int32_t* s_pos, double2* s_cs) {
+// kPosOnly (the positions test hook): run the tile's geometry and position
+// code only, and write the tile's first token and its tokens' positions to
+// pos_out[0 .. ntok] instead of loading, rotating and storing anything.
+template <int kDtype, int kG, int kTPT, bool kPosOnly = false>
+__device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, int32_t* s_pos, double2* s_cs,
+                                          int32_t* pos_out = nullptr) {
   constexpr bool k16 = kDtype != ROPE_QK_FP32;            // bf16 or fp16 storage
   constexpr int kVec = k16 ? 8 : 4;                        // elements per 16 bytes
   constexpr int kPPC = kG == kInterleaved ? kVec / 2 : kVec;  // table pairs per chunk
@@ -258,6 +262,7 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
     gchar* ptr[kTPT];
     int tt_of[kTPT], c_of[kTPT];
     bool act[kTPT], first[kTPT];
+    if constexpr (!kPosOnly) {
     // Unit tiles whose token task count divides 256 (e.g. 16 heads at D = 64):
     // a lane's tasks are tok_step tokens apart at the same head and chunk, so
     // only the first address needs the general computation.
@@ -301,6 +306,7 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
       a[u] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4*>(ptr[u]));
       if constexpr (kG == 0) b[u] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4*>(ptr[u] + p.half_bytes));
     }
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     // 3. positions (scalar loads, not ordered behind the data) and the table
@@ -326,6 +332,11 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
       const int32_t pos = pos64 <= INT32_MAX ? static_cast<int32_t>(pos64) : -1;
       if (e < nent) {
         if (i_e[v] == 0) s_pos[tt_e[v]] = pos;
+        if constexpr (kPosOnly) {
+          if (i_e[v] == 0) pos_out[1 + tt_e[v]] = pos;
+          if (e == 0) pos_out[0] = static_cast<int32_t>(t0);
+          continue;
+        }
         if (pos >= 0) {
           double sn, cs;
           // float32 convention: float32 position times float32 frequency, one rounding
@@ -336,6 +347,7 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
         }
       }
     }
+    if constexpr (kPosOnly) return;
     __syncthreads();
 
     // 4. rotate every task, then store them all; tokens outside every
@@ -394,37 +406,85 @@ void rope_qk_kernel(const RopeParams p) {
   if (tile < p.ntiles) rope_tile<kDtype, kG, kTPT>(p, tile, s_pos, s_cs);
 }
 
-__global__ __launch_bounds__(kThreads) void rope_positions_kernel(const int32_t* __restrict__ cu_seqlens,
-                                                                  int32_t nseq, int64_t T,
-                                                                  int32_t* __restrict__ out) {
-  const cu_ptr cu = (cu_ptr)cu_seqlens;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  for (int64_t t = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; t < T; t += stride)
-    out[t] = token_position(cu, nseq, t);
+// The positions test hook: one tile per workgroup, in the geometry of the
+// call it was prepared for, through the rotation tile's own position code;
+// row `tile` of out receives the tile's first token and the positions of the
+// tokens it touches.
+__global__ __launch_bounds__(kThreads) void rope_tile_positions_kernel(const RopeParams p, int32_t* out,
+                                                                       int64_t row_len) {
+  __shared__ int32_t s_pos[kMaxTileTokens];
+  const uint32_t tile = blockIdx.y * gridDim.x + blockIdx.x;
+  if (tile < p.ntiles)
+    rope_tile<ROPE_QK_BF16, 0, kPairTasks, true>(p, tile, s_pos, nullptr, out + static_cast<int64_t>(tile) * row_len);
 }
 
-int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, int64_t Hq, int64_t Hkv, int64_t D,
-                int64_t q_st, int64_t q_sh, int64_t k_st, int64_t k_sh, double theta, int dtype,
-                const rope_qk_options* options, void* stream, double sign) {
+// Per-token positions (rope_qk_positions): the same position code on tiles of
+// kPositionTileTokens whole tokens (one task per token), each tile writing
+// its positions at out[t0 ...] through a staging row in LDS.
+constexpr int kPositionTileTokens = kMaxTileTokens;
+
+__global__ __launch_bounds__(kThreads) void rope_token_positions_kernel(const RopeParams p, int32_t* out) {
+  __shared__ int32_t s_pos[kMaxTileTokens];
+  __shared__ int32_t s_row[1 + kPositionTileTokens];
+  const uint32_t tile = blockIdx.y * gridDim.x + blockIdx.x;
+  if (tile >= p.ntiles) return;
+  const int64_t t0 = static_cast<int64_t>(tile) * kPositionTileTokens;  // tiles of whole tokens
+  const int64_t t = t0 + threadIdx.x;
+  if (p.nseq == 0) {  // no sequence: every token is outside
+    if (threadIdx.x < kPositionTileTokens && t < p.T) out[t] = -1;
+    return;
+  }
+  rope_tile<ROPE_QK_BF16, 0, kPairTasks, true>(p, tile, s_pos, nullptr, s_row);
+  __syncthreads();
+  if (threadIdx.x < kPositionTileTokens && t < p.T) out[t] = s_row[1 + threadIdx.x];
+}
+
+// A rotation call after its checks: the kernel parameters, the kernel and its
+// launch shape (fn == nullptr: nothing to launch), and the most tokens one
+// tile touches.
+struct RopeLaunch {
+  RopeParams p;
+  const void* fn;
+  dim3 grid;
+  size_t lds;
+  int64_t span;
+};
+
+// Checks and geometry of a rotation call.  With tensors == false (the
+// positions hook) q, k and their strides are not looked at.
+int prepare_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, int64_t Hq, int64_t Hkv, int64_t D,
+                 int64_t q_st, int64_t q_sh, int64_t k_st, int64_t k_sh, double theta, int dtype,
+                 const rope_qk_options* options, double sign, bool tensors, RopeLaunch* L) {
+  L->fn = nullptr;
   const rope_qk_options o = options ? *options : rope_qk_options{};
   const int status = check_call(dtype, nseq, T, Hq, Hkv, D, theta, o);
   if (status != ROPE_QK_OK) return status;
   const int64_t r = o.rotary_dim == 0 ? D : o.rotary_dim;  // elements of each head that are rotated
   if (T == 0 || nseq == 0 || Hq + Hkv == 0) return ROPE_QK_OK;
-  if (cu == nullptr || (Hq > 0 && q == nullptr) || (Hkv > 0 && k == nullptr)) return ROPE_QK_ERR_NULL;
-  if ((Hq > 0 && (q_st < 0 || q_sh < 0 || rows_overlap(T, Hq, D, q_st, q_sh))) ||
-      (Hkv > 0 && (k_st < 0 || k_sh < 0 || rows_overlap(T, Hkv, D, k_st, k_sh))))
-    return ROPE_QK_ERR_LAYOUT;
-
   const int64_t esz = dtype == ROPE_QK_FP32 ? 4 : 2;
+  if (cu == nullptr) return ROPE_QK_ERR_NULL;
+  if (tensors) {
+    if ((Hq > 0 && q == nullptr) || (Hkv > 0 && k == nullptr)) return ROPE_QK_ERR_NULL;
+    if ((Hq > 0 && (q_st < 0 || q_sh < 0 || rows_overlap(T, Hq, D, q_st, q_sh))) ||
+        (Hkv > 0 && (k_st < 0 || k_sh < 0 || rows_overlap(T, Hkv, D, k_st, k_sh))))
+      return ROPE_QK_ERR_LAYOUT;
+    // q and k are rotated by one launch: they must share no byte (the
+    // strides are at most 2^40 bytes here, so the byte strides fit int64)
+    if (Hq > 0 && Hkv > 0 &&
+        !rows_disjoint(q, Hq, q_st * esz, q_sh * esz, k, Hkv, k_st * esz, k_sh * esz, T, D * esz))
+      return ROPE_QK_ERR_LAYOUT;
+  }
+
   const bool interleaved = o.pairing == ROPE_QK_PAIR_INTERLEAVED;
   const int64_t half = r / 2;  // rotated pairs per head
   // 16-byte chunks holding the first elements of pairs: half a rotated row, or all of it when interleaved
   if (((interleaved ? r : half) * esz) % 16) return ROPE_QK_ERR_ALIGN;
-  if (Hq > 0 && ((reinterpret_cast<uintptr_t>(q) % 16) || (q_st * esz) % 16 || (q_sh * esz) % 16))
-    return ROPE_QK_ERR_ALIGN;
-  if (Hkv > 0 && ((reinterpret_cast<uintptr_t>(k) % 16) || (k_st * esz) % 16 || (k_sh * esz) % 16))
-    return ROPE_QK_ERR_ALIGN;
+  if (tensors) {
+    if (Hq > 0 && ((reinterpret_cast<uintptr_t>(q) % 16) || (q_st * esz) % 16 || (q_sh * esz) % 16))
+      return ROPE_QK_ERR_ALIGN;
+    if (Hkv > 0 && ((reinterpret_cast<uintptr_t>(k) % 16) || (k_st * esz) % 16 || (k_sh * esz) % 16))
+      return ROPE_QK_ERR_ALIGN;
+  }
 
   const int64_t chunks = (interleaved ? r : half) * esz / 16;
   // rotate_half with half rows of 1, 2 or 4 chunks: unit tiles (one chunk per
@@ -452,7 +512,7 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
   const int64_t ntiles = (T * tasks_per_tok + tile_tasks - 1) / tile_tasks;
   if (ntiles > INT32_MAX) return ROPE_QK_ERR_SHAPE;
 
-  RopeParams p;
+  RopeParams& p = L->p;
   p.q = static_cast<char*>(q);
   p.k = static_cast<char*>(k);
   p.cu = cu;
@@ -488,9 +548,10 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
     if (lds < pad) lds = pad;
   }
   const int64_t gx = ntiles < kGridX ? ntiles : kGridX;
-  const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>((ntiles + gx - 1) / gx));
+  L->grid = dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>((ntiles + gx - 1) / gx));
+  L->lds = lds;
+  L->span = span;
 
-  const void* fn;
 #define ROPE_FN(DT, G, TPT) reinterpret_cast<const void*>(&rope_qk_kernel<DT, G, TPT>)
 #define ROPE_PICK(DT, UNIT)                                                                    \
   (interleaved   ? (lane_tasks == kUnitTasks ? ROPE_FN(DT, kInterleaved, kUnitTasks)           \
@@ -499,13 +560,23 @@ int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, in
    : unit_g == 2 ? ROPE_FN(DT, 2, UNIT)                                                         \
    : unit_g == 4 ? ROPE_FN(DT, 4, UNIT)                                                         \
                  : ROPE_FN(DT, 0, kPairTasks))
-  fn = dtype == ROPE_QK_BF16   ? ROPE_PICK(ROPE_QK_BF16, kUnitTasks)
-       : dtype == ROPE_QK_FP16 ? ROPE_PICK(ROPE_QK_FP16, kUnitTasks)
-                               : ROPE_PICK(ROPE_QK_FP32, kLongRowTasks);
+  L->fn = dtype == ROPE_QK_BF16   ? ROPE_PICK(ROPE_QK_BF16, kUnitTasks)
+          : dtype == ROPE_QK_FP16 ? ROPE_PICK(ROPE_QK_FP16, kUnitTasks)
+                                  : ROPE_PICK(ROPE_QK_FP32, kLongRowTasks);
 #undef ROPE_PICK
 #undef ROPE_FN
-  void* args[] = {&p};
-  const hipError_t err = hipLaunchKernel(fn, grid, dim3(kThreads), args, lds, static_cast<hipStream_t>(stream));
+  return ROPE_QK_OK;
+}
+
+int launch_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, int64_t Hq, int64_t Hkv, int64_t D,
+                int64_t q_st, int64_t q_sh, int64_t k_st, int64_t k_sh, double theta, int dtype,
+                const rope_qk_options* options, void* stream, double sign) {
+  RopeLaunch L;
+  const int status = prepare_rope(q, k, cu, nseq, T, Hq, Hkv, D, q_st, q_sh, k_st, k_sh, theta, dtype, options, sign,
+                                  true, &L);
+  if (status != ROPE_QK_OK || L.fn == nullptr) return status;
+  void* args[] = {&L.p};
+  const hipError_t err = hipLaunchKernel(L.fn, L.grid, dim3(kThreads), args, L.lds, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? ROPE_QK_OK : ROPE_QK_ERR_LAUNCH;
 }
 
@@ -545,13 +616,45 @@ int rope_qk_positions(const int32_t* cu_seqlens, int64_t nseq, int64_t T, int32_
   if (nseq < 0 || T < 0 || T > INT32_MAX || nseq >= INT32_MAX) return ROPE_QK_ERR_SHAPE;
   if (T == 0) return ROPE_QK_OK;
   if (cu_seqlens == nullptr || pos_out == nullptr) return ROPE_QK_ERR_NULL;
-  const int64_t blocks = (T + kThreads - 1) / kThreads;
-  const int64_t grid = blocks < 65536 ? blocks : 65536;
-  int32_t n = static_cast<int32_t>(nseq);
-  void* args[] = {&cu_seqlens, &n, &T, &pos_out};
-  const hipError_t err =
-      hipLaunchKernel(reinterpret_cast<const void*>(&rope_positions_kernel), dim3(static_cast<uint32_t>(grid)),
-                      dim3(kThreads), args, 0, static_cast<hipStream_t>(stream));
+  // one task per token, tiles of kPositionTileTokens whole tokens, no pos_offset
+  const int64_t ntiles = (T + kPositionTileTokens - 1) / kPositionTileTokens;
+  RopeParams p{};
+  p.cu = cu_seqlens;
+  p.T = T;
+  p.nseq = static_cast<int32_t>(nseq);
+  p.tasks_per_tok = 1;
+  p.tile_tasks = kPositionTileTokens;
+  p.half = 1;
+  p.magic_tok = uint64_t(1) << 40;
+  p.magic_half = uint64_t(1) << 32;
+  p.rcp_tok = 1.0;
+  p.ntiles = static_cast<uint32_t>(ntiles);
+  const int64_t gx = ntiles < kGridX ? ntiles : kGridX;
+  const dim3 grid(static_cast<uint32_t>(gx), static_cast<uint32_t>((ntiles + gx - 1) / gx));
+  void* args[] = {&p, &pos_out};
+  const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&rope_token_positions_kernel), grid,
+                                         dim3(kThreads), args, 0, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? ROPE_QK_OK : ROPE_QK_ERR_LAUNCH;
+}
+
+int rope_qk_tile_positions(const int32_t* cu_seqlens, int64_t nseq, int64_t T, int64_t Hq, int64_t Hkv, int64_t D,
+                           int dtype, const rope_qk_options* options, int32_t* out, int64_t out_len,
+                           int64_t* ntiles, int64_t* row_len, void* stream) {
+  if (ntiles == nullptr || row_len == nullptr) return ROPE_QK_ERR_NULL;
+  *ntiles = 0;
+  *row_len = 0;
+  RopeLaunch L;
+  const int status = prepare_rope(nullptr, nullptr, cu_seqlens, nseq, T, Hq, Hkv, D, 0, 0, 0, 0, 1.0, dtype, options,
+                                  1.0, false, &L);
+  if (status != ROPE_QK_OK || L.fn == nullptr) return status;
+  *ntiles = L.p.ntiles;
+  *row_len = 1 + L.span;
+  if (out == nullptr) return ROPE_QK_OK;  // the geometry only
+  if (out_len < *ntiles * *row_len) return ROPE_QK_ERR_SHAPE;
+  int64_t rl = *row_len;
+  void* args[] = {&L.p, &out, &rl};
+  const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&rope_tile_positions_kernel), L.grid,
+                                         dim3(kThreads), args, 0, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? ROPE_QK_OK : ROPE_QK_ERR_LAUNCH;
 }
 
@@ -564,7 +667,7 @@ const char* rope_qk_strerror(int status) {
     case ROPE_QK_ERR_ALIGN: return "misaligned: pointers, strides and D/2 must be multiples of 16 bytes";
     case ROPE_QK_ERR_THETA: return "theta must be finite and > 0";
     case ROPE_QK_ERR_LAUNCH: return "HIP kernel launch failed";
-    case ROPE_QK_ERR_LAYOUT: return "negative strides or overlapping rows";
+    case ROPE_QK_ERR_LAYOUT: return "negative strides, overlapping rows, or tensors that share memory";
     case ROPE_QK_ERR_OPTION:
       return "an option is out of range (pos_offset, rotary_dim, pairing, scaling, freq_precision, reserved or eps)";
     case ROPE_QK_ERR_WORKSPACE: return "workspace missing or smaller than rope_qk_norm_bwd_workspace_bytes";

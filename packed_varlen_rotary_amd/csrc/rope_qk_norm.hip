@@ -99,6 +99,8 @@ struct NormParams {
   int32_t pos_offset;
   int32_t freq_fp32;
   double inv_freq[kMaxHalf];
+  int32_t* pos_rows;     // positions hook only: [ntiles][pos_row_len] (first token, then positions)
+  int64_t pos_row_len;
 };
 
 // The float64 value lane (addr / 4) holds (ds_bpermute, two dwords).
@@ -425,10 +427,13 @@ __device__ __forceinline__ void seq_advance(const NormParams& p, SeqCursor& c, i
 // Positions and the table of a tile, from each entry's frequency f (and, for
 // the forward, the weights w1, w2 of the pair's two elements); ends with a
 // barrier.
-template <int kDtype, bool kIl, bool kBwd, int kL>
+// kPosOnly (the positions test hook): no table; the tile's first token and
+// its tokens' positions go to pos_out[0 .. ntok] instead.
+template <int kDtype, bool kIl, bool kBwd, int kL, bool kPosOnly = false>
 __device__ __forceinline__ void tile_table(const NormParams& p, const TileGeom& gm, const int* tt_e, const int* i_e,
                                            const double* f, const float* w1, const float* w2,
-                                           const SeqCursor& sc, int32_t* s_pos, double2* s_cs) {
+                                           const SeqCursor& sc, int32_t* s_pos, double2* s_cs,
+                                           int32_t* pos_out = nullptr) {
   constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;
   constexpr int kPPC = kIl ? kVec / 2 : kVec;
   constexpr int L = kL, hl = kL / 2;
@@ -457,6 +462,11 @@ __device__ __forceinline__ void tile_table(const NormParams& p, const TileGeom& 
     const int32_t pos = pos64 <= INT32_MAX ? static_cast<int32_t>(pos64) : -1;
     if (e < gm.nent) {
       if (i_e[v] == 0) s_pos[tt_e[v]] = pos;
+      if constexpr (kPosOnly) {
+        if (i_e[v] == 0) pos_out[1 + tt_e[v]] = pos;
+        if (e == 0) pos_out[0] = static_cast<int32_t>(gm.t0);
+        continue;
+      }
       if (pos >= 0) {
         double sn, cs;
         const double ang = p.freq_fp32 ? static_cast<double>(static_cast<float>(pos) * static_cast<float>(f[v]))
@@ -578,8 +588,10 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
 
 
 // The forward tile: its frequencies and weights are loaded before its data.
-template <int kDtype, bool kIl, int kTPT, int kL>
-__device__ __forceinline__ void fwd_tile(const NormParams& p, uint32_t tile, int32_t* s_pos, double2* s_cs) {
+// kPosOnly: the positions hook (see tile_table).
+template <int kDtype, bool kIl, int kTPT, int kL, bool kPosOnly = false>
+__device__ __forceinline__ void fwd_tile(const NormParams& p, uint32_t tile, int32_t* s_pos, double2* s_cs,
+                                         int32_t* pos_out = nullptr) {
   const TileGeom gm = tile_geom(p, tile);
   const NormTensor& tn = p.ten[gm.sel];
   int tt_e[kEnt], i_e[kEnt];
@@ -590,16 +602,20 @@ __device__ __forceinline__ void fwd_tile(const NormParams& p, uint32_t tile, int
   for (int v = 0; v < kEnt; ++v) {
     const bool live = v == 0 || v * kThreads < gm.nent;
     f[v] = live ? p.inv_freq[i_e[v]] : 0.0;
-    w1[v] = live ? tn.w[kIl ? 2 * i_e[v] : i_e[v]] : 0.f;
-    w2[v] = live ? tn.w[kIl ? 2 * i_e[v] + 1 : i_e[v] + p.half] : 0.f;
+    if constexpr (kPosOnly) {  // the hook has no weights
+      w1[v] = w2[v] = 0.f;
+    } else {
+      w1[v] = live ? tn.w[kIl ? 2 * i_e[v] : i_e[v]] : 0.f;
+      w2[v] = live ? tn.w[kIl ? 2 * i_e[v] + 1 : i_e[v] + p.half] : 0.f;
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
   TileData<kTPT> d;
-  tile_loads<false, kTPT, kL>(p, gm, d);
+  if constexpr (!kPosOnly) tile_loads<false, kTPT, kL>(p, gm, d);
   __builtin_amdgcn_sched_barrier(0);
   const SeqCursor sc = seq_cursor(p, last_start_at_or_before((cu_ptr)p.cu, p.nseq, gm.t0));
-  tile_table<kDtype, kIl, false, kL>(p, gm, tt_e, i_e, f, w1, w2, sc, s_pos, s_cs);
-  tile_compute<kDtype, kIl, false, kTPT, kL>(p, gm, d, s_pos, s_cs, nullptr, nullptr);
+  tile_table<kDtype, kIl, false, kL, kPosOnly>(p, gm, tt_e, i_e, f, w1, w2, sc, s_pos, s_cs, pos_out);
+  if constexpr (!kPosOnly) tile_compute<kDtype, kIl, false, kTPT, kL>(p, gm, d, s_pos, s_cs, nullptr, nullptr);
 }
 
 // LDS of the norm kernels after the table (the forward's one, the backward's
@@ -629,6 +645,16 @@ __global__ __launch_bounds__(kThreads) void rope_qk_norm_fwd_kernel(const NormPa
   const uint32_t tile = blockIdx.y * gridDim.x + blockIdx.x;
   if (tile >= p.ntiles) return;
   fwd_tile<kDtype, kIl, kTPT, kL>(p, tile, s_pos, s_cs);
+}
+
+// The positions hook of the forward: one tile per workgroup through the
+// forward tile's own geometry, sequence search and position code.
+__global__ __launch_bounds__(kThreads) void rope_qk_norm_fwd_positions_kernel(const NormParams p) {
+  __shared__ int32_t s_pos[kMaxTileTokens];
+  const uint32_t tile = blockIdx.y * gridDim.x + blockIdx.x;
+  if (tile >= p.ntiles) return;
+  fwd_tile<ROPE_QK_BF16, false, kFwdTasks, 8, true>(p, tile, s_pos, nullptr,
+                                                    p.pos_rows + static_cast<int64_t>(tile) * p.pos_row_len);
 }
 
 // Adds this thread's weight-gradient terms of tensor `sel` into the
@@ -671,7 +697,10 @@ __device__ __forceinline__ void flush_dw(const NormParams& p, int sel, const dou
 // registers while the tiles are of one tensor (q's tiles come first, so that
 // changes at most once) and are summed across the workgroup only then and at
 // the end.
-template <int kDtype, bool kIl, int kTPT, int kL>
+// kPosOnly (the positions test hook): the same runs of tiles and the same
+// sequence cursor, writing each tile's first token and positions to row
+// `tile` of p.pos_rows; nothing is loaded, computed or stored.
+template <int kDtype, bool kIl, int kTPT, int kL, bool kPosOnly = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBwdWaves16)))
 void rope_qk_norm_bwd_kernel(const NormParams p) {
   constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;
@@ -684,10 +713,12 @@ void rope_qk_norm_bwd_kernel(const NormParams p) {
   double* s_freq = s_wave + kWaves * p.D;                    // [D / 2]
   const int tid = threadIdx.x;
   const int D = p.D;
-  load_weights(p, s_w);
-  for (int i = tid; i < 2 * D; i += kThreads) s_acc[i] = 0.0;
-  for (int i = tid; i < p.half; i += kThreads) s_freq[i] = p.inv_freq[i];
-  __syncthreads();
+  if constexpr (!kPosOnly) {
+    load_weights(p, s_w);
+    for (int i = tid; i < 2 * D; i += kThreads) s_acc[i] = 0.0;
+    for (int i = tid; i < p.half; i += kThreads) s_freq[i] = p.inv_freq[i];
+    __syncthreads();
+  }
   double acc[kVec];
 #pragma unroll
   for (int j = 0; j < kVec; ++j) acc[j] = 0.0;
@@ -705,13 +736,15 @@ void rope_qk_norm_bwd_kernel(const NormParams p) {
     const TileGeom gm = tile_geom(p, tile);
     const bool fresh = gm.sel != cur;
     if (fresh) {
-      if (cur >= 0) flush_dw<kVec, kL>(p, cur, acc, s_wave, s_acc);
+      if constexpr (!kPosOnly) {
+        if (cur >= 0) flush_dw<kVec, kL>(p, cur, acc, s_wave, s_acc);
 #pragma unroll
-      for (int j = 0; j < kVec; ++j) acc[j] = 0.0;
+        for (int j = 0; j < kVec; ++j) acc[j] = 0.0;
+      }
       cur = gm.sel;
     }
     TileData<kTPT> d;
-    tile_loads<true, kTPT, kL>(p, gm, d);
+    if constexpr (!kPosOnly) tile_loads<true, kTPT, kL>(p, gm, d);
     __builtin_amdgcn_sched_barrier(0);
     if (fresh)
       sc = seq_cursor(p, last_start_at_or_before((cu_ptr)p.cu, p.nseq, gm.t0));
@@ -721,14 +754,21 @@ void rope_qk_norm_bwd_kernel(const NormParams p) {
     double f[kEnt];
     tile_entries(p, gm, tt_e, i_e);
 #pragma unroll
-    for (int v = 0; v < kEnt; ++v) f[v] = s_freq[i_e[v]];
-    tile_table<kDtype, kIl, true, kL>(p, gm, tt_e, i_e, f, nullptr, nullptr, sc, s_pos[b], s_cs + b * tab_len);
-    tile_compute<kDtype, kIl, true, kTPT, kL>(p, gm, d, s_pos[b], s_cs + b * tab_len, s_w, acc);
+    for (int v = 0; v < kEnt; ++v) f[v] = kPosOnly ? 0.0 : s_freq[i_e[v]];
+    if constexpr (kPosOnly) {
+      tile_table<kDtype, kIl, true, kL, true>(p, gm, tt_e, i_e, f, nullptr, nullptr, sc, s_pos[b], nullptr,
+                                              p.pos_rows + static_cast<int64_t>(tile) * p.pos_row_len);
+    } else {
+      tile_table<kDtype, kIl, true, kL>(p, gm, tt_e, i_e, f, nullptr, nullptr, sc, s_pos[b], s_cs + b * tab_len);
+      tile_compute<kDtype, kIl, true, kTPT, kL>(p, gm, d, s_pos[b], s_cs + b * tab_len, s_w, acc);
+    }
     b ^= 1;
   }
-  if (cur >= 0) flush_dw<kVec, kL>(p, cur, acc, s_wave, s_acc);
-  double* dst = p.partial + static_cast<int64_t>(blockIdx.x) * 2 * D;
-  for (int i = tid; i < 2 * D; i += kThreads) dst[i] = s_acc[i];
+  if constexpr (!kPosOnly) {
+    if (cur >= 0) flush_dw<kVec, kL>(p, cur, acc, s_wave, s_acc);
+    double* dst = p.partial + static_cast<int64_t>(blockIdx.x) * 2 * D;
+    for (int i = tid; i < 2 * D; i += kThreads) dst[i] = s_acc[i];
+  }
 }
 
 // The weight gradients: column blockIdx.x of the workgroups' sums, added in a
@@ -830,6 +870,22 @@ int check_norm_call(int dtype, int64_t nseq, int64_t T, int64_t Hq, int64_t Hkv,
     if (!aligned16(ts[i].base) || (ts[i].st * esz) % 16 || (ts[i].sh * esz) % 16) return ROPE_QK_ERR_ALIGN;
     if (ts[i].st < 0 || ts[i].sh < 0 || rows_overlap(T, H, D, ts[i].st, ts[i].sh)) return ROPE_QK_ERR_LAYOUT;
   }
+  // the last two tensors are written (q's, then k's): each must be exactly
+  // its own input (in place: ts[i - first_out]) or share no byte with any
+  // other tensor of the call
+  const int first_out = nts - 2;
+  for (int i = first_out; i < nts; ++i) {
+    const int64_t Hi = (i % 2 == 0) ? Hq : Hkv;
+    for (int j = 0; j < nts; ++j) {
+      const int64_t Hj = (j % 2 == 0) ? Hq : Hkv;
+      if (j == i || Hi == 0 || Hj == 0) continue;
+      const Tensor& a = ts[i];
+      const Tensor& b = ts[j];
+      if (j == i - first_out && a.base == b.base && a.st == b.st && a.sh == b.sh) continue;
+      if (!rows_disjoint(a.base, Hi, a.st * esz, a.sh * esz, b.base, Hj, b.st * esz, b.sh * esz, T, D * esz))
+        return ROPE_QK_ERR_LAYOUT;
+    }
+  }
   if ((Hq > 0 && !aligned16(wq)) || (Hkv > 0 && !aligned16(wk))) return ROPE_QK_ERR_ALIGN;
   return ROPE_QK_OK;
 }
@@ -863,6 +919,8 @@ void fill_params(NormParams* p, const NormGeometry& g, const int32_t* cu, int64_
   p->pos_offset = static_cast<int32_t>(o.pos_offset);
   p->freq_fp32 = o.freq_precision == ROPE_QK_FREQ_FP32;
   fill_inv_freq(theta, D, o, p->inv_freq);
+  p->pos_rows = nullptr;
+  p->pos_row_len = 0;
 }
 
 void set_tensor(NormTensor* tn, const void* x, const Tensor& tx, const void* gr, const Tensor* tg, void* o,
@@ -1079,6 +1137,46 @@ int64_t rope_qk_norm_bwd_workspace_bytes(int64_t T, int64_t Hq, int64_t Hkv, int
   const int status = norm_geometry(T, Hq, Hkv, D, dtype, true, &g);
   if (status != ROPE_QK_OK) return status;
   return workspace_bytes(g, D);
+}
+
+int rope_qk_norm_tile_positions(const int32_t* cu_seqlens, int64_t nseq, int64_t T, int64_t Hq, int64_t Hkv,
+                                int64_t D, int dtype, const rope_qk_options* options, int backward, int32_t* out,
+                                int64_t out_len, int64_t* ntiles, int64_t* row_len, void* stream) {
+  if (ntiles == nullptr || row_len == nullptr) return ROPE_QK_ERR_NULL;
+  *ntiles = 0;
+  *row_len = 0;
+  const rope_qk_options o = options ? *options : rope_qk_options{};
+  int status = check_call(dtype, nseq, T, Hq, Hkv, D, 1.0, o);
+  if (status != ROPE_QK_OK) return status;
+  if (o.rotary_dim != 0 && o.rotary_dim != D) return ROPE_QK_ERR_OPTION;
+  NormGeometry g;
+  status = norm_geometry(T, Hq, Hkv, D, dtype, backward != 0, &g);
+  if (status != ROPE_QK_OK) return status;
+  if (T == 0 || Hq + Hkv == 0) return ROPE_QK_OK;
+  *ntiles = g.ntiles[0] + g.ntiles[1];
+  *row_len = 1 + g.span;
+  if (out == nullptr) return ROPE_QK_OK;  // the geometry only
+  if (cu_seqlens == nullptr) return ROPE_QK_ERR_NULL;
+  if (out_len < *ntiles * *row_len) return ROPE_QK_ERR_SHAPE;
+  NormParams p;
+  fill_params(&p, g, cu_seqlens, nseq, T, Hq, Hkv, D, 1.0, 1.0, o, nullptr, nullptr, backward ? -1.0 : 1.0);
+  p.partial = nullptr;
+  p.pos_rows = out;
+  p.pos_row_len = *row_len;
+  void* args[] = {&p};
+  hipError_t err;
+  if (backward) {
+    err = hipLaunchKernel(reinterpret_cast<const void*>(&rope_qk_norm_bwd_kernel<ROPE_QK_BF16, false, kBwdTasks, 8, true>),
+                          dim3(static_cast<uint32_t>(g.groups)), dim3(kThreads), args, 0,
+                          static_cast<hipStream_t>(stream));
+  } else {
+    const int64_t nt = *ntiles;
+    const int64_t gx = nt < kGridX ? nt : kGridX;
+    err = hipLaunchKernel(reinterpret_cast<const void*>(&rope_qk_norm_fwd_positions_kernel),
+                          dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>((nt + gx - 1) / gx)), dim3(kThreads),
+                          args, 0, static_cast<hipStream_t>(stream));
+  }
+  return err == hipSuccess ? ROPE_QK_OK : ROPE_QK_ERR_LAUNCH;
 }
 
 int rope_qk_norm_bwd(const void* dq_out, const void* dk_out, const void* q, const void* k, void* dq, void* dk,

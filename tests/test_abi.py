@@ -40,7 +40,8 @@ C = header_constants()
 lib = P.load()
 
 # fake but 16-byte aligned device addresses; never dereferenced by these calls
-Q, K, CU = 0x10000, 0x20000, 0x30000
+# (1 TiB apart, so that the tensors of these calls never share memory)
+Q, K, CU = 1 << 40, 2 << 40, 3 << 40
 
 
 def fwd(q=Q, k=K, cu=CU, nseq=4, T=256, Hq=14, Hkv=2, D=64, qst=None, qsh=None, kst=None, ksh=None,
@@ -230,7 +231,8 @@ def test_pairing_and_scaling_constants_match_binding():
 # per-head RMSNorm + rotation: argument checks (nothing is launched)
 # ---------------------------------------------------------------------------
 
-W_Q, W_K, WS = 0x40000, 0x50000, 0x60000
+W_Q, W_K, WS = 4 << 40, 5 << 40, 6 << 40
+DWQ, DWK = 7 << 40, 8 << 40
 
 
 def norm_fwd(q=Q, k=K, qo=None, ko=None, wq=W_Q, wk=W_K, eps=1e-6, cu=CU, nseq=4, T=256, Hq=14, Hkv=2, D=64,
@@ -244,7 +246,7 @@ def norm_fwd(q=Q, k=K, qo=None, ko=None, wq=W_Q, wk=W_K, eps=1e-6, cu=CU, nseq=4
                                 D, st, theta, dtype, ctypes.byref(opts) if opts is not None else None, None)
 
 
-def norm_bwd(ws=WS, ws_size=1 << 30, dwq=0x70000, dwk=0x80000, wq=W_Q, eps=1e-6, T=256, Hq=14, Hkv=2, D=64,
+def norm_bwd(ws=WS, ws_size=1 << 30, dwq=DWQ, dwk=DWK, wq=W_Q, eps=1e-6, T=256, Hq=14, Hkv=2, D=64,
              dtype=1, cu=CU, opts=None):
     st = (ctypes.c_int64 * 12)(*([Hq * D, D, Hkv * D, D] * 3))
     return lib.rope_qk_norm_bwd(ctypes.c_void_p(Q), ctypes.c_void_p(K), ctypes.c_void_p(Q + (1 << 24)),
@@ -297,14 +299,14 @@ def test_norm_bwd_error_codes_and_workspace_size():
     assert norm_bwd(ws_size=need - 16) == C["ROPE_QK_ERR_WORKSPACE"]
     assert norm_bwd(ws=WS + 8) == C["ROPE_QK_ERR_ALIGN"]
     assert norm_bwd(dwq=0) == C["ROPE_QK_ERR_NULL"]
-    assert norm_bwd(dwq=0x70004) == C["ROPE_QK_ERR_ALIGN"]
+    assert norm_bwd(dwq=DWQ + 4) == C["ROPE_QK_ERR_ALIGN"]
     assert norm_bwd(eps=0.0) == C["ROPE_QK_ERR_OPTION"]
     assert norm_bwd(wq=0) == C["ROPE_QK_ERR_NULL"]
     assert norm_bwd(cu=0) == C["ROPE_QK_ERR_NULL"]
     assert norm_bwd(dtype=5) == C["ROPE_QK_ERR_DTYPE"]
 
 
-def norm_bwd_noalloc(dwq=0x70000, dwk=0x80000, wq=W_Q, eps=1e-6, T=256, Hq=14, Hkv=2, D=64, dtype=1, cu=CU,
+def norm_bwd_noalloc(dwq=DWQ, dwk=DWK, wq=W_Q, eps=1e-6, T=256, Hq=14, Hkv=2, D=64, dtype=1, cu=CU,
                      opts=None, theta=1e6, strides="default"):
     st = None if strides is None else (ctypes.c_int64 * 12)(*([Hq * D, D, Hkv * D, D] * 3))
     return lib.rope_qk_norm_bwd_noalloc(ctypes.c_void_p(Q), ctypes.c_void_p(K), ctypes.c_void_p(Q + (1 << 24)),
@@ -326,7 +328,7 @@ def test_norm_bwd_noalloc_checks_before_any_hip_call():
     assert norm_bwd_noalloc(strides=None) == C["ROPE_QK_ERR_NULL"]
     assert norm_bwd_noalloc(wq=0) == C["ROPE_QK_ERR_NULL"]
     assert norm_bwd_noalloc(dwq=0) == C["ROPE_QK_ERR_NULL"]
-    assert norm_bwd_noalloc(dwq=0x70004) == C["ROPE_QK_ERR_ALIGN"]
+    assert norm_bwd_noalloc(dwq=DWQ + 4) == C["ROPE_QK_ERR_ALIGN"]
     assert norm_bwd_noalloc(cu=0) == C["ROPE_QK_ERR_NULL"]
     # the same calls give the same codes in the workspace form
     assert norm_bwd(dtype=5) == C["ROPE_QK_ERR_DTYPE"] and norm_bwd(D=96) == C["ROPE_QK_ERR_SHAPE"]
@@ -336,3 +338,97 @@ def test_norm_bwd_noalloc_checks_before_any_hip_call():
                lib.rope_qk_norm_bwd_workspace_bytes(10 ** 6, 8, 8, 512, 2),
                lib.rope_qk_norm_bwd_workspace_bytes(10 ** 6, 8, 8, 256, 0)) == 24 << 20
     assert "24 MiB" in P.rope_qk_strerror(C["ROPE_QK_ERR_SCRATCH"])
+
+
+# ---------------------------------------------------------------------------
+# tensors that share memory (checked from the pointers and strides)
+# ---------------------------------------------------------------------------
+
+def test_q_and_k_that_share_memory_are_refused():
+    """q and k are rotated by one launch, so they must share no byte.  D = 72
+    (bf16: 72-byte half rows) makes every layout the check accepts stop at
+    the alignment check that follows it, so nothing is launched."""
+    E, A = C["ROPE_QK_ERR_LAYOUT"], C["ROPE_QK_ERR_ALIGN"]
+    T, Hq, Hkv, D, e = 256, 14, 2, 72, 2
+    g = lambda **kw: fwd(T=T, Hq=Hq, Hkv=Hkv, D=D, **kw)  # noqa: E731
+    assert g() == A  # separate buffers
+    assert g(k=Q, kst=Hq * D, ksh=D) == E  # the same tensor passed twice
+    assert g(k=Q + Hq * D * e, kst=Hq * D, ksh=D) == E  # k starts at q's second token
+    assert g(k=Q + 5 * D * e) == E  # k inside q's rows
+    # fused QKV buffer [T, Hq + 2 Hkv, D]: q, k (and v) views with one token stride
+    H = Hq + 2 * Hkv
+    assert g(qst=H * D, kst=H * D, k=Q + Hq * D * e) == A
+    assert g(qst=H * D, kst=H * D, k=Q + (Hq - 1) * D * e) == E  # k's first head is q's last
+    assert g(qst=H * D, kst=H * D, k=Q + (Hq + Hkv) * D * e) == A  # k where v would be
+    # interleaved heads: q's rows every other head slot, k's in between
+    assert g(qst=2 * H * D, qsh=2 * D, kst=2 * H * D, ksh=2 * D, k=Q + D * e) == E  # refused: spans meet
+    # head-major views [H, T, D] of one buffer: q heads first, then k heads
+    assert g(qst=D, qsh=T * D, kst=D, ksh=T * D, k=Q + Hq * T * D * e) == A
+    assert g(qst=D, qsh=T * D, kst=D, ksh=T * D, k=Q + (Hq - 1) * T * D * e) == E
+
+
+def test_norm_outputs_that_share_memory_are_refused():
+    E = C["ROPE_QK_ERR_LAYOUT"]
+    # an output over the other tensor's input
+    assert norm_fwd(qo=K, cu=0) == E
+    # an output partly over its own input (neither in place nor separate)
+    assert norm_fwd(qo=Q + 64 * 2, cu=0) == E
+    # k_out over q_out
+    assert norm_fwd(qo=Q + (1 << 24), ko=Q + (1 << 24) + 64 * 2, cu=0) == E
+    # in place and separate outputs pass the check (and stop at the NULL cu_seqlens)
+    assert norm_fwd(cu=0) == C["ROPE_QK_ERR_NULL"]
+    assert norm_fwd(qo=Q + (1 << 24), ko=K + (1 << 24), cu=0) == C["ROPE_QK_ERR_NULL"]
+
+
+LAYOUT_DRIVER = r"""
+#include <stdio.h>
+#include <stdint.h>
+#include "rope_layout.h"
+int main(void) {
+  long long a, Ha, ast, ash, b, Hb, bst, bsh, T, row;
+  while (scanf("%lld %lld %lld %lld %lld %lld %lld %lld %lld %lld", &a, &Ha, &ast, &ash, &b, &Hb, &bst, &bsh, &T,
+               &row) == 10)
+    printf("%d\n", rows_disjoint((const void*)(uintptr_t)a, Ha, ast, ash, (const void*)(uintptr_t)b, Hb, bst, bsh,
+                                 T, row) ? 1 : 0);
+  return 0;
+}
+"""
+
+
+def test_rows_disjoint_never_accepts_an_overlap(tmp_path):
+    """The host check against brute force on small byte grids: it never calls
+    two grids that share a byte disjoint, and it accepts the fused-projection
+    and separate-buffer layouts."""
+    import numpy as np
+
+    src = tmp_path / "drv.cpp"
+    src.write_text(LAYOUT_DRIVER)
+    exe = tmp_path / "drv"
+    hdr = os.path.join(ROOT, "packed_varlen_rotary_amd", "csrc")
+    subprocess.run(["g++", "-O1", "-std=c++17", "-I", hdr, str(src), "-o", str(exe)], check=True)
+    rng = np.random.default_rng(5)
+    cases = []
+    for _ in range(3000):
+        T, Ha, Hb = (int(x) for x in rng.integers(1, 5, 3))
+        row = int(rng.choice([2, 4, 8]))
+        S = int(rng.integers(row, 6 * row))
+        ast = S if rng.random() < 0.7 else int(rng.integers(0, 6 * row))
+        bst = S if rng.random() < 0.7 else int(rng.integers(0, 6 * row))
+        ash, bsh = (int(rng.integers(row, 3 * row)) for _ in range(2))
+        a = 1 << 20
+        b = a + int(rng.integers(-4 * S, 8 * S))
+        cases.append((a, Ha, ast, ash, b, Hb, bst, bsh, T, row))
+    # layouts that must be accepted
+    cases += [(1 << 20, 4, 96 * 8, 96, (1 << 20) + 4 * 96, 2, 96 * 8, 96, 5, 96),  # fused projection
+              (1 << 20, 4, 96, 96 * 7, (1 << 20) + 4 * 96 * 7, 2, 96, 96 * 7, 7, 96)]  # head-major
+    inp = "\n".join(" ".join(str(v) for v in c) for c in cases) + "\n"
+    got = [int(x) for x in subprocess.run([str(exe)], input=inp, capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    for c, g in zip(cases, got):
+        a, Ha, ast, ash, b, Hb, bst, bsh, T, row = c
+        ba = {a + t * ast + h * ash + i for t in range(T) for h in range(Ha) for i in range(row)}
+        bb = {b + t * bst + h * bsh + i for t in range(T) for h in range(Hb) for i in range(row)}
+        if g == 1:
+            assert not (ba & bb), c
+    assert got[-2:] == [1, 1]
+    assert sum(got) > 500  # the check is not vacuous

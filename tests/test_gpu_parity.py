@@ -289,9 +289,13 @@ def test_side_stream_and_binding_errors():
     s.synchronize()
     check_against(t["q"], oracle.rope(x, w.cu_seqlens, w.theta, 1), "side stream")
     odd = torch.zeros(8, 2, 66, dtype=torch.bfloat16, device=DEV)[:, :, 1:65]  # 2-byte misaligned view
+    odd_k = torch.zeros(8, 1, 66, dtype=torch.bfloat16, device=DEV)[:, :, 1:65]
     with pytest.raises(P.RopeQKError) as e:
-        P.rope_qk_fwd(odd, odd[:, :1], cu_dev([0, 8]), 1e4)
+        P.rope_qk_fwd(odd, odd_k, cu_dev([0, 8]), 1e4)
     assert e.value.status == -4
+    with pytest.raises(P.RopeQKError) as e:  # q and k sharing memory
+        P.rope_qk_fwd(t["q"], t["q"][:, :2], cu_dev(w.cu_seqlens), w.theta)
+    assert e.value.status == -7
 
 
 @pytest.mark.parametrize("offset", [0, 2 ** 31 - 1 - 600])
