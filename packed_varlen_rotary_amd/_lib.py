@@ -523,7 +523,7 @@ def packed_cu_seqlens(lengths, bin_of, offset_of, nbins: int, capacity: int):
 
 class _DeviceInt32:
     """A device int32 vector owned by the native cache, shown to torch through
-    the CUDA array interface (zero copy)."""
+    the CUDA array interface (zero copy) so that it can be copied once."""
 
     def __init__(self, ptr: int, n: int):
         self.__cuda_array_interface__ = {"shape": (n,), "typestr": "<i4", "data": (ptr, False), "version": 2,
@@ -532,11 +532,12 @@ class _DeviceInt32:
 
 class PackPlan:
     """One packed batch from PackCache.get.  cu_seqlens: device int32 tensor
-    (a view of the cache's buffer; None for a host-only cache); the rest are
-    host copies.  The device view stays valid until the plan is evicted from
-    its cache (after max_entries other batches) or the cache is closed."""
+    owned by torch (None for a host-only cache), copied once from the cache's
+    upload when the batch is first packed, on the caller's stream, and shared
+    by every later hit; it stays valid while referenced, whatever the cache
+    evicts or closes.  The rest are host copies."""
 
-    def __init__(self, s: PackPlanStruct, device):
+    def __init__(self, s: PackPlanStruct, device, stream=None):
         import numpy as np
 
         nseg, n = int(s.nseg), int(s.n)
@@ -549,12 +550,17 @@ class PackPlan:
         self.n, self.nseg, self.nbins, self.T = n, nseg, int(s.nbins), int(s.T)
         self.max_seqlen = int(s.max_seqlen)
         self.hit = bool(s.hit)
-        self.cu_seqlens_ptr = int(s.cu_seqlens_device or 0)
+        self.cu_seqlens_ptr = int(s.cu_seqlens_device or 0)  # the cache's own buffer (freed on eviction)
         self.cu_seqlens = None
         if self.cu_seqlens_ptr:
             import torch
 
-            self.cu_seqlens = torch.as_tensor(_DeviceInt32(self.cu_seqlens_ptr, nseg + 1), device=device)
+            # a torch-owned copy, ordered after the cache's upload on the same
+            # stream; evicting the plan frees the cache's buffer only after
+            # the device is idle (hipFree), so the copy has been made by then
+            view = torch.as_tensor(_DeviceInt32(self.cu_seqlens_ptr, nseg + 1), device=device)
+            with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream(device)):
+                self.cu_seqlens = view.clone()
 
 
 class PackCache:
@@ -595,7 +601,7 @@ class PackCache:
         key = int(s.cu_seqlens_host or 0)
         view = self._views.get(key) if s.hit else None
         if view is None:
-            view = PackPlan(s, self.device)
+            view = PackPlan(s, self.device, stream)
             self._views[key] = view
             if len(self._views) > 4 * self._max_entries:  # drop views of plans long evicted
                 self._views = {key: view}

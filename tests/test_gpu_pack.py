@@ -35,6 +35,7 @@ def test_device_plan_and_hits():
     assert np.array_equal(p.cu_seqlens_host, oracle.packed_cu_seqlens(lengths, rb, ro, rnb, 16384))
     q = cache.get(lengths, 16384)
     assert q.hit and q.cu_seqlens_ptr == p.cu_seqlens_ptr
+    assert q.cu_seqlens.data_ptr() == p.cu_seqlens.data_ptr()  # a hit shares the first copy
     assert cache.stats() == (1, 1, 1)
     cache.close()
 
@@ -97,3 +98,27 @@ def test_eviction_keeps_live_plans_correct():
     torch.cuda.synchronize()
     assert not again.hit and np.array_equal(again.cu_seqlens.cpu().numpy(), plans[0].cu_seqlens_host)
     cache.close()
+
+
+def test_plans_outlive_eviction_and_close():
+    """A plan's device cu_seqlens is torch-owned: after its cache entry is
+    evicted (and its cache buffer freed) and after the cache is closed, it
+    still holds the plan and drives the rotation like a fresh upload."""
+    cache = P.PackCache(max_entries=1)
+    batches = [mixture(60, s) for s in (20, 21, 22)]
+    plans = [cache.get(b, 8192) for b in batches]  # each evicts the one before
+    torch.cuda.synchronize()
+    junk = [torch.full((4096,), -7, dtype=torch.int32, device=DEV) for _ in range(64)]  # reuse freed memory
+    cache.close()
+    torch.cuda.synchronize()
+    for pl in plans:
+        assert np.array_equal(pl.cu_seqlens.cpu().numpy(), pl.cu_seqlens_host)
+    p0 = plans[0]
+    q = W.randn((p0.T, 4, 64), "bf16", seed=8, device=DEV)
+    k = W.randn((p0.T, 2, 64), "bf16", seed=9, device=DEV)
+    q2, k2 = q.clone(), k.clone()
+    P.rope_qk_fwd(q, k, p0.cu_seqlens, 1e6)
+    P.rope_qk_fwd(q2, k2, torch.as_tensor(p0.cu_seqlens_host, device=DEV), 1e6)
+    torch.cuda.synchronize()
+    assert torch.equal(q, q2) and torch.equal(k, k2)
+    del junk
