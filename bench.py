@@ -367,13 +367,15 @@ def run_gpu(args):
     del graph
 
     # the forward and the backward on their own (same replay, enough launches
-    # for a region of MIN_REGION_S)
+    # for a region of MIN_REGION_S); --no-split leaves them out (counter runs)
     n = launches_for(w.bytes_per_pass, args.steps)
-    fwd_us = timed_us(lambda i: P.rope_qk_fwd(sets[i % nsets]["q"], sets[i % nsets]["k"], cu, w.theta), n,
-                      args.graph)
-    bwd_us = timed_us(lambda i: P.rope_qk_bwd(sets[i % nsets]["dq"], sets[i % nsets]["dk"], cu, w.theta), n,
-                      args.graph)
-    log(f"[bench] {w.name}: forward {fwd_us:.2f} us, backward {bwd_us:.2f} us per launch ({n} launches each)")
+    fwd_us = bwd_us = None
+    if args.split:
+        fwd_us = timed_us(lambda i: P.rope_qk_fwd(sets[i % nsets]["q"], sets[i % nsets]["k"], cu, w.theta), n,
+                          args.graph)
+        bwd_us = timed_us(lambda i: P.rope_qk_bwd(sets[i % nsets]["dq"], sets[i % nsets]["dk"], cu, w.theta), n,
+                          args.graph)
+        log(f"[bench] {w.name}: forward {fwd_us:.2f} us, backward {bwd_us:.2f} us per launch ({n} launches each)")
     del sets
     torch.cuda.empty_cache()
 
@@ -386,9 +388,10 @@ def run_gpu(args):
     gbs = lambda us: w.bytes_per_pass / (us * 1e-6) / 1e9  # noqa: E731
     row = {"workload": w.name, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "nseq": w.nseq,
            "bytes_per_launch": w.bytes_per_pass, "launches_timed": n, "resident_batches": nsets,
-           "fwd_us": fwd_us, "bwd_us": bwd_us, "fwd_frac": gbs(fwd_us) / HBM_PEAK_GBS,
-           "bwd_frac": gbs(bwd_us) / HBM_PEAK_GBS, "traffic": measured_traffic(w.name)}
-    if args.ceiling:
+           "fwd_us": fwd_us, "bwd_us": bwd_us,
+           "fwd_frac": gbs(fwd_us) / HBM_PEAK_GBS if fwd_us else None,
+           "bwd_frac": gbs(bwd_us) / HBM_PEAK_GBS if bwd_us else None, "traffic": measured_traffic(w.name)}
+    if args.ceiling and args.split:
         c = stream_ceiling(w.bytes_per_pass, dev, args.steps, args.graph)
         row["stream_ceiling"] = {k: c[k] for k in ("us", "frac", "variant")}
         row["fwd_of_ceiling"] = c["us"] / fwd_us
@@ -806,6 +809,8 @@ def main():
                     help="other workloads measured in the same run (comma-separated; empty: none)")
     ap.add_argument("--no-ceiling", dest="ceiling", action="store_false",
                     help="skip the plain-stream ceiling beside each workload")
+    ap.add_argument("--no-split", dest="split", action="store_false",
+                    help="skip the forward-only and backward-only timings (few launches, for counter runs)")
     ap.add_argument("--stream-ceiling", action="store_true",
                     help="only time every plain in-place stream variant with one launch's traffic of --workload")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
