@@ -504,8 +504,9 @@ def run_copy_ceiling(args):
 def run_norm(args):
     """The fused per-head RMSNorm + rotation (rope_qk_norm_fwd out of place,
     rope_qk_norm_bwd into a separate dx) on a workload's shapes: each pass
-    timed on its own as a graph of K calls over resident sets of >= 1 GiB,
-    HIP events around the replay.  Algorithmic bytes: forward read x + write
+    timed on its own as a graph of K calls over resident sets of >= 1 GiB
+    (one by one with --no-graph), HIP events around the replays after 0.1 s
+    of warm-up.  Algorithmic bytes: forward read x + write
     y, backward read x and dy + write dx (the weight-gradient workspace is
     extra traffic, reported separately)."""
     import torch
@@ -551,25 +552,10 @@ def run_norm(args):
 
     res = {}
     for name, fn, nbytes in (("fwd", fwd, 2 * qk_bytes), ("bwd", bwd, 3 * qk_bytes)):
-        for i in range(args.warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for i in range(args.steps):
-                fn(i)
-        graph.replay()
-        torch.cuda.synchronize()
-        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        graph.replay()
-        b_.record()
-        torch.cuda.synchronize()
-        us = a.elapsed_time(b_) * 1e3 / args.steps
+        us = timed_us(fn, args.steps, args.graph, warmup=args.warmup)
         gbs = nbytes / (us * 1e-6) / 1e9
         res[name] = {"us_per_call": us, "algorithmic_bytes": nbytes, "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS}
         log(f"[bench] norm {name}: {us:.2f} us per call, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak)")
-        del graph
     print(json.dumps({"metric": "fused per-head QK-RMSNorm + RoPE, achieved HBM GB/s per pass", "workload": w.name,
                       "io_dtype": w.dtype, "resident_sets": nsets, "workspace_bytes": ws_bytes, "steps": args.steps,
                       "peak": HBM_PEAK_GBS, **res}))

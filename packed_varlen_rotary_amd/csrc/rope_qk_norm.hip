@@ -771,13 +771,22 @@ void rope_qk_norm_bwd_kernel(const NormParams p) {
   }
 }
 
-// The weight gradients: column blockIdx.x of the workgroups' sums, added in a
-// fixed tree order, rounded once to float32.
+// The weight gradients: one column of the workgroups' sums per workgroup,
+// added in a fixed tree order, rounded once to float32.  Workgroups go to
+// the 8 XCDs in turn (blockIdx.x % 8), each XCD with its own L2, so XCD x
+// takes a contiguous range of columns: the columns that share a 128-byte
+// line of a row are summed on one XCD, and each line comes from HBM once
+// rather than once per XCD.  (The order only places work; the sums are the
+// same whatever XCD runs them.)
+constexpr int kXcds = 8;
+
 __global__ __launch_bounds__(kThreads) void dw_reduce_kernel(const double* __restrict__ partial, uint32_t ngroups,
                                                             int32_t D, float* __restrict__ dwq,
                                                             float* __restrict__ dwk) {
   __shared__ double s[kThreads];
-  const int col = blockIdx.x;
+  const int per_xcd = gridDim.x / kXcds;  // the grid is kXcds * ceil(2 D / kXcds) workgroups
+  const int col = static_cast<int>(blockIdx.x % kXcds) * per_xcd + static_cast<int>(blockIdx.x / kXcds);
+  if (col >= 2 * D) return;
   const int tid = threadIdx.x;
   double acc = 0.0;
   for (uint32_t i = tid; i < ngroups; i += kThreads) acc += partial[static_cast<int64_t>(i) * 2 * D + col];
@@ -1085,8 +1094,9 @@ int norm_bwd_impl(const void* dq_out, const void* dk_out, const void* q, const v
   int32_t d32 = static_cast<int32_t>(D);
   const double* partial_c = partial;
   void* args[] = {const_cast<double**>(&partial_c), &ng, &d32, &dq_weight, &dk_weight};
-  const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&dw_reduce_kernel),
-                                         dim3(static_cast<uint32_t>(2 * D)), dim3(kThreads), args, 0, s);
+  const uint32_t reduce_groups = static_cast<uint32_t>(kXcds * ((2 * D + kXcds - 1) / kXcds));
+  const hipError_t err = hipLaunchKernel(reinterpret_cast<const void*>(&dw_reduce_kernel), dim3(reduce_groups),
+                                         dim3(kThreads), args, 0, s);
   return err == hipSuccess ? ROPE_QK_OK : ROPE_QK_ERR_LAUNCH;
 }
 
