@@ -22,13 +22,18 @@
 //  * Per row: the sum of squares in float64, summed over the row's lanes by
 //    a xor butterfly (ds_bpermute; every lane ends with the same bits),
 //    r = 1/sqrt(mean + eps) from v_rsq_f64 and two Newton steps, then the
-//    rotation exactly as in the rotation kernels: the rotate_half partner
-//    chunk comes from lane l ^ L/2 (negated in the first half), interleaved
-//    pairs sit inside a chunk; the cos/sin table is built once per tile.
+//    rotation: the rotate_half partner chunk comes from lane l ^ L/2,
+//    interleaved pairs sit inside a chunk; the table, built once per tile,
+//    holds one (A, B) entry per element with the signs (and weights) in it,
+//    so that an element becomes x_e A_e + x_p B_e.
 //  * A tile holds rows of q only or of k only, so it needs one weight vector
 //    and one set of weight-gradient sums.
-//  * Backward: the rotation by -angle (the table holds -sin), then the RMSNorm
-//    gradient with a second row sum (sum_j g_j x_j).  A fixed number of
+//  * Backward: the rotation by -angle, then the RMSNorm gradient with a
+//    second row sum (sum_j g_j x_j).  When every weight is finite and nonzero
+//    the weights are folded into the per-element table, so the rotation of
+//    dy yields g = w dn directly and the weight-gradient sums (of w dn x r)
+//    are divided by w once at the end; otherwise the table has unit weights
+//    and dn is multiplied by w.  A fixed number of
 //    workgroups each take a contiguous run of tiles, carrying a cursor into
 //    cu_seqlens from tile to tile, with one barrier per tile.  Each lane
 //    keeps the weight-gradient terms of its rows in registers while the
@@ -54,6 +59,10 @@ constexpr int kBwdTasks = 2;          // rows per lane per backward tile (regist
 constexpr int64_t kMaxHeads = 65535;  // row -> (token, head) division limit
 constexpr int kWaves = kThreads / 64;
 constexpr int kFwdTableBytes = 32768;  // forward table per workgroup (one entry per element)
+// Table entries (pairs, two 16-byte elements each) per thread, at most: the
+// forward's one table, or each of the backward's two of kMaxTableBytes.
+constexpr int kFwdEnt = kFwdTableBytes / 32 / kThreads;
+constexpr int kBwdEnt = kMaxTableBytes / 32 / kThreads;
 // Backward workgroups, each looping over a contiguous run of tiles: four
 // times as many as the 256 compute units hold at once (3 per unit at the
 // 16-bit kernels' 168 VGPRs, 4 for float32).  Units that run ahead then take
@@ -215,78 +224,84 @@ __device__ __forceinline__ bool fwd_chunk(const u32x4& own, const u32x4& pr, dou
   return tie;
 }
 
-// The incoming gradient of one chunk rotated by -angle (the table holds
-// -sin; pr is the rotate_half partner chunk, already negated in the first
-// half): dn[j] for the chunk's elements j.
+// The incoming gradient of one chunk rotated by -angle, from the per-element
+// table (A_e, B_e): v_e = dy_e A_e + dy_p B_e, p the pair partner of element
+// e (rotate_half: the same element of the partner chunk pr; interleaved: its
+// neighbour in the chunk).  With the weights folded into the table
+// (A_e = w_e cos, B_e = -+w_e sin) v is g = w dn; with unit weights it is dn.
+// tab: the chunk's first entry, consecutive elements L entries apart.
 template <int kDtype, bool kIl>
-__device__ __forceinline__ void bwd_chunk_dn(const u32x4& dy, const u32x4& pr, const double2* cs, int step,
-                                             double* dn) {
+__device__ __forceinline__ void bwd_chunk_rot(const u32x4& dy, const u32x4& pr, const double2* tab, int L,
+                                              double* v) {
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const f64x2 dv = element_pair<kDtype>(dy, d);
     if constexpr (kDtype == ROPE_QK_FP32) {
-      if constexpr (kIl) {
-        const f64x2 dz = element_pair<kDtype>(dy, d ^ 1);
-        const double2 c = cs[(d >> 1) * step];
-        dn[d] = (d & 1) ? fma(dv.x, c.x, dz.x * c.y) : fma(dv.x, c.x, -(dz.x * c.y));
-      } else {
-        const f64x2 pv = element_pair<kDtype>(pr, d);
-        const double2 c = cs[d * step];
-        dn[d] = fma(dv.x, c.x, pv.x * c.y);
-      }
+      const double dp = kIl ? element_pair<kDtype>(dy, d ^ 1).x : element_pair<kDtype>(pr, d).x;
+      const double2 c = tab[d * L];
+      v[d] = fma(dv.x, c.x, dp * c.y);
     } else {
+      double p0, p1;
       if constexpr (kIl) {
-        const double2 c = cs[d * step];
-        dn[2 * d] = fma(dv.x, c.x, -(dv.y * c.y));
-        dn[2 * d + 1] = fma(dv.y, c.x, dv.x * c.y);
+        p0 = dv.y;
+        p1 = dv.x;
       } else {
         const f64x2 pv = element_pair<kDtype>(pr, d);
-        const double2 c0 = cs[(2 * d) * step];
-        const double2 c1 = cs[(2 * d + 1) * step];
-        dn[2 * d] = fma(dv.x, c0.x, pv.x * c0.y);
-        dn[2 * d + 1] = fma(dv.y, c1.x, pv.y * c1.y);
+        p0 = pv.x;
+        p1 = pv.y;
       }
+      const double2 c0 = tab[(2 * d) * L];
+      const double2 c1 = tab[(2 * d + 1) * L];
+      v[2 * d] = fma(dv.x, c0.x, p0 * c0.y);
+      v[2 * d + 1] = fma(dv.y, c1.x, p1 * c1.y);
     }
   }
 }
 
-// Backward of one chunk, first part: sum_j g_j x_j over its elements, with
-// g = dn * w.
-template <int kDtype>
-__device__ __forceinline__ double bwd_chunk_gx(const u32x4& x, const double* dn, const float* w_own) {
+// Backward of one chunk, first part: sum_j g_j x_j over its elements.  kFold:
+// v is g already; otherwise v is dn and g = dn w.
+template <int kDtype, bool kFold>
+__device__ __forceinline__ double bwd_chunk_gx(const u32x4& x, const double* v, const float* w_own) {
   double gx = 0.0;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const f64x2 xv = element_pair<kDtype>(x, d);
     if constexpr (kDtype == ROPE_QK_FP32) {
-      gx = fma(dn[d] * static_cast<double>(w_own[d]), xv.x, gx);
+      gx = fma(kFold ? v[d] : v[d] * static_cast<double>(w_own[d]), xv.x, gx);
     } else {
-      gx = fma(dn[2 * d] * static_cast<double>(w_own[2 * d]), xv.x, gx);
-      gx = fma(dn[2 * d + 1] * static_cast<double>(w_own[2 * d + 1]), xv.y, gx);
+      gx = fma(kFold ? v[2 * d] : v[2 * d] * static_cast<double>(w_own[2 * d]), xv.x, gx);
+      gx = fma(kFold ? v[2 * d + 1] : v[2 * d + 1] * static_cast<double>(w_own[2 * d + 1]), xv.y, gx);
     }
   }
   return gx;
 }
 
-// Backward of one chunk, second part: dx_j = r (g_j - x_j coef), rounded,
-// and (when acc is given) dn_j x_j r added to acc.
-template <int kDtype, bool kExact>
-__device__ __forceinline__ bool bwd_chunk_dx(const u32x4& x, const double* dn, const float* w_own, double r,
+// Backward of one chunk, second part: dx_j = r g_j - (x_j r) coef (that is
+// r (g_j - x_j coef)), rounded, and (on the fast pass, not the exact redo)
+// the weight-gradient term v_j x_j r added to acc: dn x r without the fold,
+// w dn x r with it (the sums are divided by w once at the end).
+template <int kDtype, bool kExact, bool kFold>
+__device__ __forceinline__ bool bwd_chunk_dx(const u32x4& x, const double* v, const float* w_own, double r,
                                              double coef, double* acc, u32x4& out) {
   bool tie = false;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const f64x2 xv = element_pair<kDtype>(x, d);
     if constexpr (kDtype == ROPE_QK_FP32) {
-      out[d] = __float_as_uint(static_cast<float>(r * (dn[d] * static_cast<double>(w_own[d]) - xv.x * coef)));
-      if (acc) acc[d] = fma(dn[d] * xv.x, r, acc[d]);
+      const double xr = xv.x * r;
+      const double g = kFold ? v[d] : v[d] * static_cast<double>(w_own[d]);
+      out[d] = __float_as_uint(static_cast<float>(fma(-xr, coef, r * g)));
+      if constexpr (!kExact) acc[d] = fma(v[d], xr, acc[d]);
     } else {
-      const double y0 = r * (dn[2 * d] * static_cast<double>(w_own[2 * d]) - xv.x * coef);
-      const double y1 = r * (dn[2 * d + 1] * static_cast<double>(w_own[2 * d + 1]) - xv.y * coef);
+      const double xr0 = xv.x * r, xr1 = xv.y * r;
+      const double g0 = kFold ? v[2 * d] : v[2 * d] * static_cast<double>(w_own[2 * d]);
+      const double g1 = kFold ? v[2 * d + 1] : v[2 * d + 1] * static_cast<double>(w_own[2 * d + 1]);
+      const double y0 = fma(-xr0, coef, r * g0);
+      const double y1 = fma(-xr1, coef, r * g1);
       out[d] = kExact ? pack16_exact<kDtype>(y0, y1) : pack16_fast<kDtype>(y0, y1, tie);
-      if (acc) {
-        acc[2 * d] = fma(dn[2 * d] * xv.x, r, acc[2 * d]);
-        acc[2 * d + 1] = fma(dn[2 * d + 1] * xv.y, r, acc[2 * d + 1]);
+      if constexpr (!kExact) {
+        acc[2 * d] = fma(v[2 * d], xr0, acc[2 * d]);
+        acc[2 * d + 1] = fma(v[2 * d + 1], xr1, acc[2 * d + 1]);
       }
     }
   }
@@ -386,9 +401,10 @@ __device__ __forceinline__ void tile_loads(const NormParams& p, const TileGeom& 
 }
 
 // This thread's table entries e = tid + v * 256 of a tile: token and pair.
+template <int kE>
 __device__ __forceinline__ void tile_entries(const NormParams& p, const TileGeom& gm, int* tt_e, int* i_e) {
 #pragma unroll
-  for (int v = 0; v < kEnt; ++v) {
+  for (int v = 0; v < kE; ++v) {
     const int e = threadIdx.x + v * kThreads;
     const int tt = e < gm.nent ? static_cast<int>(div_small(static_cast<uint32_t>(e), p.magic_half)) : 0;
     tt_e[v] = tt;
@@ -435,25 +451,25 @@ __device__ __forceinline__ void tile_table(const NormParams& p, const TileGeom& 
                                            const SeqCursor& sc, int32_t* s_pos, double2* s_cs,
                                            int32_t* pos_out = nullptr) {
   constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;
-  constexpr int kPPC = kIl ? kVec / 2 : kVec;
-  constexpr int L = kL, hl = kL / 2;
+  constexpr int L = kL;
+  constexpr int kE = kBwd ? kBwdEnt : kFwdEnt;
   const cu_ptr cu = (cu_ptr)p.cu;
   const int32_t nseq = p.nseq;
   const int64_t cu_last = cu[nseq];
   const int64_t cu_first_end = nseq >= 1 ? static_cast<int64_t>(cu[1]) : INT64_MIN;  // cu[1] exists only then
-  int64_t start[kEnt];
+  int64_t start[kE];
 #pragma unroll
-  for (int v = 0; v < kEnt; ++v) start[v] = sc.start0;
+  for (int v = 0; v < kE; ++v) start[v] = sc.start0;
   // the sequence starts inside the tile
   int64_t cv = sc.next;
   for (int32_t j = sc.s0 + 1; cv < gm.t_end;) {
 #pragma unroll
-    for (int v = 0; v < kEnt; ++v) start[v] = cv <= gm.t0 + tt_e[v] ? cv : start[v];
+    for (int v = 0; v < kE; ++v) start[v] = cv <= gm.t0 + tt_e[v] ? cv : start[v];
     ++j;
     cv = j <= nseq ? static_cast<int64_t>(cu[j]) : INT64_MAX;
   }
 #pragma unroll
-  for (int v = 0; v < kEnt; ++v) {
+  for (int v = 0; v < kE; ++v) {
     if (v > 0 && v * kThreads >= gm.nent) break;
     const int e = threadIdx.x + v * kThreads;
     const int64_t t = gm.t0 + tt_e[v];
@@ -467,27 +483,35 @@ __device__ __forceinline__ void tile_table(const NormParams& p, const TileGeom& 
         if (e == 0) pos_out[0] = static_cast<int32_t>(gm.t0);
         continue;
       }
+      // one entry per element: element e of token tt at (tt * kVec + e % kVec) * L + e / kVec
+      const int e1 = kIl ? 2 * i_e[v] : i_e[v];
+      const int e2 = kIl ? 2 * i_e[v] + 1 : i_e[v] + p.half;
+      double2* slot1 = s_cs + (tt_e[v] * kVec + e1 % kVec) * L + e1 / kVec;
+      double2* slot2 = s_cs + (tt_e[v] * kVec + e2 % kVec) * L + e2 / kVec;
       if (pos >= 0) {
         double sn, cs;
         const double ang = p.freq_fp32 ? static_cast<double>(static_cast<float>(pos) * static_cast<float>(f[v]))
                                        : static_cast<double>(pos) * f[v];
         rope_sincos(ang, &sn, &cs);
+        const double a = static_cast<double>(w1[v]), b = static_cast<double>(w2[v]);
         if constexpr (kBwd) {
-          s_cs[cs_slot(tt_e[v], i_e[v], kPPC, kIl ? L : hl)] = make_double2(cs, p.sign * sn);
+          // the rotation by -angle (p.sign = -1: the first element of a pair
+          // takes +sin times its partner, the second -sin), each entry
+          // scaled by its own element's weight (1 when not folded)
+          const double s2 = p.sign * sn;
+          *slot1 = make_double2(a * cs, -(a * s2));
+          *slot2 = make_double2(b * cs, b * s2);
         } else {
-          // one entry per element: element e of token tt at (tt * kVec + e % kVec) * L + e / kVec
-          const int e1 = kIl ? 2 * i_e[v] : i_e[v];
-          const int e2 = kIl ? 2 * i_e[v] + 1 : i_e[v] + p.half;
-          const double a = static_cast<double>(w1[v]), b = static_cast<double>(w2[v]);
-          s_cs[(tt_e[v] * kVec + e1 % kVec) * L + e1 / kVec] = make_double2(a * cs, -(b * sn));
-          s_cs[(tt_e[v] * kVec + e2 % kVec) * L + e2 / kVec] = make_double2(b * cs, a * sn);
+          *slot1 = make_double2(a * cs, -(b * sn));
+          *slot2 = make_double2(b * cs, a * sn);
         }
       } else if constexpr (kBwd) {
         // a token in no sequence: its rows enter the backward as zeros and
         // must stay zeros through the rotation, so its entries are the
         // identity rather than whatever an earlier kernel left in this LDS
         // (0 times a stale NaN would reach the weight-gradient sums)
-        s_cs[cs_slot(tt_e[v], i_e[v], kPPC, kIl ? L : hl)] = make_double2(1.0, 0.0);
+        *slot1 = make_double2(1.0, 0.0);
+        *slot2 = make_double2(1.0, 0.0);
       }
     }
   }
@@ -497,13 +521,14 @@ __device__ __forceinline__ void tile_table(const NormParams& p, const TileGeom& 
 // Every row of a tile (after its table): r for all rows (their lane sums
 // together), then the forward rows one at a time, or the backward in phases;
 // then the stores.  s_w holds both tensors' weights (q then k); acc
-// (backward) receives this lane's weight-gradient terms.
-template <int kDtype, bool kIl, bool kBwd, int kTPT, int kL>
+// (backward) receives this lane's weight-gradient terms.  kFold (backward):
+// the table carries the weights, so the rotation gives g = w dn directly and
+// acc receives w dn x r.
+template <int kDtype, bool kIl, bool kBwd, int kTPT, int kL, bool kFold = false>
 __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom& gm, const TileData<kTPT>& d,
                                              const int32_t* s_pos, const double2* s_cs, const float* s_w,
                                              double* acc) {
   constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;  // elements per chunk
-  constexpr int kPPC = kIl ? kVec / 2 : kVec;          // table pairs per chunk
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   constexpr int L = kL, hl = kL / 2;
@@ -513,7 +538,6 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
   const int* tt_of = d.tt_of;
   const bool* act = d.act;
   const int paddr = (lane ^ hl) << 2;  // rotate_half partner lane
-  const bool first = c < hl;
   const bool copy = tn.copy != 0;
   bool st[kTPT], inside[kTPT];
   u32x4 out[kTPT];
@@ -549,23 +573,21 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
       out[u] = inside[u] ? y : a[u];
     }
   } else {
-    const float* w_own = s_w + sel * (kL * kVec) + c * kVec;
-    const int step = kIl ? L : hl;
-    // dn stays in registers from the first pass to the second; the
-    // weight-gradient terms are added in the second, where x is unpacked
-    // again anyway (in the first they kept x's float64 values live longer:
-    // 185 against 168 VGPRs, 2 against 3 waves per SIMD)
+    const float* w_own = s_w + sel * (kL * kVec) + c * kVec;  // read only when not folded
+    // v (g when folded, else dn) stays in registers from the first pass to
+    // the second; the weight-gradient terms are added in the second, where x
+    // is unpacked again anyway (in the first they kept x's float64 values
+    // live longer: 185 against 168 VGPRs, 2 against 3 waves per SIMD)
     double gx[kTPT];
-    double dn[kTPT][kVec];
+    double v[kTPT][kVec];
 #pragma unroll
     for (int u = 0; u < kTPT; ++u) {
       __builtin_amdgcn_sched_barrier(0);
-      const int tt = tt_of[u];
-      const double2* cs = kIl ? s_cs + tt * kPPC * L + c : s_cs + tt * kPPC * hl + (c & (hl - 1));
+      const double2* tab = s_cs + tt_of[u] * kVec * L + c;
       u32x4 pr = g[u];
-      if constexpr (!kIl) pr = partner_chunk<kDtype>(g[u], paddr, first);
-      bwd_chunk_dn<kDtype, kIl>(g[u], pr, cs, step, dn[u]);
-      gx[u] = bwd_chunk_gx<kDtype>(a[u], dn[u], w_own);
+      if constexpr (!kIl) pr = partner_chunk<kDtype>(g[u], paddr, false);  // signs are in the table
+      bwd_chunk_rot<kDtype, kIl>(g[u], pr, tab, L, v[u]);
+      gx[u] = bwd_chunk_gx<kDtype, kFold>(a[u], v[u], w_own);
     }
     __builtin_amdgcn_sched_barrier(0);
     row_sums<kTPT, kL>(gx, lane);
@@ -574,8 +596,8 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
       __builtin_amdgcn_sched_barrier(0);
       const double coef = (r[u] * r[u]) * (gx[u] * p.inv_d);
       u32x4 y;
-      if (bwd_chunk_dx<kDtype, false>(a[u], dn[u], w_own, r[u], coef, acc, y))
-        bwd_chunk_dx<kDtype, true>(a[u], dn[u], w_own, r[u], coef, nullptr, y);
+      if (bwd_chunk_dx<kDtype, false, kFold>(a[u], v[u], w_own, r[u], coef, acc, y))
+        bwd_chunk_dx<kDtype, true, kFold>(a[u], v[u], w_own, r[u], coef, acc, y);
       out[u] = inside[u] ? y : d.g[u];
     }
   }
@@ -594,12 +616,12 @@ __device__ __forceinline__ void fwd_tile(const NormParams& p, uint32_t tile, int
                                          int32_t* pos_out = nullptr) {
   const TileGeom gm = tile_geom(p, tile);
   const NormTensor& tn = p.ten[gm.sel];
-  int tt_e[kEnt], i_e[kEnt];
-  tile_entries(p, gm, tt_e, i_e);
-  double f[kEnt];
-  float w1[kEnt], w2[kEnt];
+  int tt_e[kFwdEnt], i_e[kFwdEnt];
+  tile_entries<kFwdEnt>(p, gm, tt_e, i_e);
+  double f[kFwdEnt];
+  float w1[kFwdEnt], w2[kFwdEnt];
 #pragma unroll
-  for (int v = 0; v < kEnt; ++v) {
+  for (int v = 0; v < kFwdEnt; ++v) {
     const bool live = v == 0 || v * kThreads < gm.nent;
     f[v] = live ? p.inv_freq[i_e[v]] : 0.0;
     if constexpr (kPosOnly) {  // the hook has no weights
@@ -688,37 +710,17 @@ __device__ __forceinline__ void flush_dw(const NormParams& p, int sel, const dou
   __syncthreads();
 }
 
-// Backward: gridDim.x workgroups, each taking a contiguous run of tiles; the
-// weights and frequencies sit in LDS for all of a workgroup's tiles.
-// Consecutive tiles alternate between two tables, so one barrier per tile
-// (after its table) suffices: a wave that writes table b for tile i has passed
-// tile i - 1's barrier, which every wave reaches only after its tile i - 2
-// work, the last reader of table b.  The weight-gradient terms stay in
-// registers while the tiles are of one tensor (q's tiles come first, so that
-// changes at most once) and are summed across the workgroup only then and at
-// the end.
-// kPosOnly (the positions test hook): the same runs of tiles and the same
-// sequence cursor, writing each tile's first token and positions to row
-// `tile` of p.pos_rows; nothing is loaded, computed or stored.
-template <int kDtype, bool kIl, int kTPT, int kL, bool kPosOnly = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBwdWaves16)))
-void rope_qk_norm_bwd_kernel(const NormParams p) {
+// The loop of the backward kernel over its workgroup's run of tiles, then
+// the workgroup's weight-gradient sums.  kFold: the tables carry the weights
+// (see rope_qk_norm_bwd_kernel).  Instantiated once per kFold, so that each
+// loop gets its own register allocation.
+template <int kDtype, bool kIl, int kTPT, int kL, bool kPosOnly, bool kFold>
+__device__ __forceinline__ void bwd_runs(const NormParams& p, int32_t (*s_pos)[kMaxTileTokens], double2* s_cs,
+                                         float* s_w, double* s_acc, double* s_wave, double* s_freq) {
   constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;
-  __shared__ int32_t s_pos[2][kMaxTileTokens];
-  extern __shared__ double2 s_cs[];
   const int tab_len = p.table_bytes / static_cast<int>(sizeof(double2));  // entries per table
-  float* s_w = lds_weights(s_cs, p, 2);
-  double* s_acc = reinterpret_cast<double*>(s_w + 2 * p.D);  // [2 D]
-  double* s_wave = s_acc + 2 * p.D;                          // [kWaves][D]
-  double* s_freq = s_wave + kWaves * p.D;                    // [D / 2]
   const int tid = threadIdx.x;
   const int D = p.D;
-  if constexpr (!kPosOnly) {
-    load_weights(p, s_w);
-    for (int i = tid; i < 2 * D; i += kThreads) s_acc[i] = 0.0;
-    for (int i = tid; i < p.half; i += kThreads) s_freq[i] = p.inv_freq[i];
-    __syncthreads();
-  }
   double acc[kVec];
 #pragma unroll
   for (int j = 0; j < kVec; ++j) acc[j] = 0.0;
@@ -750,25 +752,87 @@ void rope_qk_norm_bwd_kernel(const NormParams p) {
       sc = seq_cursor(p, last_start_at_or_before((cu_ptr)p.cu, p.nseq, gm.t0));
     else
       seq_advance(p, sc, gm.t0);
-    int tt_e[kEnt], i_e[kEnt];
-    double f[kEnt];
-    tile_entries(p, gm, tt_e, i_e);
+    int tt_e[kBwdEnt], i_e[kBwdEnt];
+    double f[kBwdEnt];
+    float w1[kBwdEnt], w2[kBwdEnt];
+    tile_entries<kBwdEnt>(p, gm, tt_e, i_e);
 #pragma unroll
-    for (int v = 0; v < kEnt; ++v) f[v] = kPosOnly ? 0.0 : s_freq[i_e[v]];
+    for (int v = 0; v < kBwdEnt; ++v) {
+      f[v] = kPosOnly ? 0.0 : s_freq[i_e[v]];
+      const float* wt = s_w + gm.sel * D;
+      w1[v] = kFold ? wt[kIl ? 2 * i_e[v] : i_e[v]] : 1.f;
+      w2[v] = kFold ? wt[kIl ? 2 * i_e[v] + 1 : i_e[v] + p.half] : 1.f;
+    }
     if constexpr (kPosOnly) {
-      tile_table<kDtype, kIl, true, kL, true>(p, gm, tt_e, i_e, f, nullptr, nullptr, sc, s_pos[b], nullptr,
+      tile_table<kDtype, kIl, true, kL, true>(p, gm, tt_e, i_e, f, w1, w2, sc, s_pos[b], nullptr,
                                               p.pos_rows + static_cast<int64_t>(tile) * p.pos_row_len);
     } else {
-      tile_table<kDtype, kIl, true, kL>(p, gm, tt_e, i_e, f, nullptr, nullptr, sc, s_pos[b], s_cs + b * tab_len);
-      tile_compute<kDtype, kIl, true, kTPT, kL>(p, gm, d, s_pos[b], s_cs + b * tab_len, s_w, acc);
+      tile_table<kDtype, kIl, true, kL>(p, gm, tt_e, i_e, f, w1, w2, sc, s_pos[b], s_cs + b * tab_len);
+      tile_compute<kDtype, kIl, true, kTPT, kL, kFold>(p, gm, d, s_pos[b], s_cs + b * tab_len, s_w, acc);
     }
     b ^= 1;
   }
   if constexpr (!kPosOnly) {
     if (cur >= 0) flush_dw<kVec, kL>(p, cur, acc, s_wave, s_acc);
     double* dst = p.partial + static_cast<int64_t>(blockIdx.x) * 2 * D;
-    for (int i = tid; i < 2 * D; i += kThreads) dst[i] = s_acc[i];
+    for (int i = tid; i < 2 * D; i += kThreads) {
+      double sum = s_acc[i];
+      if (kFold && p.ten[i < D ? 0 : 1].H > 0) sum /= static_cast<double>(s_w[i]);  // sums of w dn x r
+      dst[i] = sum;
+    }
   }
+}
+
+// Backward: gridDim.x workgroups, each taking a contiguous run of tiles; the
+// weights and frequencies sit in LDS for all of a workgroup's tiles.
+// Consecutive tiles alternate between two tables, so one barrier per tile
+// (after its table) suffices: a wave that writes table b for tile i has passed
+// tile i - 1's barrier, which every wave reaches only after its tile i - 2
+// work, the last reader of table b.  The weight-gradient terms stay in
+// registers while the tiles are of one tensor (q's tiles come first, so that
+// changes at most once) and are summed across the workgroup only then and at
+// the end.
+// kPosOnly (the positions test hook): the same runs of tiles and the same
+// sequence cursor, writing each tile's first token and positions to row
+// `tile` of p.pos_rows; nothing is loaded, computed or stored.
+template <int kDtype, bool kIl, int kTPT, int kL, bool kPosOnly = false>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kBwdWaves16)))
+void rope_qk_norm_bwd_kernel(const NormParams p) {
+  __shared__ int32_t s_pos[2][kMaxTileTokens];
+  extern __shared__ double2 s_cs[];
+  float* s_w = lds_weights(s_cs, p, 2);
+  double* s_acc = reinterpret_cast<double*>(s_w + 2 * p.D);  // [2 D]
+  double* s_wave = s_acc + 2 * p.D;                          // [kWaves][D]
+  double* s_freq = s_wave + kWaves * p.D;                    // [D / 2]
+  const int tid = threadIdx.x;
+  const int D = p.D;
+  if constexpr (!kPosOnly) {
+    load_weights(p, s_w);
+    for (int i = tid; i < 2 * D; i += kThreads) s_acc[i] = 0.0;
+    for (int i = tid; i < p.half; i += kThreads) s_freq[i] = p.inv_freq[i];
+    __syncthreads();
+  }
+  // Fold the weights into the tables when every weight of a tensor with
+  // heads is finite and nonzero (the usual case): the rotation then yields
+  // g = w dn directly, and the weight-gradient sums of w dn x r are divided
+  // by w at the end.  Otherwise dn is rotated with unit weights and
+  // multiplied by w.  Every wave reads all weights itself (wave-uniform, no
+  // barrier).
+  bool fold = false;
+  if constexpr (!kPosOnly) {
+    bool bad = false;
+    for (int i = tid & 63; i < 2 * D; i += 64) {
+      const float w = s_w[i];
+      bad |= p.ten[i < D ? 0 : 1].H > 0 && !(w != 0.f && fabsf(w) < __builtin_inff());
+    }
+    fold = __ballot(bad) == 0;
+  }
+  if constexpr (kPosOnly)
+    bwd_runs<kDtype, kIl, kTPT, kL, true, false>(p, s_pos, s_cs, s_w, s_acc, s_wave, s_freq);
+  else if (fold)
+    bwd_runs<kDtype, kIl, kTPT, kL, false, true>(p, s_pos, s_cs, s_w, s_acc, s_wave, s_freq);
+  else
+    bwd_runs<kDtype, kIl, kTPT, kL, false, false>(p, s_pos, s_cs, s_w, s_acc, s_wave, s_freq);
 }
 
 // The weight gradients: one column of the workgroups' sums per workgroup,
@@ -828,9 +892,8 @@ int norm_geometry(int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int dtype, bool
   const int64_t L = D * esz / 16;
   if ((D * esz) % 16 || L < 2 || L > 64 || (L & (L - 1))) return ROPE_QK_ERR_SHAPE;
   if (Hq > kMaxHeads || Hkv > kMaxHeads) return ROPE_QK_ERR_SHAPE;
-  // table bytes per token: the backward keeps (cos, -sin) per pair, the
-  // forward (w cos, +-w' sin) per element
-  const int64_t per_token = s_bwd ? D / 2 * 16 : D * 16;
+  // table bytes per token: one (cos, sin) entry per element, scaled by weights
+  const int64_t per_token = D * 16;
   int64_t cap_tokens = (s_bwd ? kMaxTableBytes : kFwdTableBytes) / per_token;
   if (cap_tokens > kMaxTileTokens) cap_tokens = kMaxTileTokens;
   g->L = L;

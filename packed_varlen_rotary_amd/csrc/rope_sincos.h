@@ -11,8 +11,9 @@
 // The reduced argument r lies in [-pi/4, pi/4] (up to rounding of k) and is
 // accurate to a few units of 2^-54 in absolute terms.  sin r and cos r are
 // the Taylor series through r^19 and r^20 (first omitted terms below 1e-21
-// on |r| <= 0.8), evaluated by Horner's rule with fused multiply-adds; the
-// coefficients are 1/n! rounded to float64.  The constants were derived from
+// on |r| <= 0.8), evaluated by Horner's rule with fused multiply-adds after
+// a first step of a multiply and an add; the coefficients are 1/n! rounded
+// to float64.  The constants were derived from
 // pi and n! directly (mpmath at 400 bits).
 //
 // Exact at x = 0: sin 0 = 0 and cos 0 = 1, so position 0 is the identity.
@@ -43,6 +44,19 @@ ROPE_HD double rope_fma_k(double a, double b, double c) {
 #endif
 }
 
+// a * k + c for constants k and c, rounded twice (a multiply, then an add):
+// the first Horner step of a series.  As one FMA it would need one of its two
+// constants in a vector register (an instruction reads at most one scalar
+// register), which the compiler then keeps live across a whole loop of
+// tables.  The highest-order term it rounds is below 2^-60 of the result.
+ROPE_HD double rope_mul_add_k(double a, double k, double c) {
+#if defined(__clang__)
+#pragma clang fp contract(off)
+#endif
+  const double t = a * k;
+  return t + c;
+}
+
 ROPE_HD void rope_sincos(double x, double* s_out, double* c_out) {
   const double kTwoOverPi = 0x1.45f306dc9c883p-1;
   const double kP1 = 0x1.921fb00000000p+0;   // pi/2, leading 21 bits
@@ -54,8 +68,8 @@ ROPE_HD void rope_sincos(double x, double* s_out, double* c_out) {
   r = fma(-k, kP3, r);
   const double z = r * r;
   // sin r = r (1 - z/3! + z^2/5! - ... - z^9/19!)
-  double ps = -0x1.2f49b46814157p-57;             // -1/19!
-  ps = rope_fma_k(ps, z, 0x1.952c77030ad4ap-49);         // +1/17!
+  double ps = rope_mul_add_k(z, -0x1.2f49b46814157p-57,  // -1/19!
+                             0x1.952c77030ad4ap-49);  // +1/17!
   ps = rope_fma_k(ps, z, -0x1.ae7f3e733b81fp-41);        // -1/15!
   ps = rope_fma_k(ps, z, 0x1.6124613a86d09p-33);         // +1/13!
   ps = rope_fma_k(ps, z, -0x1.ae64567f544e4p-26);        // -1/11!
@@ -65,8 +79,8 @@ ROPE_HD void rope_sincos(double x, double* s_out, double* c_out) {
   ps = rope_fma_k(ps, z, -0x1.5555555555555p-3);         // -1/3!
   const double sr = fma(ps * z, r, r);
   // cos r = 1 - z/2! + z^2/4! - ... + z^10/20!
-  double pc = 0x1.e542ba4020225p-62;              // +1/20!
-  pc = rope_fma_k(pc, z, -0x1.6827863b97d97p-53);        // -1/18!
+  double pc = rope_mul_add_k(z, 0x1.e542ba4020225p-62,   // +1/20!
+                             -0x1.6827863b97d97p-53);  // -1/18!
   pc = rope_fma_k(pc, z, 0x1.ae7f3e733b81fp-45);         // +1/16!
   pc = rope_fma_k(pc, z, -0x1.93974a8c07c9dp-37);        // -1/14!
   pc = rope_fma_k(pc, z, 0x1.1eed8eff8d898p-29);         // +1/12!

@@ -123,12 +123,16 @@ def test_norm_fwd_options(dt, opts):
     run_fwd(q, k, weights(D, 5), weights(D, 6), [0, 100, 100, 290], 5e5, True, **opts)
 
 
-def run_bwd(T, Hq, Hkv, D, dt, cu, theta, seed, in_place, **opts):
+def run_bwd(T, Hq, Hkv, D, dt, cu, theta, seed, in_place, zero_w=None, **opts):
+    """zero_w: {"q": [elements], "k": [...]} set to exactly 0 in that tensor's weights."""
     q = W.randn((T, Hq, D), dt, seed=seed, device=DEV)
     k = W.randn((T, Hkv, D), dt, seed=seed + 1, device=DEV)
     dyq = W.randn((T, Hq, D), dt, seed=seed + 2, device=DEV)
     dyk = W.randn((T, Hkv, D), dt, seed=seed + 3, device=DEV)
     wq, wk = weights(D, seed + 4), weights(D, seed + 5)
+    for name, w in (("q", wq), ("k", wk)):
+        for j in (zero_w or {}).get(name, []):
+            w[j] = 0.0
     xq, xk, gq, gk = f64(q), f64(k), f64(dyq), f64(dyk)
     if in_place:
         dq, dk = dyq, dyk
@@ -158,6 +162,46 @@ def test_norm_bwd_shapes(shape):
                          ids=["plain", "interleaved", "offset_llama3_fp32"])
 def test_norm_bwd_out_of_place_and_options(opts):
     run_bwd(700, 8, 2, 128, "bf16", [3, 100, 100, 620, 690], 5e5, seed=91, in_place=False, **opts)
+
+
+@pytest.mark.parametrize("which", ["q", "k"])
+@pytest.mark.parametrize("shape", [(300, 6, 2, 128, "bf16", {}), (257, 5, 3, 64, "fp16", {}),
+                                   (300, 6, 2, 64, "fp32", {}), (300, 6, 2, 128, "bf16", dict(interleaved=True))],
+                         ids=lambda s: f"T{s[0]}_H{s[1]}x{s[2]}_D{s[3]}_{s[4]}_{'il' if s[5] else 'half'}")
+def test_norm_bwd_zero_weights(shape, which):
+    """With every weight finite and nonzero the backward folds the weights
+    into its cos/sin tables (the rotation of dy then gives w dn directly, and
+    the weight-gradient sums of w dn x r are divided by w at the end).  A
+    weight of exactly zero, in q's vector or in k's, rules that out: the
+    kernel then rotates with unit weights and multiplies by w.  Zeros on an
+    element, on its rotation partner and on one more: dx bit-exact (g is 0
+    there) and the weight gradients, nonzero where w is 0, against the oracle."""
+    T, Hq, Hkv, D, dt, opts = shape
+    zeros = [0, 1 if opts.get("interleaved") else D // 2, 5]
+    s = run_bwd(T, Hq, Hkv, D, dt, [0, 1, T // 3, T // 3, T - 5], 1e4, seed=D + T, in_place=False,
+                zero_w={which: zeros}, **opts)
+    if dt != "fp32":
+        assert s["q"]["exact_fraction"] == 1.0 and s["k"]["exact_fraction"] == 1.0, s
+
+
+def test_norm_bwd_tensor_without_heads():
+    """k with no heads: its weight vector (all zeros here) plays no part, so
+    q's backward still folds its weights; q's results match the oracle and
+    k's weight gradient is zero."""
+    T, Hq, D = 300, 6, 128
+    cu = [0, 1, 100, 100, 295]
+    q = W.randn((T, Hq, D), "bf16", seed=61, device=DEV)
+    dyq = W.randn((T, Hq, D), "bf16", seed=62, device=DEV)
+    k = torch.empty((T, 0, D), dtype=torch.bfloat16, device=DEV)
+    wq, wk = weights(D, 63), torch.zeros(D, dtype=torch.float32, device=DEV)
+    dq, dk, dwq, dwk = P.rope_qk_norm_bwd(dyq.clone(), k.clone(), q, k, wq, wk, EPS, cu_dev(cu), 1e4)
+    torch.cuda.synchronize()
+    o = oracle_opts({})
+    rdx, rdw = oracle.norm_rope_bwd(f64(dyq), f64(q), w64(wq), EPS, cu, 1e4, **o)
+    s = check_against(dq, rdx, "dq without k heads")
+    assert s["exact_fraction"] == 1.0, s
+    check_dw(dwq, rdw, dw_terms(f64(dyq), f64(q), w64(wq), cu, 1e4, o), "dwq without k heads")
+    assert torch.equal(dwk, torch.zeros_like(dwk))
 
 
 @pytest.mark.parametrize("shape", [(2000, 6, 2, 128, "bf16"), (1500, 1, 1, 64, "bf16"), (900, 40, 8, 128, "fp16"),
