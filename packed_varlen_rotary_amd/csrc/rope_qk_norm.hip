@@ -12,20 +12,22 @@
 // Design (HBM-bound like the rotation: the forward reads and writes each
 // element once, the backward reads x and dy and writes dx):
 //
-//  * Row tiles.  A row is one head of one token: D elements in L = D*size/16
-//    chunks of 16 bytes, L a power of two from 2 to 64.  Lane l of a
-//    workgroup holds chunk l % L of row u * (256 / L) + l / L of the tile, for
-//    u < kTPT, so the chunks of a row sit on L consecutive lanes of one wave
-//    and each wave-wide load or store covers whole rows.  A tile is a run of
+//  * Row tiles.  A row is one head of one token: D elements, 16 bytes of it
+//    per lane on L = D*size/16 lanes, L a power of two from 2 to 64.  Lane l
+//    of a workgroup holds part l % L of row u * (256 / L) + l / L of the
+//    tile, for u < kTPT, so a row sits on L consecutive lanes of one wave and
+//    each wave-wide load or store covers whole rows.  Interleaved pairs: the
+//    part is chunk l % L (a pair inside a dword).  rotate_half pairs ("split"
+//    rows): 8 bytes from each half of the row, so that both elements of every
+//    pair sit in the lane and no lane exchange is needed.  A tile is a run of
 //    whole rows in (token, head of q then k) order that may begin and end
 //    inside a token.
 //  * Per row: the sum of squares in float64, summed over the row's lanes by
 //    a xor butterfly (ds_bpermute; every lane ends with the same bits),
 //    r = 1/sqrt(mean + eps) from v_rsq_f64 and two Newton steps, then the
-//    rotation: the rotate_half partner chunk comes from lane l ^ L/2,
-//    interleaved pairs sit inside a chunk; the table, built once per tile,
-//    holds one (A, B) entry per element with the signs (and weights) in it,
-//    so that an element becomes x_e A_e + x_p B_e.
+//    rotation; the table, built once per tile, holds one (A, B) entry per
+//    element with the signs (and weights) in it, so that an element becomes
+//    x_e A_e + x_p B_e.
 //  * A tile holds rows of q only or of k only, so it needs one weight vector
 //    and one set of weight-gradient sums.
 //  * Backward: the rotation by -angle, then the RMSNorm gradient with a
@@ -63,6 +65,21 @@ constexpr int kFwdTableBytes = 32768;  // forward table per workgroup (one entry
 // forward's one table, or each of the backward's two of kMaxTableBytes.
 constexpr int kFwdEnt = kFwdTableBytes / 32 / kThreads;
 constexpr int kBwdEnt = kMaxTableBytes / 32 / kThreads;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) u32x2 gu32x2;
+
+// The elements of its row that a lane holds (kVec of them, 16 bytes).
+// Interleaved pairs: chunk c, elements c kVec + j (a pair inside a dword).
+// rotate_half pairs ("split" rows): kVec / 2 elements from each half, 8 bytes
+// each, so that both elements of every pair sit in the lane: element j <
+// kVec / 2 is c kVec / 2 + j of the first half, j >= kVec / 2 the same
+// element of the second half (the partner of j is j ^ kVec / 2).  The offset
+// of element j from element 0 in the row (half = kL kVec / 2):
+template <bool kSplit, int kVec, int kL>
+__device__ __forceinline__ constexpr int elem_off(int j) {
+  return (kSplit && j >= kVec / 2) ? j - kVec / 2 + kL * kVec / 2 : j;
+}
 // Backward workgroups, each looping over a contiguous run of tiles: four
 // times as many as the 256 compute units hold at once (3 per unit at the
 // 16-bit kernels' 168 VGPRs, 4 for float32).  Units that run ahead then take
@@ -143,18 +160,6 @@ __device__ __forceinline__ f64x2 element_pair(const u32x4& w, int d) {
   } else {
     return unpack16<kDtype>(w[d]);
   }
-}
-
-// The 16-byte chunk lane (addr / 4) holds, with the sign of every element
-// flipped when `neg` (the rotate_half partner of a first-half chunk).
-template <int kDtype>
-__device__ __forceinline__ u32x4 partner_chunk(const u32x4& v, int addr, bool neg) {
-  const uint32_t flip = neg ? (kDtype == ROPE_QK_FP32 ? 0x80000000u : 0x80008000u) : 0u;
-  u32x4 out;
-#pragma unroll
-  for (int d = 0; d < 4; ++d)
-    out[d] = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(addr, static_cast<int>(v[d]))) ^ flip;
-  return out;
 }
 
 // Sum of squares of a chunk's elements, in float64.
@@ -259,18 +264,22 @@ __device__ __forceinline__ void bwd_chunk_rot(const u32x4& dy, const u32x4& pr, 
 }
 
 // Backward of one chunk, first part: sum_j g_j x_j over its elements.  kFold:
-// v is g already; otherwise v is dn and g = dn w.
-template <int kDtype, bool kFold>
+// v is g already; otherwise v is dn and g = dn w, with element j's weight at
+// w_own[kOff(j)] (its offset in the row from the lane's element 0).
+template <int kDtype, bool kFold, bool kSplit, int kL>
 __device__ __forceinline__ double bwd_chunk_gx(const u32x4& x, const double* v, const float* w_own) {
+  constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;
   double gx = 0.0;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const f64x2 xv = element_pair<kDtype>(x, d);
     if constexpr (kDtype == ROPE_QK_FP32) {
-      gx = fma(kFold ? v[d] : v[d] * static_cast<double>(w_own[d]), xv.x, gx);
+      gx = fma(kFold ? v[d] : v[d] * static_cast<double>(w_own[elem_off<kSplit, kVec, kL>(d)]), xv.x, gx);
     } else {
-      gx = fma(kFold ? v[2 * d] : v[2 * d] * static_cast<double>(w_own[2 * d]), xv.x, gx);
-      gx = fma(kFold ? v[2 * d + 1] : v[2 * d + 1] * static_cast<double>(w_own[2 * d + 1]), xv.y, gx);
+      gx = fma(kFold ? v[2 * d] : v[2 * d] * static_cast<double>(w_own[elem_off<kSplit, kVec, kL>(2 * d)]), xv.x,
+               gx);
+      gx = fma(kFold ? v[2 * d + 1] : v[2 * d + 1] * static_cast<double>(w_own[elem_off<kSplit, kVec, kL>(2 * d + 1)]),
+               xv.y, gx);
     }
   }
   return gx;
@@ -280,22 +289,24 @@ __device__ __forceinline__ double bwd_chunk_gx(const u32x4& x, const double* v, 
 // r (g_j - x_j coef)), rounded, and (on the fast pass, not the exact redo)
 // the weight-gradient term v_j x_j r added to acc: dn x r without the fold,
 // w dn x r with it (the sums are divided by w once at the end).
-template <int kDtype, bool kExact, bool kFold>
+template <int kDtype, bool kExact, bool kFold, bool kSplit, int kL>
 __device__ __forceinline__ bool bwd_chunk_dx(const u32x4& x, const double* v, const float* w_own, double r,
                                              double coef, double* acc, u32x4& out) {
+  constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;
   bool tie = false;
 #pragma unroll
   for (int d = 0; d < 4; ++d) {
     const f64x2 xv = element_pair<kDtype>(x, d);
     if constexpr (kDtype == ROPE_QK_FP32) {
       const double xr = xv.x * r;
-      const double g = kFold ? v[d] : v[d] * static_cast<double>(w_own[d]);
+      const double g = kFold ? v[d] : v[d] * static_cast<double>(w_own[elem_off<kSplit, kVec, kL>(d)]);
       out[d] = __float_as_uint(static_cast<float>(fma(-xr, coef, r * g)));
       if constexpr (!kExact) acc[d] = fma(v[d], xr, acc[d]);
     } else {
       const double xr0 = xv.x * r, xr1 = xv.y * r;
-      const double g0 = kFold ? v[2 * d] : v[2 * d] * static_cast<double>(w_own[2 * d]);
-      const double g1 = kFold ? v[2 * d + 1] : v[2 * d + 1] * static_cast<double>(w_own[2 * d + 1]);
+      const double g0 = kFold ? v[2 * d] : v[2 * d] * static_cast<double>(w_own[elem_off<kSplit, kVec, kL>(2 * d)]);
+      const double g1 =
+          kFold ? v[2 * d + 1] : v[2 * d + 1] * static_cast<double>(w_own[elem_off<kSplit, kVec, kL>(2 * d + 1)]);
       const double y0 = fma(-xr0, coef, r * g0);
       const double y1 = fma(-xr1, coef, r * g1);
       out[d] = kExact ? pack16_exact<kDtype>(y0, y1) : pack16_fast<kDtype>(y0, y1, tie);
@@ -353,14 +364,37 @@ __device__ __forceinline__ int64_t mul_u32_wide(uint32_t a, int64_t b) {
   return static_cast<int64_t>(static_cast<uint64_t>(a) * static_cast<uint32_t>(b));
 }
 
+// One row's 16 bytes for this lane: a whole chunk, or (split rows) 8 bytes
+// from each half of the row, the second kL * 8 bytes after the first.
+template <bool kSplit, int kL>
+__device__ __forceinline__ u32x4 row_load(const gchar* ptr) {
+  if constexpr (kSplit) {
+    const u32x2 lo = __builtin_nontemporal_load(reinterpret_cast<const gu32x2*>(ptr));
+    const u32x2 hi = __builtin_nontemporal_load(reinterpret_cast<const gu32x2*>(ptr + kL * 8));
+    return u32x4{lo.x, lo.y, hi.x, hi.y};
+  } else {
+    return __builtin_nontemporal_load(reinterpret_cast<const gu32x4*>(ptr));
+  }
+}
+
+template <bool kSplit, int kL>
+__device__ __forceinline__ void row_store(const u32x4& v, gchar* ptr) {
+  if constexpr (kSplit) {
+    __builtin_nontemporal_store(u32x2{v.x, v.y}, reinterpret_cast<gu32x2*>(ptr));
+    __builtin_nontemporal_store(u32x2{v.z, v.w}, reinterpret_cast<gu32x2*>(ptr + kL * 8));
+  } else {
+    __builtin_nontemporal_store(v, reinterpret_cast<gu32x4*>(ptr));
+  }
+}
+
 // Issue every load of a tile (rows past the tile's end re-read its first row).
-template <bool kBwd, int kTPT, int kL>
+template <bool kBwd, bool kSplit, int kTPT, int kL>
 __device__ __forceinline__ void tile_loads(const NormParams& p, const TileGeom& gm, TileData<kTPT>& d) {
   const int tid = threadIdx.x;
   const NormTensor& tn = p.ten[gm.sel];
   const int32_t H = tn.H;
   constexpr int rows_per_step = kThreads / kL;
-  const int64_t off = static_cast<int64_t>(tid & (kL - 1)) * 16;
+  const int64_t off = static_cast<int64_t>(tid & (kL - 1)) * (kSplit ? 8 : 16);
   if (tn.lin) {
     // token-major rows: row n0 + lr at (n0 + lr) * stride_h, the tile's part
     // of it once per tile
@@ -374,9 +408,8 @@ __device__ __forceinline__ void tile_loads(const NormParams& p, const TileGeom& 
       const uint32_t r = d.act[u] ? static_cast<uint32_t>(lr) : 0u;
       // head strides below 2^32 bytes (checked on the host for this form):
       // each row offset is one 32 x 32 -> 64-bit multiply
-      d.a[u] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4*>(xb + mul_u32_wide(r, tn.x_sh)));
-      if constexpr (kBwd)
-        d.g[u] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4*>(gb + mul_u32_wide(r, tn.g_sh)));
+      d.a[u] = row_load<kSplit, kL>(xb + mul_u32_wide(r, tn.x_sh));
+      if constexpr (kBwd) d.g[u] = row_load<kSplit, kL>(gb + mul_u32_wide(r, tn.g_sh));
       d.optr[u] = ob + mul_u32_wide(r, tn.o_sh);
       d.tt_of[u] = static_cast<int>(div_tok(gm.r0 + r, tn.magic_heads));
     }
@@ -390,11 +423,8 @@ __device__ __forceinline__ void tile_loads(const NormParams& p, const TileGeom& 
     const uint32_t tt = div_tok(l, tn.magic_heads);
     const int64_t h = static_cast<int64_t>(l - tt * static_cast<uint32_t>(H));
     const int64_t t = gm.t0 + tt;
-    d.a[u] = __builtin_nontemporal_load(
-        reinterpret_cast<const gu32x4*>((const gchar*)tn.x + t * tn.x_st + h * tn.x_sh + off));
-    if constexpr (kBwd)
-      d.g[u] = __builtin_nontemporal_load(
-          reinterpret_cast<const gu32x4*>((const gchar*)tn.g + t * tn.g_st + h * tn.g_sh + off));
+    d.a[u] = row_load<kSplit, kL>((const gchar*)tn.x + t * tn.x_st + h * tn.x_sh + off);
+    if constexpr (kBwd) d.g[u] = row_load<kSplit, kL>((const gchar*)tn.g + t * tn.g_st + h * tn.g_sh + off);
     d.optr[u] = (gchar*)tn.o + t * tn.o_st + h * tn.o_sh + off;
     d.tt_of[u] = static_cast<int>(tt);
   }
@@ -483,11 +513,16 @@ __device__ __forceinline__ void tile_table(const NormParams& p, const TileGeom& 
         if (e == 0) pos_out[0] = static_cast<int32_t>(gm.t0);
         continue;
       }
-      // one entry per element: element e of token tt at (tt * kVec + e % kVec) * L + e / kVec
-      const int e1 = kIl ? 2 * i_e[v] : i_e[v];
-      const int e2 = kIl ? 2 * i_e[v] + 1 : i_e[v] + p.half;
-      double2* slot1 = s_cs + (tt_e[v] * kVec + e1 % kVec) * L + e1 / kVec;
-      double2* slot2 = s_cs + (tt_e[v] * kVec + e2 % kVec) * L + e2 / kVec;
+      // one entry per element: lane c's element j of token tt at (tt * kVec
+      // + j) * L + c (lanes read consecutive slots); the pair's elements:
+      // interleaved 2 i and 2 i + 1 of chunk i / (kVec / 2), rotate_half
+      // (split rows) i and i + half, both in lane i / (kVec / 2)
+      const int i = i_e[v];
+      const int c = i / (kVec / 2);
+      const int j1 = kIl ? 2 * (i % (kVec / 2)) : i % (kVec / 2);
+      const int j2 = kIl ? j1 + 1 : j1 + kVec / 2;
+      double2* slot1 = s_cs + (tt_e[v] * kVec + j1) * L + c;
+      double2* slot2 = s_cs + (tt_e[v] * kVec + j2) * L + c;
       if (pos >= 0) {
         double sn, cs;
         const double ang = p.freq_fp32 ? static_cast<double>(static_cast<float>(pos) * static_cast<float>(f[v]))
@@ -528,16 +563,16 @@ template <int kDtype, bool kIl, bool kBwd, int kTPT, int kL, bool kFold = false>
 __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom& gm, const TileData<kTPT>& d,
                                              const int32_t* s_pos, const double2* s_cs, const float* s_w,
                                              double* acc) {
-  constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;  // elements per chunk
+  constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;  // elements per lane and row
+  constexpr bool kSplit = !kIl;                         // rotate_half: split rows
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  constexpr int L = kL, hl = kL / 2;
+  constexpr int L = kL;
   const int c = tid & (L - 1);
   const int sel = gm.sel;
   const NormTensor& tn = p.ten[sel];
   const int* tt_of = d.tt_of;
   const bool* act = d.act;
-  const int paddr = (lane ^ hl) << 2;  // rotate_half partner lane
   const bool copy = tn.copy != 0;
   bool st[kTPT], inside[kTPT];
   u32x4 out[kTPT];
@@ -566,14 +601,14 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
       // values live and cut the occupancy
       __builtin_amdgcn_sched_barrier(0);
       const double2* tab = s_cs + tt_of[u] * kVec * L + c;
-      u32x4 pr = a[u];
-      if constexpr (!kIl) pr = partner_chunk<kDtype>(a[u], paddr, false);  // signs are in the table
+      // rotate_half partners: the lane's other half (signs are in the table)
+      const u32x4 pr = kSplit ? u32x4{a[u].z, a[u].w, a[u].x, a[u].y} : a[u];
       u32x4 y;
       if (fwd_chunk<kDtype, kIl, false>(a[u], pr, r[u], tab, L, y)) fwd_chunk<kDtype, kIl, true>(a[u], pr, r[u], tab, L, y);
       out[u] = inside[u] ? y : a[u];
     }
   } else {
-    const float* w_own = s_w + sel * (kL * kVec) + c * kVec;  // read only when not folded
+    const float* w_own = s_w + sel * (kL * kVec) + c * (kSplit ? kVec / 2 : kVec);  // read only when not folded
     // v (g when folded, else dn) stays in registers from the first pass to
     // the second; the weight-gradient terms are added in the second, where x
     // is unpacked again anyway (in the first they kept x's float64 values
@@ -584,10 +619,9 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
     for (int u = 0; u < kTPT; ++u) {
       __builtin_amdgcn_sched_barrier(0);
       const double2* tab = s_cs + tt_of[u] * kVec * L + c;
-      u32x4 pr = g[u];
-      if constexpr (!kIl) pr = partner_chunk<kDtype>(g[u], paddr, false);  // signs are in the table
+      const u32x4 pr = kSplit ? u32x4{g[u].z, g[u].w, g[u].x, g[u].y} : g[u];
       bwd_chunk_rot<kDtype, kIl>(g[u], pr, tab, L, v[u]);
-      gx[u] = bwd_chunk_gx<kDtype, kFold>(a[u], v[u], w_own);
+      gx[u] = bwd_chunk_gx<kDtype, kFold, kSplit, kL>(a[u], v[u], w_own);
     }
     __builtin_amdgcn_sched_barrier(0);
     row_sums<kTPT, kL>(gx, lane);
@@ -596,15 +630,15 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
       __builtin_amdgcn_sched_barrier(0);
       const double coef = (r[u] * r[u]) * (gx[u] * p.inv_d);
       u32x4 y;
-      if (bwd_chunk_dx<kDtype, false, kFold>(a[u], v[u], w_own, r[u], coef, acc, y))
-        bwd_chunk_dx<kDtype, true, kFold>(a[u], v[u], w_own, r[u], coef, acc, y);
+      if (bwd_chunk_dx<kDtype, false, kFold, kSplit, kL>(a[u], v[u], w_own, r[u], coef, acc, y))
+        bwd_chunk_dx<kDtype, true, kFold, kSplit, kL>(a[u], v[u], w_own, r[u], coef, acc, y);
       out[u] = inside[u] ? y : d.g[u];
     }
   }
 #pragma unroll
   for (int u = 0; u < kTPT; ++u) {
     if (!st[u]) continue;
-    __builtin_nontemporal_store(out[u], reinterpret_cast<gu32x4*>(d.optr[u]));
+    row_store<kSplit, kL>(out[u], d.optr[u]);
   }
 }
 
@@ -633,7 +667,7 @@ __device__ __forceinline__ void fwd_tile(const NormParams& p, uint32_t tile, int
   }
   __builtin_amdgcn_sched_barrier(0);
   TileData<kTPT> d;
-  if constexpr (!kPosOnly) tile_loads<false, kTPT, kL>(p, gm, d);
+  if constexpr (!kPosOnly) tile_loads<false, !kIl, kTPT, kL>(p, gm, d);
   __builtin_amdgcn_sched_barrier(0);
   const SeqCursor sc = seq_cursor(p, last_start_at_or_before((cu_ptr)p.cu, p.nseq, gm.t0));
   tile_table<kDtype, kIl, false, kL, kPosOnly>(p, gm, tt_e, i_e, f, w1, w2, sc, s_pos, s_cs, pos_out);
@@ -681,8 +715,9 @@ __global__ __launch_bounds__(kThreads) void rope_qk_norm_fwd_positions_kernel(co
 
 // Adds this thread's weight-gradient terms of tensor `sel` into the
 // workgroup's sums: across the lanes of a wave that hold the same chunk, then
-// across the waves (in a fixed order); ends with a barrier.
-template <int kVec, int kL>
+// across the waves (in a fixed order); ends with a barrier.  kSplit: the
+// lane's elements are those of a split row (elem_off).
+template <int kVec, int kL, bool kSplit>
 __device__ __forceinline__ void flush_dw(const NormParams& p, int sel, const double* acc, double* s_wave,
                                          double* s_acc) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -698,7 +733,7 @@ __device__ __forceinline__ void flush_dw(const NormParams& p, int sel, const dou
   }
   if (lane < L) {
 #pragma unroll
-    for (int j = 0; j < kVec; ++j) s_wave[wave * D + c * kVec + j] = v[j];
+    for (int j = 0; j < kVec; ++j) s_wave[wave * D + c * (kSplit ? kVec / 2 : kVec) + elem_off<kSplit, kVec, kL>(j)] = v[j];
   }
   __syncthreads();
   for (int col = tid; col < D; col += kThreads) {
@@ -739,14 +774,14 @@ __device__ __forceinline__ void bwd_runs(const NormParams& p, int32_t (*s_pos)[k
     const bool fresh = gm.sel != cur;
     if (fresh) {
       if constexpr (!kPosOnly) {
-        if (cur >= 0) flush_dw<kVec, kL>(p, cur, acc, s_wave, s_acc);
+        if (cur >= 0) flush_dw<kVec, kL, !kIl>(p, cur, acc, s_wave, s_acc);
 #pragma unroll
         for (int j = 0; j < kVec; ++j) acc[j] = 0.0;
       }
       cur = gm.sel;
     }
     TileData<kTPT> d;
-    if constexpr (!kPosOnly) tile_loads<true, kTPT, kL>(p, gm, d);
+    if constexpr (!kPosOnly) tile_loads<true, !kIl, kTPT, kL>(p, gm, d);
     __builtin_amdgcn_sched_barrier(0);
     if (fresh)
       sc = seq_cursor(p, last_start_at_or_before((cu_ptr)p.cu, p.nseq, gm.t0));
@@ -773,7 +808,7 @@ __device__ __forceinline__ void bwd_runs(const NormParams& p, int32_t (*s_pos)[k
     b ^= 1;
   }
   if constexpr (!kPosOnly) {
-    if (cur >= 0) flush_dw<kVec, kL>(p, cur, acc, s_wave, s_acc);
+    if (cur >= 0) flush_dw<kVec, kL, !kIl>(p, cur, acc, s_wave, s_acc);
     double* dst = p.partial + static_cast<int64_t>(blockIdx.x) * 2 * D;
     for (int i = tid; i < 2 * D; i += kThreads) {
       double sum = s_acc[i];
