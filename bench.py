@@ -720,6 +720,12 @@ def run_variants(args):
         ("interleaved+llama3+freq_fp32+pos_offset", dict(interleaved=True, llama3=llama3, freq_fp32=True,
                                                          pos_offset=77), w.dtype),
     ]
+    if args.case:
+        want = args.case.split(",")
+        unknown = [c for c in want if c not in [n for n, _, _ in cases]]
+        if unknown:
+            raise SystemExit(f"unknown --case {unknown}; cases: {[n for n, _, _ in cases]}")
+        cases = [c for c in cases if c[0] in want]
     res = []
     for name, opts, dt in cases:
         wd = dataclasses.replace(w, dtype=dt)
@@ -733,16 +739,23 @@ def run_variants(args):
         for i in range(args.warmup):
             fwd(i)
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if args.graph:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(args.steps):
+                    fwd(i)
+            graph.replay()
+            torch.cuda.synchronize()
+            a.record()
+            graph.replay()
+            b_.record()
+        else:  # one launch at a time (counter runs)
+            graph = None
+            a.record()
             for i in range(args.steps):
                 fwd(i)
-        graph.replay()
-        torch.cuda.synchronize()
-        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        graph.replay()
-        b_.record()
+            b_.record()
         torch.cuda.synchronize()
         us = a.elapsed_time(b_) * 1e3 / args.steps
         r = opts.get("rotary_dim", 0) or w.D
@@ -810,6 +823,8 @@ def main():
                     help="only time an unfused PyTorch-eager RoPE beside the fused kernel (context)")
     ap.add_argument("--variants", action="store_true",
                     help="only time the rotation's options (forward) on the workload")
+    ap.add_argument("--case", default="",
+                    help="with --variants: only these cases (comma-separated names, e.g. plain,fp16)")
     ap.add_argument("--pack", action="store_true",
                     help="only time the BFD packer and the packed-metadata cache")
     ap.add_argument("--norm", action="store_true",
