@@ -328,10 +328,13 @@ struct TileGeom {
   int64_t n0, t0, n_end, t_end;
 };
 
+// The tensor descriptors are read by value (p.ten[sel] into registers):
+// references into the kernel argument, selected between q's and k's, have
+// made the compiler copy the whole argument (2.4 KB) to scratch memory.
 __device__ __forceinline__ TileGeom tile_geom(const NormParams& p, uint32_t tile) {
   TileGeom gm;
   gm.sel = tile >= p.ten[0].ntiles ? 1 : 0;  // wave-uniform
-  const NormTensor& tn = p.ten[gm.sel];
+  const NormTensor tn = p.ten[gm.sel];
   const uint32_t lt = tile - (gm.sel ? p.ten[0].ntiles : 0u);
   const int32_t H = tn.H;
   // n0 < 2^47 is exact in float64; the rounded quotient is off by at most one
@@ -391,7 +394,7 @@ __device__ __forceinline__ void row_store(const u32x4& v, gchar* ptr) {
 template <bool kBwd, bool kSplit, int kTPT, int kL>
 __device__ __forceinline__ void tile_loads(const NormParams& p, const TileGeom& gm, TileData<kTPT>& d) {
   const int tid = threadIdx.x;
-  const NormTensor& tn = p.ten[gm.sel];
+  const NormTensor tn = p.ten[gm.sel];
   const int32_t H = tn.H;
   constexpr int rows_per_step = kThreads / kL;
   const int64_t off = static_cast<int64_t>(tid & (kL - 1)) * (kSplit ? 8 : 16);
@@ -570,7 +573,7 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
   constexpr int L = kL;
   const int c = tid & (L - 1);
   const int sel = gm.sel;
-  const NormTensor& tn = p.ten[sel];
+  const NormTensor tn = p.ten[sel];
   const int* tt_of = d.tt_of;
   const bool* act = d.act;
   const bool copy = tn.copy != 0;
@@ -649,7 +652,7 @@ template <int kDtype, bool kIl, int kTPT, int kL, bool kPosOnly = false>
 __device__ __forceinline__ void fwd_tile(const NormParams& p, uint32_t tile, int32_t* s_pos, double2* s_cs,
                                          int32_t* pos_out = nullptr) {
   const TileGeom gm = tile_geom(p, tile);
-  const NormTensor& tn = p.ten[gm.sel];
+  const NormTensor tn = p.ten[gm.sel];
   int tt_e[kFwdEnt], i_e[kFwdEnt];
   tile_entries<kFwdEnt>(p, gm, tt_e, i_e);
   double f[kFwdEnt];
