@@ -184,6 +184,40 @@ def test_norm_bwd_zero_weights(shape, which):
         assert s["q"]["exact_fraction"] == 1.0 and s["k"]["exact_fraction"] == 1.0, s
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp16", "fp32"])
+def test_norm_bwd_weights_of_every_magnitude(dt):
+    """The folded backward forms g = w dn in its tables and divides the
+    weight-gradient sums of w dn x r by w at the end: weights from 1e-20 to
+    1e20 in size in bf16, of either sign (1e-3 to 1e3 for fp16, whose
+    outputs must stay in range, and for fp32, checked against the scaled
+    fp32 bound), against the oracle's unfolded float64 sums."""
+    T, Hq, Hkv, D = 300, 6, 2, 128
+    lo, hi = (-3.0, 3.0) if dt != "bf16" else (-20.0, 20.0)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(81)
+    mags = 10.0 ** (lo + (hi - lo) * torch.rand(2, D, generator=g, dtype=torch.float64))
+    signs = torch.where(torch.rand(2, D, generator=g) < 0.5, -1.0, 1.0).double()
+    ws = (mags * signs).float().to(DEV)
+    cu = [0, 1, 120, 120, 296]
+    q = W.randn((T, Hq, D), dt, seed=82, device=DEV)
+    k = W.randn((T, Hkv, D), dt, seed=83, device=DEV)
+    dyq = W.randn((T, Hq, D), dt, seed=84, device=DEV)
+    dyk = W.randn((T, Hkv, D), dt, seed=85, device=DEV)
+    dq, dk, dwq, dwk = P.rope_qk_norm_bwd(dyq.clone(), dyk.clone(), q, k, ws[0], ws[1], EPS, cu_dev(cu), 1e4)
+    torch.cuda.synchronize()
+    o = oracle_opts({})
+    for name, dx, dw, x, dy, w in (("q", dq, dwq, q, dyq, ws[0]), ("k", dk, dwk, k, dyk, ws[1])):
+        rdx, rdw = oracle.norm_rope_bwd(f64(dy), f64(x), w64(w), EPS, cu, 1e4, **o)
+        if dt == "fp32":  # the fp32 bound of the unit-scale tests, scaled by the outputs' size
+            err = np.abs(f64(dx) - rdx)
+            scale = max(1.0, float(np.abs(rdx).max()))
+            assert float(err.max()) <= 1e-5 * scale, f"d{name}: {err.max()} at scale {scale}"
+        else:
+            st = check_against(dx, rdx, f"d{name} weights 1e{lo:+.0f}..1e{hi:+.0f}")
+            assert st["exact_fraction"] == 1.0, st
+        check_dw(dw, rdw, dw_terms(f64(dy), f64(x), w64(w), cu, 1e4, o), f"dw{name} weights of every magnitude")
+
+
 def test_norm_bwd_tensor_without_heads():
     """k with no heads: its weight vector (all zeros here) plays no part, so
     q's backward still folds its weights; q's results match the oracle and
