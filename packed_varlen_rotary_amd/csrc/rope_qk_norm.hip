@@ -35,9 +35,9 @@
 //    the weights are folded into the per-element table, so the rotation of
 //    dy yields g = w dn directly and the weight-gradient sums (of w dn x r)
 //    are divided by w once at the end; otherwise the table has unit weights
-//    and dn is multiplied by w.  A fixed number of
-//    workgroups each take a contiguous run of tiles, carrying a cursor into
-//    cu_seqlens from tile to tile, with one barrier per tile.  Each lane
+//    and dn is multiplied by w.  A fixed number of workgroups each take a
+//    contiguous run of tiles, carrying a cursor into cu_seqlens from tile to
+//    tile, with one barrier per tile.  Each lane
 //    keeps the weight-gradient terms of its rows in registers while the
 //    tiles are of one tensor; then they are summed across the lanes of a
 //    wave that hold the same chunk and across the 4 waves, into float64 sums
@@ -80,6 +80,7 @@ template <bool kSplit, int kVec, int kL>
 __device__ __forceinline__ constexpr int elem_off(int j) {
   return (kSplit && j >= kVec / 2) ? j - kVec / 2 + kL * kVec / 2 : j;
 }
+
 // Backward workgroups, each looping over a contiguous run of tiles: four
 // times as many as the 256 compute units hold at once (3 per unit at the
 // 16-bit kernels' 168 VGPRs, 4 for float32).  Units that run ahead then take
@@ -191,10 +192,10 @@ __device__ __forceinline__ void row_sums(double* v, int lane) {
   }
 }
 
-// The forward output of one chunk from the weight-folded table: element e
-// becomes r * (x_e * A_e + x_p * B_e), with p its pair partner (rotate_half:
-// the same element of the partner chunk pr; interleaved: its neighbour in
-// the chunk) and (A_e, B_e) = (w_e cos, -w_p sin) for the first element of a
+// The forward output of one lane's 16 bytes of a row from the weight-folded
+// table: element e becomes r * (x_e * A_e + x_p * B_e), with p its pair
+// partner (rotate_half: the same element of pr, the lane's other half of a
+// split row; interleaved: its neighbour in the chunk) and (A_e, B_e) = (w_e cos, -w_p sin) for the first element of a
 // pair, (w_e cos, w_p sin) for the second.  tab: the chunk's first entry,
 // consecutive elements L entries apart.  16-bit storage: kExact selects the
 // exact rounding; returns whether a value was hard for the fast one.
@@ -229,10 +230,10 @@ __device__ __forceinline__ bool fwd_chunk(const u32x4& own, const u32x4& pr, dou
   return tie;
 }
 
-// The incoming gradient of one chunk rotated by -angle, from the per-element
-// table (A_e, B_e): v_e = dy_e A_e + dy_p B_e, p the pair partner of element
-// e (rotate_half: the same element of the partner chunk pr; interleaved: its
-// neighbour in the chunk).  With the weights folded into the table
+// The incoming gradient of one lane's 16 bytes of a row rotated by -angle,
+// from the per-element table (A_e, B_e): v_e = dy_e A_e + dy_p B_e, p the pair
+// partner of element e (rotate_half: the same element of pr, the lane's other
+// half of a split row; interleaved: its neighbour in the chunk).  With the weights folded into the table
 // (A_e = w_e cos, B_e = -+w_e sin) v is g = w dn; with unit weights it is dn.
 // tab: the chunk's first entry, consecutive elements L entries apart.
 template <int kDtype, bool kIl>
@@ -265,7 +266,7 @@ __device__ __forceinline__ void bwd_chunk_rot(const u32x4& dy, const u32x4& pr, 
 
 // Backward of one chunk, first part: sum_j g_j x_j over its elements.  kFold:
 // v is g already; otherwise v is dn and g = dn w, with element j's weight at
-// w_own[kOff(j)] (its offset in the row from the lane's element 0).
+// w_own[elem_off(j)] (its offset in the row from the lane's element 0).
 template <int kDtype, bool kFold, bool kSplit, int kL>
 __device__ __forceinline__ double bwd_chunk_gx(const u32x4& x, const double* v, const float* w_own) {
   constexpr int kVec = kDtype == ROPE_QK_FP32 ? 4 : 8;
@@ -644,7 +645,6 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
     row_store<kSplit, kL>(out[u], d.optr[u]);
   }
 }
-
 
 // The forward tile: its frequencies and weights are loaded before its data.
 // kPosOnly: the positions hook (see tile_table).
