@@ -31,7 +31,8 @@
 //  * A tile holds rows of q only or of k only, so it needs one weight vector
 //    and one set of weight-gradient sums.
 //  * Backward: the rotation by -angle, then the RMSNorm gradient with a
-//    second row sum (sum_j g_j x_j).  When every weight is finite and nonzero
+//    second row sum (sum_j g_j x_j), summed over the row's lanes in the same
+//    butterfly as the squares.  When every weight is finite and nonzero
 //    the weights are folded into the per-element table, so the rotation of
 //    dy yields g = w dn directly and the weight-gradient sums (of w dn x r)
 //    are divided by w once at the end; otherwise the table has unit weights
@@ -195,10 +196,11 @@ __device__ __forceinline__ void row_sums(double* v, int lane) {
 // The forward output of one lane's 16 bytes of a row from the weight-folded
 // table: element e becomes r * (x_e * A_e + x_p * B_e), with p its pair
 // partner (rotate_half: the same element of pr, the lane's other half of a
-// split row; interleaved: its neighbour in the chunk) and (A_e, B_e) = (w_e cos, -w_p sin) for the first element of a
-// pair, (w_e cos, w_p sin) for the second.  tab: the chunk's first entry,
-// consecutive elements L entries apart.  16-bit storage: kExact selects the
-// exact rounding; returns whether a value was hard for the fast one.
+// split row; interleaved: its neighbour in the chunk) and (A_e, B_e) =
+// (w_e cos, -w_p sin) for the first element of a pair, (w_e cos, w_p sin)
+// for the second.  tab: the chunk's first entry, consecutive elements L
+// entries apart.  16-bit storage: kExact selects the exact rounding; returns
+// whether a value was hard for the fast one.
 template <int kDtype, bool kIl, bool kExact>
 __device__ __forceinline__ bool fwd_chunk(const u32x4& own, const u32x4& pr, double r, const double2* tab, int L,
                                           u32x4& out) {
@@ -557,9 +559,11 @@ __device__ __forceinline__ void tile_table(const NormParams& p, const TileGeom& 
   __syncthreads();
 }
 
-// Every row of a tile (after its table): r for all rows (their lane sums
-// together), then the forward rows one at a time, or the backward in phases;
-// then the stores.  s_w holds both tensors' weights (q then k); acc
+// Every row of a tile (after its table).  Forward: r for all rows (their
+// lane sums together), then the rows one at a time.  Backward, in phases:
+// the squares, the rotation of dy and the lane's part of sum g x; both row
+// sums of all rows in one butterfly; r; dx and the weight-gradient terms.
+// Then the stores.  s_w holds both tensors' weights (q then k); acc
 // (backward) receives this lane's weight-gradient terms.  kFold (backward):
 // the table carries the weights, so the rotation gives g = w dn directly and
 // acc receives w dn x r.
@@ -595,10 +599,10 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
     if constexpr (kBwd) g[u] = use ? d.g[u] : zero;
     r[u] = chunk_squares<kDtype>(a[u]);
   }
-  row_sums<kTPT, kL>(r, lane);
-#pragma unroll
-  for (int u = 0; u < kTPT; ++u) r[u] = rsqrt_f64(fma(r[u], p.inv_d, p.eps));
   if constexpr (!kBwd) {
+    row_sums<kTPT, kL>(r, lane);
+#pragma unroll
+    for (int u = 0; u < kTPT; ++u) r[u] = rsqrt_f64(fma(r[u], p.inv_d, p.eps));
 #pragma unroll
     for (int u = 0; u < kTPT; ++u) {
       // one row at a time: interleaving rows would keep several rows' float64
@@ -628,7 +632,20 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
       gx[u] = bwd_chunk_gx<kDtype, kFold, kSplit, kL>(a[u], v[u], w_own);
     }
     __builtin_amdgcn_sched_barrier(0);
-    row_sums<kTPT, kL>(gx, lane);
+    // both row sums (of x^2 and of g x; neither needs the other) go through
+    // one butterfly, one chain of lane exchanges instead of two
+    double sums[2 * kTPT];
+#pragma unroll
+    for (int u = 0; u < kTPT; ++u) {
+      sums[u] = r[u];
+      sums[kTPT + u] = gx[u];
+    }
+    row_sums<2 * kTPT, kL>(sums, lane);
+#pragma unroll
+    for (int u = 0; u < kTPT; ++u) {
+      r[u] = rsqrt_f64(fma(sums[u], p.inv_d, p.eps));
+      gx[u] = sums[kTPT + u];
+    }
 #pragma unroll
     for (int u = 0; u < kTPT; ++u) {
       __builtin_amdgcn_sched_barrier(0);
