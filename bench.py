@@ -111,53 +111,72 @@ def cpu_model() -> str:
 # CPU baseline: the oracle as it stands, on a bounded sample
 # ---------------------------------------------------------------------------
 
+def oracle_inputs(w, nchunks: int, chunk: int):
+    """Seeded inputs for the first `nchunks` token chunks of a workload: each
+    chunk's positions and its q and k in float64 (bf16 workloads: rounded to
+    bf16), drawn before any clock starts."""
+    import numpy as np
+
+    import oracle
+
+    pos_all = oracle.segment_positions(w.cu_seqlens, w.T)
+    rng = np.random.default_rng(0)
+    chunks = []
+    for s in list(range(0, w.T, chunk))[:nchunks]:
+        n = min(s + chunk, w.T) - s
+        xs = []
+        for H in (w.Hq, w.Hkv):
+            x = rng.standard_normal((n, H, w.D))
+            xs.append(oracle.bf16_rne(x) if w.dtype == "bf16" else x.astype(np.float32).astype(np.float64))
+        chunks.append((pos_all[s:s + n], xs))
+    return chunks
+
+
+def oracle_pass(w, pos, xs, directions) -> int:
+    """The oracle on one chunk: positions already found, float64 rotation of
+    q and k in each direction, rounding to the storage type.  Returns the
+    chunk's tokens."""
+    import numpy as np
+
+    import oracle
+
+    for x in xs:
+        for direction in directions:
+            y = oracle.rotate(x, pos, w.theta, direction)
+            if w.dtype == "bf16":
+                oracle.bf16_bits(oracle.bf16_rne(y))
+            else:
+                y.astype(np.float32)
+    return len(pos)
+
+
+def oracle_rate(w, chunks, directions, threads: int, budget_s: float):
+    """Tokens per second of the oracle over the chunks, for at least budget_s:
+    a thread pool over chunks (numpy releases the GIL), or one thread."""
+    t0 = time.perf_counter()
+    tokens = 0
+    if threads > 1:
+        with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+            while time.perf_counter() - t0 < budget_s:
+                tokens += sum(ex.map(lambda c: oracle_pass(w, c[0], c[1], directions), chunks))
+    else:
+        while time.perf_counter() - t0 < budget_s:
+            tokens += oracle_pass(w, chunks[0][0], chunks[0][1], directions)
+    dt = time.perf_counter() - t0
+    return tokens, dt
+
+
 def cpu_baseline(w, budget_s: float = 12.0, chunk: int = 1024, single_s: float = 3.0):
     """The oracle on the host cores: positions, float64 rotation of q and k
     forward and backward, rounding to the storage type, on chunks of the
     workload's tokens.  Inputs are drawn before the clock starts, so only the
     oracle is timed; a thread pool over chunks (numpy releases the GIL), and
     the same work on one thread for reference."""
-    import numpy as np
-
-    import oracle
-
     host_cores = len(os.sched_getaffinity(0))
     threads = min(host_cores, CPU_SHARE)
-    pos_all = oracle.segment_positions(w.cu_seqlens, w.T)
-    rng = np.random.default_rng(0)
-    starts = list(range(0, w.T, chunk))[:threads]
-    inputs = {}
-    for s in starts:
-        n = min(s + chunk, w.T) - s
-        xs = []
-        for H in (w.Hq, w.Hkv):
-            x = rng.standard_normal((n, H, w.D))
-            xs.append(oracle.bf16_rne(x) if w.dtype == "bf16" else x)
-        inputs[s] = xs
-
-    def one_chunk(s):
-        n = min(s + chunk, w.T) - s
-        pos = pos_all[s:s + n]
-        for x in inputs[s]:
-            for direction in (1, -1):
-                y = oracle.rotate(x, pos, w.theta, direction)
-                if w.dtype == "bf16":
-                    oracle.bf16_bits(oracle.bf16_rne(y))
-                else:
-                    y.astype(np.float32)
-        return n
-
-    t0 = time.perf_counter()
-    tokens = 0
-    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
-        while time.perf_counter() - t0 < budget_s:
-            tokens += sum(ex.map(one_chunk, starts))
-    dt = time.perf_counter() - t0
-    t1 = time.perf_counter()
-    tokens1 = 0
-    while time.perf_counter() - t1 < single_s:
-        tokens1 += one_chunk(starts[0])
-    dt1 = time.perf_counter() - t1
+    chunks = oracle_inputs(w, threads, chunk)
+    tokens, dt = oracle_rate(w, chunks, (1, -1), threads, budget_s)
+    tokens1, dt1 = oracle_rate(w, chunks, (1, -1), 1, single_s)
     return {
         "value": tokens / dt,
         "unit": "tokens/s",
@@ -171,6 +190,33 @@ def cpu_baseline(w, budget_s: float = 12.0, chunk: int = 1024, single_s: float =
         "thread_cap": f"the pool stops at {CPU_SHARE} threads, the host CPU share one GPU's jobs get",
         "single_thread_value": tokens1 / dt1,
     }
+
+
+def run_cpu_table(args):
+    """The oracle per workload and direction, on one thread and on the pool:
+    tokens/s and the effective GB/s of the same algorithmic bytes (read and
+    write of q and k).  Host only; one JSON line per workload."""
+    import workloads as W
+
+    host_cores = len(os.sched_getaffinity(0))
+    threads = min(host_cores, CPU_SHARE)
+    log(f"[bench] oracle table: {cpu_model()}, {host_cores} host cores, pool of {threads} threads")
+    cfgs = [int(c) for c in args.table.split(",") if c.strip()] if args.table else [1, 2, 3, 4, 5]
+    for cfg in cfgs:
+        w = W.make_workload(cfg)
+        chunks = oracle_inputs(w, threads, 1024)
+        bytes_per_token = 2 * (w.Hq + w.Hkv) * w.D * (2 if w.dtype == "bf16" else 4)
+        row = {"workload": w.name, "io_dtype": w.dtype, "threads": threads, "host_cores": host_cores,
+               "cpu_model": cpu_model()}
+        for name, direction in (("fwd", 1), ("bwd", -1)):
+            tp, dtp = oracle_rate(w, chunks, (direction,), threads, args.cpu_seconds)
+            t1, dt1 = oracle_rate(w, chunks, (direction,), 1, max(1.0, args.cpu_seconds / 3))
+            row[name] = {"pool_tokens_per_s": tp / dtp, "pool_gb_per_s": tp / dtp * bytes_per_token / 1e9,
+                         "single_tokens_per_s": t1 / dt1, "single_gb_per_s": t1 / dt1 * bytes_per_token / 1e9,
+                         "pool_tokens": tp, "pool_seconds": dtp}
+            log(f"[bench] oracle {w.name} {name}: {tp / dtp:.0f} tokens/s on {threads} threads, "
+                f"{t1 / dt1:.0f} on one")
+        print(json.dumps(row), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -831,6 +877,9 @@ def main():
                     help="only time the fused RMSNorm + rotation kernels (forward and backward) on --workload")
     ap.add_argument("--copy-ceiling", action="store_true",
                     help="only time the runtime's device copy with one launch's HBM traffic (roofline context)")
+    ap.add_argument("--cpu-table", action="store_true",
+                    help="only time the oracle per workload (--table, default all) and direction, on the host "
+                         "(--cpu-seconds per pool measurement)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -838,6 +887,11 @@ def main():
               "exchange, so more GPUs would each run this same one-GPU workload on their own shard.",
               file=sys.stderr)
         sys.exit(2)
+    if args.cpu_table:
+        if not any(a.startswith("--table") for a in sys.argv[1:]):
+            args.table = ""
+        run_cpu_table(args)
+        return
     if args.copy_calibration:
         run_copy_calibration(args)
         return
