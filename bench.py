@@ -61,12 +61,13 @@ CPU_SHARE = 16
 # own overhead (a few microseconds) stays under ~0.2% of the region
 MIN_REGION_S = 4e-3
 # plain in-place stream variants timed for the ceiling: (chunks per lane,
-# persistent workgroups or 0 for one tile per workgroup, non-temporal,
-# resident workgroups per compute unit or 0 for as many as fit)
+# persistent workgroups (each with the next two tiles' loads in flight) or 0
+# for one tile per workgroup, non-temporal, resident workgroups per compute
+# unit or 0 for as many as fit)
 CEILING_VARIANTS = [(1, 0, 1, 0), (2, 0, 1, 0), (4, 0, 1, 0), (8, 0, 1, 0), (16, 0, 1, 0), (4, 0, 0, 0),
                     (1, 0, 1, 4), (1, 0, 1, 6), (2, 0, 1, 2), (2, 0, 1, 3), (2, 0, 1, 4), (2, 0, 1, 6),
                     (4, 0, 1, 1), (4, 0, 1, 2), (4, 0, 1, 3), (8, 0, 1, 1), (8, 0, 1, 2),
-                    (4, 1024, 1, 0), (8, 1024, 1, 0), (16, 1024, 1, 0)]
+                    (1, 512, 1, 0), (2, 768, 1, 0), (4, 512, 1, 0), (4, 768, 1, 0)]
 
 
 def log(*a):

@@ -42,7 +42,9 @@ extern "C" {
  *   chunks_per_lane  1, 2, 4, 8 or 16
  *   groups           0: one tile of 256 * chunks_per_lane chunks per
  *                    workgroup (one-shot grid); > 0: that many workgroups,
- *                    each looping over every groups-th tile (persistent)
+ *                    each looping over every groups-th tile (persistent),
+ *                    with the next two tiles' loads issued before a tile's
+ *                    stores
  *   nontemporal      non-zero: non-temporal loads and stores (as the
  *                    rotation kernels use), else ordinary ones
  *   groups_per_cu    0: as many resident workgroups per compute unit as

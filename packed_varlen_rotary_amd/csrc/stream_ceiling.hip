@@ -59,12 +59,72 @@ __global__ __launch_bounds__(kThreads) void stream_oneshot(u32x4* data, int64_t 
   if (tile < ntiles) stream_tile<kTPL, kNT>(buf, nchunks, tile, key);
 }
 
-// gridDim.x workgroups, each taking every gridDim.x-th tile.
+// One tile's chunks into registers and back.  Chunks past the buffer use
+// its last chunk: they re-read it and store back the value its own lane of
+// the same tile stores, so every store instruction is issued and the
+// compiler's wait counts stay exact.
+template <int kTPL, bool kNT>
+__device__ __forceinline__ void load_tile(gu32x4* buf, int64_t nchunks, int64_t tile, u32x4* v) {
+  const int64_t base = tile * (kThreads * kTPL) + threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kTPL; ++u) {
+    int64_t i = base + static_cast<int64_t>(u) * kThreads;
+    i = i < nchunks ? i : nchunks - 1;
+    v[u] = kNT ? __builtin_nontemporal_load(buf + i) : buf[i];
+  }
+}
+
+template <int kTPL, bool kNT>
+__device__ __forceinline__ void store_tile(gu32x4* buf, int64_t nchunks, int64_t tile, u32x4* v, uint32_t key) {
+  const int64_t base = tile * (kThreads * kTPL) + threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kTPL; ++u) {
+    int64_t i = base + static_cast<int64_t>(u) * kThreads;
+    i = i < nchunks ? i : nchunks - 1;
+    v[u] ^= key;
+    if (kNT)
+      __builtin_nontemporal_store(v[u], buf + i);
+    else
+      buf[i] = v[u];
+  }
+}
+
+// gridDim.x workgroups, each taking every gridDim.x-th tile, with the next
+// two tiles' loads in flight while a tile is stored: three register sets in
+// turn (the loop unrolled by three), the loads ahead issued unconditionally
+// (past the last tile they re-read it) so that the compiler's wait counts
+// are exact, and only real tiles stored.
 template <int kTPL, bool kNT>
 __global__ __launch_bounds__(kThreads) void stream_persistent(u32x4* data, int64_t nchunks, int64_t ntiles,
                                                               uint32_t key) {
   gu32x4* buf = (gu32x4*)data;
-  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) stream_tile<kTPL, kNT>(buf, nchunks, tile, key);
+  const int64_t step = gridDim.x;
+  int64_t t = blockIdx.x;
+  if (t >= ntiles) return;
+  const auto ahead = [&](int64_t x) { return x < ntiles ? x : ntiles - 1; };
+  u32x4 a[kTPL], b[kTPL], c[kTPL];
+  load_tile<kTPL, kNT>(buf, nchunks, t, a);
+  load_tile<kTPL, kNT>(buf, nchunks, ahead(t + step), b);
+  for (;;) {
+    load_tile<kTPL, kNT>(buf, nchunks, ahead(t + 2 * step), c);
+    __builtin_amdgcn_sched_barrier(0);
+    store_tile<kTPL, kNT>(buf, nchunks, t, a, key);
+    __builtin_amdgcn_sched_barrier(0);
+    t += step;
+    if (t >= ntiles) break;
+    load_tile<kTPL, kNT>(buf, nchunks, ahead(t + 2 * step), a);
+    __builtin_amdgcn_sched_barrier(0);
+    store_tile<kTPL, kNT>(buf, nchunks, t, b, key);
+    __builtin_amdgcn_sched_barrier(0);
+    t += step;
+    if (t >= ntiles) break;
+    load_tile<kTPL, kNT>(buf, nchunks, ahead(t + 2 * step), b);
+    __builtin_amdgcn_sched_barrier(0);
+    store_tile<kTPL, kNT>(buf, nchunks, t, c, key);
+    __builtin_amdgcn_sched_barrier(0);
+    t += step;
+    if (t >= ntiles) break;
+  }
 }
 
 template <int kTPL>
