@@ -46,3 +46,11 @@ def test_cpu_table_prints_one_line_per_workload():
         assert r["threads"] >= 1 and r["host_cores"] >= r["threads"]
         for d in ("fwd", "bwd"):
             assert r[d]["pool_tokens"] > 0 and r[d]["pool_tokens_per_s"] > 0 and r[d]["single_tokens_per_s"] > 0
+
+
+def test_more_than_one_gpu_is_refused_before_any_gpu_work():
+    out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=300)
+    assert out.returncode == 2
+    assert out.stdout == ""
+    assert "one GPU" in out.stderr
