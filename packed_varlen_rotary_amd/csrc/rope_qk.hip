@@ -22,10 +22,12 @@
 //    or 4 chunks): a task is a single 16-byte chunk and consecutive lanes
 //    cover whole rows, so every wave-wide load and store covers whole 128-byte
 //    lines (partner halves loaded by separate instructions cost ~13% of HBM
-//    throughput on MI355X at D = 64); the partner chunk comes from the lane
-//    kG away through a DPP move.
+//    throughput on MI355X at D = 64).  A lane and the lane kG away hold the
+//    two chunks of a row; through ds_swizzle each sends the other half of its
+//    chunk's dwords, rotates its half of the pairs whole and sends the
+//    other's outputs back, so each element is unpacked once.
 //  * A workgroup owns one tile of consecutive tasks (256 lanes x 2 pairs or
-//    x 4 chunks), which may begin and end inside a token, so every tile but
+//    x 4-8 chunks), which may begin and end inside a token, so every tile but
 //    the last is full whatever the head count.  The grid is two-dimensional
 //    rather than a grid-stride loop: a loop's second copy of the body would
 //    set the register count (and so the occupancy) of every launch.
@@ -132,10 +134,10 @@ __device__ __forceinline__ void rotate_f32(const u32x4& a, const u32x4& b, const
 }
 
 // Partner exchange for unit tiles: lane l receives the dword lane l ^ kG
-// holds (the 16-byte chunk D/2 further on, or back, in the same row; a row's
-// 2*kG chunks sit on 2*kG consecutive lanes).  ds_swizzle in bit-mask mode
-// (and-mask 31, xor-mask kG, within each 32-lane half) moves it through the
-// LDS crossbar, leaving the vector ALU to the rotation.
+// passes (that lane holds the 16-byte chunk D/2 further on, or back, in the
+// same row; a row's 2*kG chunks sit on 2*kG consecutive lanes).  ds_swizzle
+// in bit-mask mode (and-mask 31, xor-mask kG, within each 32-lane half)
+// moves it through the LDS crossbar, leaving the vector ALU to the rotation.
 template <int kG>
 __device__ __forceinline__ uint32_t partner_dword(uint32_t x) {
   static_assert(kG == 1 || kG == 2 || kG == 4, "unit tiles need a half row of 1, 2 or 4 chunks");
@@ -143,34 +145,56 @@ __device__ __forceinline__ uint32_t partner_dword(uint32_t x) {
   return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(x), kPattern));
 }
 
-// Rotate one 16-byte chunk of 16-bit data in place of its row: own holds
-// x[m .. m+7], par the partner elements D/2 away, negated when own lies in
-// the first half, so every output is own * cos + par * sin (the same
-// float64 operations as the paired form).
+// (mask & x) | (~mask & y) in one bitfield insert.  Written out because a
+// select between two elements of one vector register group becomes an
+// element extract at a variable index (a compare and a select per element).
+__device__ __forceinline__ uint32_t lane_pick(uint32_t mask, uint32_t x, uint32_t y) {
+  uint32_t r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(mask), "v"(x), "v"(y));
+  return r;
+}
+
+// Unit tiles: a lane and its partner (the lane kG away) hold the two 16-byte
+// chunks of one row (x[m .. m+7] and x[m+D/2 .. m+D/2+7] for 16-bit data).
+// Each rotates two dwords' worth of the chunks' pairs whole: m holds two
+// dwords of the lane's own chunk, g the same dwords of the partner's chunk,
+// and the outputs are its own chunk's (om) and the partner chunk's (op), in
+// the float64 operations of the paired form.
 template <int kDtype, bool kExact>
-__device__ __forceinline__ bool rotate_unit16(const u32x4& own, const u32x4& par, const double2* __restrict__ cs,
-                                              int chunks, u32x4& out) {
+__device__ __forceinline__ bool rotate_half16(const uint32_t (&m)[2], const uint32_t (&g)[2],
+                                              const double2* __restrict__ cs, int chunks, uint32_t (&om)[2],
+                                              uint32_t (&op)[2]) {
   bool tie = false;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const double2 c0 = cs[(2 * j) * chunks];
     const double2 c1 = cs[(2 * j + 1) * chunks];
-    const f64x2 x = unpack16<kDtype>(own[j]), y = unpack16<kDtype>(par[j]);
-    const double yl = fma(x.x, c0.x, y.x * c0.y);
-    const double yh = fma(x.y, c1.x, y.y * c1.y);
-    out[j] = kExact ? pack16_exact<kDtype>(yl, yh) : pack16_fast<kDtype>(yl, yh, tie);
+    const f64x2 x1 = unpack16<kDtype>(m[j]), x2 = unpack16<kDtype>(g[j]);
+    const double y1l = fma(x1.x, c0.x, -(x2.x * c0.y));
+    const double y2l = fma(x2.x, c0.x, x1.x * c0.y);
+    const double y1h = fma(x1.y, c1.x, -(x2.y * c1.y));
+    const double y2h = fma(x2.y, c1.x, x1.y * c1.y);
+    if (kExact) {
+      om[j] = pack16_exact<kDtype>(y1l, y1h);
+      op[j] = pack16_exact<kDtype>(y2l, y2h);
+    } else {
+      om[j] = pack16_fast<kDtype>(y1l, y1h, tie);
+      op[j] = pack16_fast<kDtype>(y2l, y2h, tie);
+    }
   }
   return tie;
 }
 
-__device__ __forceinline__ void rotate_unit_f32(const u32x4& own, const u32x4& par, const double2* __restrict__ cs,
-                                                int chunks, u32x4& out) {
+__device__ __forceinline__ void rotate_half_f32(const uint32_t (&m)[2], const uint32_t (&g)[2],
+                                                const double2* __restrict__ cs, int chunks, uint32_t (&om)[2],
+                                                uint32_t (&op)[2]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const double2 c = cs[j * chunks];
-    const double x = static_cast<double>(__uint_as_float(own[j]));
-    const double y = static_cast<double>(__uint_as_float(par[j]));
-    out[j] = __float_as_uint(static_cast<float>(fma(x, c.x, y * c.y)));
+    const double x1 = static_cast<double>(__uint_as_float(m[j]));
+    const double x2 = static_cast<double>(__uint_as_float(g[j]));
+    om[j] = __float_as_uint(static_cast<float>(fma(x1, c.x, -(x2 * c.y))));
+    op[j] = __float_as_uint(static_cast<float>(fma(x2, c.x, x1 * c.y)));
   }
 }
 
@@ -241,6 +265,10 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
     const int ntok = static_cast<int>(div_tok(static_cast<uint32_t>(n_end - n0) + r0 - 1, p.magic_tok)) + 1;
     const int64_t t_end = t0 + ntok;  // one past the tile's last token
     const int nent = ntok * p.half;
+    // unit tiles: where the table's second copy (sine negated) starts; the 4
+    // entries past a multiple of 16 keep a wave's reads of the two copies on
+    // different LDS banks
+    const int alt = ((nent + 15) & ~15) + 4;
 
     // 1. inv_freq of this thread's table entries.  Issued before the tile's
     //    data: the memory counter completes in order, so the table can be
@@ -261,7 +289,7 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
     u32x4 a[kTPT], b[kTPT];
     gchar* ptr[kTPT];
     int tt_of[kTPT], c_of[kTPT];
-    bool act[kTPT], first[kTPT];
+    bool act[kTPT];
     if constexpr (!kPosOnly) {
     // Unit tiles whose token task count divides 256 (e.g. 16 heads at D = 64):
     // a lane's tasks are tok_step tokens apart at the same head and chunk, so
@@ -276,7 +304,6 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
         ptr[u] = ptr[0] + (act[u] ? step : int64_t(0));  // offset select keeps the global address space
         tt_of[u] = act[u] ? tt_of[0] + u * static_cast<int>(p.tok_step) : tt_of[0];
         c_of[u] = c_of[0];
-        first[u] = first[0];
       } else {
         const uint32_t l_raw = r0 + static_cast<uint32_t>(tid + u * kThreads);  // task index from the tile's first token
         const uint32_t l = act[u] ? l_raw : r0;
@@ -300,7 +327,6 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
         ptr[u] = row + static_cast<int64_t>(c) * 16;
         tt_of[u] = static_cast<int>(tt);
         c_of[u] = static_cast<int>(cc);
-        first[u] = kG > 0 && c < static_cast<uint32_t>(kG);
       }
       // streamed once: non-temporal, so they do not displace other data in the caches
       a[u] = __builtin_nontemporal_load(reinterpret_cast<const gu32x4*>(ptr[u]));
@@ -343,7 +369,9 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
           const double ang = p.freq_fp32 ? static_cast<double>(static_cast<float>(pos) * static_cast<float>(f[v]))
                                          : static_cast<double>(pos) * f[v];
           rope_sincos(ang, &sn, &cs);
-          s_cs[cs_slot(tt_e[v], i_e[v], kPPC, p.chunks)] = make_double2(cs, p.sign * sn);
+          const int slot = cs_slot(tt_e[v], i_e[v], kPPC, p.chunks);
+          s_cs[slot] = make_double2(cs, p.sign * sn);
+          if constexpr (kG > 0) s_cs[alt + slot] = make_double2(cs, -p.sign * sn);
         }
       }
     }
@@ -354,11 +382,18 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
     //    sequence are left untouched
     bool st[kTPT];
     u32x4 oa[kTPT], ob[kTPT];
+    // Unit tiles: a lane's chunks all sit at the lane's index modulo 2 kG in
+    // their rows, so its half of every pair (first or second) is fixed; the
+    // second-half lane reads the table copy with the sine negated, from its
+    // pairs' entries on (see the rotation below).
+    const bool fst = kG <= 0 || (tid & kG) == 0;
+    const uint32_t keep = fst ? 0xFFFFFFFFu : 0u;  // bit mask selecting the first operand of lane_pick
+    const double2* tab = kG > 0 && !fst ? s_cs + alt + (kPPC / 2) * kG : s_cs;
 #pragma unroll
     for (int u = 0; u < kTPT; ++u) {
       st[u] = act[u] && s_pos[tt_of[u]] >= 0;
       const int chunks = kG > 0 ? kG : p.chunks;
-      const double2* cs = s_cs + tt_of[u] * kPPC * chunks + c_of[u];
+      const double2* cs = tab + tt_of[u] * kPPC * chunks + c_of[u];
       if constexpr (kG == kInterleaved) {
         if constexpr (k16) {
           if (rotate_pairs16<kDtype, false>(a[u], cs, chunks, oa[u]))
@@ -374,17 +409,31 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
           rotate_f32(a[u], b[u], cs, chunks, oa[u], ob[u]);
         }
       } else {
-        // partner chunk from the lane kG away; negated when this chunk is in the first half
-        const uint32_t neg = first[u] ? (k16 ? 0x80008000u : 0x80000000u) : 0u;
-        u32x4 par;
+        // The lane with the first-half chunk rotates the pairs of dwords 0-1
+        // of both chunks, its partner those of dwords 2-3: each sends the
+        // dwords of its own chunk that the other needs, rotates, and sends the
+        // other's outputs back, so every element is unpacked once and every
+        // table entry read once for both elements of its pair.  The partner
+        // reads the table copy with the sine negated, which turns the pair
+        // rotation (own, received) into (second element's output, first
+        // element's output): the paired form's float64 operations, bit for bit.
+        uint32_t m[2], g[2], om[2], op[2];
 #pragma unroll
-        for (int d = 0; d < 4; ++d) par[d] = partner_dword<kG>(a[u][d]) ^ neg;
-        if constexpr (k16) {
-          if (rotate_unit16<kDtype, false>(a[u], par, cs, chunks, oa[u]))
-            rotate_unit16<kDtype, true>(a[u], par, cs, chunks, oa[u]);
-        } else {
-          rotate_unit_f32(a[u], par, cs, chunks, oa[u]);
+        for (int d = 0; d < 2; ++d) {
+          m[d] = lane_pick(keep, a[u][d], a[u][d + 2]);
+          g[d] = partner_dword<kG>(lane_pick(keep, a[u][d + 2], a[u][d]));
         }
+        if constexpr (k16) {
+          if (rotate_half16<kDtype, false>(m, g, cs, chunks, om, op))
+            rotate_half16<kDtype, true>(m, g, cs, chunks, om, op);
+        } else {
+          rotate_half_f32(m, g, cs, chunks, om, op);
+        }
+        uint32_t back[2];
+#pragma unroll
+        for (int d = 0; d < 2; ++d) back[d] = partner_dword<kG>(op[d]);
+        oa[u] = u32x4{lane_pick(keep, om[0], back[0]), lane_pick(keep, om[1], back[1]),
+                      lane_pick(keep, back[0], om[0]), lane_pick(keep, back[1], om[1])};
       }
     }
 #pragma unroll
@@ -541,7 +590,8 @@ int prepare_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, i
 
   // LDS: the table of the tokens one tile touches; for pair tiles, padded so
   // that at most the measured best number of workgroups share a compute unit
-  size_t lds = static_cast<size_t>(span * half) * sizeof(double2);
+  // (unit tiles: two copies, the second with the sine negated, 16-entry aligned plus 4)
+  size_t lds = static_cast<size_t>(unit_g ? 2 * span * half + 20 : span * half) * sizeof(double2);
   if (!chunk_tasks) {
     const int64_t cap = tasks_per_tok >= kWideTasksPerToken ? kPairCapWide : kPairCapNarrow;
     const size_t pad = static_cast<size_t>(kLdsPerCu / (cap + 1) + 1024 - kMaxTileTokens * sizeof(int32_t));
