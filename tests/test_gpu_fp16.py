@@ -59,6 +59,8 @@ SHAPES = [
     (300, 6, 2, 16, "unit, half row of 1 chunk"),
     (513, 7, 1, 32, "unit, 2 chunks"),
     (400, 14, 2, 64, "unit, 4 chunks"),
+    (301, 5, 1, 64, "unit, 4 chunks, 48 tasks per token: general addresses"),
+    (150, 3, 2, 32, "unit, 2 chunks, 20 tasks per token: general addresses"),
     (257, 5, 3, 128, "pair tasks"),
     (129, 2, 2, 48, "pair tasks, 3 chunks"),
     (300, 5, 5, 80, "pair tasks, 5 chunks"),

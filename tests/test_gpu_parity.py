@@ -132,6 +132,8 @@ SHAPES = [
     (33, 4, 2, 512, "bf16", [0, 33]),
     (130, 128, 16, 128, "bf16", [0, 60, 130]),  # more than one pass of tasks per token
     (513, 7, 1, 32, "bf16", [0, 100, 513]),  # half row of 2 chunks: chunk tasks, partner 2 lanes away
+    (211, 5, 1, 64, "bf16", [4, 90, 90, 200]),  # 4 chunks, 48 tasks per token (general addresses), outside at both ends
+    (77, 2, 3, 16, "bf16", [0, 0, 30, 77]),  # half row of 1 chunk, 10 tasks per token, empty first segment
     (129, 2, 2, 48, "bf16", [0, 64, 129]),  # 3 chunks per half row: chunk-pair tasks
     (300, 5, 3, 32, "fp32", [0, 17, 300]),  # fp32 half row of 4 chunks
     (77, 3, 2, 16, "fp32", [0, 77]),  # fp32 half row of 2 chunks
