@@ -177,22 +177,6 @@ __device__ __forceinline__ double chunk_squares(const u32x4& a) {
   return ss;
 }
 
-// Sums over the L consecutive lanes of a row for kN rows at once (xor
-// butterfly; a + b and b + a are the same float64, so every lane of a row
-// ends with the same bits), so that the lane exchanges of the rows overlap.
-template <int kN, int kL>
-__device__ __forceinline__ void row_sums(double* v, int lane) {
-#pragma unroll 1
-  for (int m = 1; m < kL; m <<= 1) {
-    const int addr = (lane ^ m) << 2;
-    double o[kN];
-#pragma unroll
-    for (int u = 0; u < kN; ++u) o[u] = lane_f64(v[u], addr);
-#pragma unroll
-    for (int u = 0; u < kN; ++u) v[u] += o[u];
-  }
-}
-
 // The float64 value of the lane that DPP control kCtrl selects within the
 // lane's row of 16 (two 32-bit DPP moves: there is no 64-bit DPP form for
 // these controls on gfx950).
@@ -206,41 +190,45 @@ __device__ __forceinline__ double dpp_f64(double v) {
   return __builtin_bit_cast(double, (static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// row_sums with the steps inside a 16-lane DPP row done by DPP moves, which
-// need no trip through the LDS crossbar: lane ^ 1 and lane ^ 2 are quad
-// permutations; once every quad holds one value, the half-row mirror (lane
-// i with 7 - i) pairs quad 0 with quad 1 as lane ^ 4 does, and once every
-// half row holds one value the row mirror (i with 15 - i) pairs the halves
-// as lane ^ 8 does.  The same additions as the xor butterfly, so the same
-// bits.  Steps across rows (kL = 32, 64) stay lane exchanges.
-template <int kN, int kL>
-__device__ __forceinline__ void row_sums_dpp(double* v, int lane) {
+// Sums over the L consecutive lanes of a row for kN rows at once (xor
+// butterfly; a + b and b + a are the same float64, so every lane of a row
+// ends with the same bits), so that the lane exchanges of the rows overlap.
+// The first kDpp steps (at most the four inside a 16-lane DPP row) are DPP
+// moves, which need no trip through the LDS crossbar: lane ^ 1 and lane ^ 2
+// are quad permutations; once every quad holds one value, the half-row
+// mirror (lane i with 7 - i) pairs quad 0 with quad 1 as lane ^ 4 does, and
+// once every half row holds one value the row mirror (i with 15 - i) pairs
+// the halves as lane ^ 8 does.  The same additions as the xor butterfly, so
+// the same bits.  The remaining steps are ds_bpermute lane exchanges.
+template <int kN, int kL, int kDpp>
+__device__ __forceinline__ void row_sums(double* v, int lane) {
   constexpr int kQuadXor1 = 0xB1;       // quad_perm [1, 0, 3, 2]
   constexpr int kQuadXor2 = 0x4E;       // quad_perm [2, 3, 0, 1]
   constexpr int kRowHalfMirror = 0x141;
   constexpr int kRowMirror = 0x140;
-  if constexpr (kL >= 2) {
+  static_assert(kDpp >= 0 && kDpp <= 4, "at most the four steps inside a 16-lane row");
+  if constexpr (kDpp >= 1 && kL >= 2) {
 #pragma unroll
     for (int u = 0; u < kN; ++u) v[u] += dpp_f64<kQuadXor1>(v[u]);
+    __builtin_amdgcn_sched_barrier(0);  // one step at a time, as measured
   }
-  __builtin_amdgcn_sched_barrier(0);  // one step at a time, as measured
-  if constexpr (kL >= 4) {
+  if constexpr (kDpp >= 2 && kL >= 4) {
 #pragma unroll
     for (int u = 0; u < kN; ++u) v[u] += dpp_f64<kQuadXor2>(v[u]);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (kL >= 8) {
+  if constexpr (kDpp >= 3 && kL >= 8) {
 #pragma unroll
     for (int u = 0; u < kN; ++u) v[u] += dpp_f64<kRowHalfMirror>(v[u]);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_barrier(0);
-  if constexpr (kL >= 16) {
+  if constexpr (kDpp >= 4 && kL >= 16) {
 #pragma unroll
     for (int u = 0; u < kN; ++u) v[u] += dpp_f64<kRowMirror>(v[u]);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll 1
-  for (int m = 16; m < kL; m <<= 1) {
+  for (int m = 1 << kDpp; m < kL; m <<= 1) {
     const int addr = (lane ^ m) << 2;
     double o[kN];
 #pragma unroll
@@ -657,7 +645,11 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
     r[u] = chunk_squares<kDtype>(a[u]);
   }
   if constexpr (!kBwd) {
-    row_sums<kTPT, kL>(r, lane);
+    // the two quad steps as DPP moves; the others would raise the register
+    // count past 128 and cost the fourth wave (so would the quad steps on
+    // interleaved 16-bit rows of 4 or 8 lanes: 125 -> 131 VGPRs)
+    constexpr int kFwdDpp = kIl && kDtype != ROPE_QK_FP32 && kL < 16 ? 0 : 2;
+    row_sums<kTPT, kL, kFwdDpp>(r, lane);
 #pragma unroll
     for (int u = 0; u < kTPT; ++u) r[u] = rsqrt_f64(fma(r[u], p.inv_d, p.eps));
 #pragma unroll
@@ -691,15 +683,14 @@ __device__ __forceinline__ void tile_compute(const NormParams& p, const TileGeom
     __builtin_amdgcn_sched_barrier(0);
     // both row sums (of x^2 and of g x; neither needs the other) go through
     // one butterfly, one chain of lane exchanges instead of two; DPP moves
-    // inside a 16-lane row (the forward keeps the LDS exchanges of row_sums:
-    // with these its register count passes 128 and it loses its fourth wave)
+    // for every step inside a 16-lane row
     double sums[2 * kTPT];
 #pragma unroll
     for (int u = 0; u < kTPT; ++u) {
       sums[u] = r[u];
       sums[kTPT + u] = gx[u];
     }
-    row_sums_dpp<2 * kTPT, kL>(sums, lane);
+    row_sums<2 * kTPT, kL, 4>(sums, lane);
 #pragma unroll
     for (int u = 0; u < kTPT; ++u) {
       r[u] = rsqrt_f64(fma(sums[u], p.inv_d, p.eps));
