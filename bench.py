@@ -25,9 +25,12 @@ Prints ONE JSON line on stdout (progress goes to stderr) with:
                when they were taken on the current kernel source, else null
   workloads    per workload: forward and backward us per launch and fraction
                of 8 TB/s, the stream ceiling of the same traffic, traffic
+  norm         the fused per-head RMSNorm + rotation on --norm-table's
+               workloads: forward and backward us per call and fraction
   cpu_baseline the fp64 numpy oracle on a bounded sample of the headline
                workload, on the host cores (threads used, host cores, CPU)
-  parity       a fresh batch checked against the oracle in the same run
+  parity       a fresh batch's GPU outputs checked against the oracle in the
+               same run (the oracle's leg: it runs only with cpu_baseline)
 Workloads: 1 tiny fp32, 2 Qwen2.5-0.5B-shaped, 3 Qwen3-8B-shaped,
 4 Qwen3-32B-shaped, 5 Llama-3.1-8B-shaped 524,288-token context (default).
 """
@@ -426,8 +429,8 @@ def run_gpu(args):
     del sets
     torch.cuda.empty_cache()
 
-    # parity of a fresh batch in the same run
-    parity = check_parity(w, cu, dev)
+    # a fresh batch's outputs for the oracle leg's parity check, in the same run
+    sample = parity_sample(w, cu, dev)
     torch.cuda.empty_cache()
 
     launch_ms = region_ms / (2 * args.steps)  # HIP events around the K steps, on the launch stream
@@ -453,18 +456,22 @@ def run_gpu(args):
         "traffic": row["traffic"],
         "fwd_us": fwd_us,
         "bwd_us": bwd_us,
-        "parity": parity,
+        "parity_sample": sample,
         "resident_batches": nsets,
         "device": torch.cuda.get_device_name(dev),
         "row": row,
     }
 
 
-def check_parity(w, cu, dev):
+def parity_sample(w, cu, dev):
+    """A fresh batch of the workload through rope_qk_fwd (q, k) and
+    rope_qk_bwd (dq, dk): the inputs and outputs of every token (workloads of
+    up to 4e7 elements) or of sampled tokens (the first, the last, every
+    sequence start and 512 drawn at random), copied to the host.  The oracle
+    leg checks them."""
     import numpy as np
     import torch
 
-    import oracle
     import packed_varlen_rotary_amd as P
     import workloads as W
 
@@ -479,18 +486,32 @@ def check_parity(w, cu, dev):
     P.rope_qk_fwd(t["q"], t["k"], cu, w.theta)
     P.rope_qk_bwd(t["dq"], t["dk"], cu, w.theta)
     torch.cuda.synchronize()
+    out = {}
+    for n in t:
+        o = t[n].index_select(0, idx_d).cpu()
+        out[n] = o.numpy().astype(np.float64) if w.dtype == "fp32" else o.view(torch.int16).numpy().view(np.uint16)
+    return {"idx": idx, "x": x, "out": out}
+
+
+def oracle_parity(w, sample):
+    """The oracle's outputs for the sampled tokens against the GPU's: bf16 as
+    ulp distance on the bf16 grid (with the bit-exact fraction), fp32 as
+    the largest absolute difference."""
+    import numpy as np
+
+    import oracle
+
+    idx = sample["idx"]
     pos = oracle.segment_positions(w.cu_seqlens, w.T)[idx]
     worst = {"max_ulp": 0, "max_abs": 0.0, "exact_fraction": 1.0, "tokens_checked": int(len(idx))}
     exact_n, total_n = 0, 0
     for n, d in (("q", 1), ("k", 1), ("dq", -1), ("dk", -1)):
-        ref = oracle.rotate(x[n], pos, w.theta, d)
-        out = t[n].index_select(0, idx_d)
+        ref = oracle.rotate(sample["x"][n], pos, w.theta, d)
+        got = sample["out"][n]
         if w.dtype == "fp32":
-            worst["max_abs"] = max(worst["max_abs"], float(np.abs(out.cpu().numpy().astype(np.float64) - ref).max()))
+            worst["max_abs"] = max(worst["max_abs"], float(np.abs(got - ref).max()))
         else:
-            want = oracle.bf16_bits(oracle.bf16_rne(ref))
-            got = out.cpu().view(torch.int16).numpy().view(np.uint16)
-            dist = oracle.ulp_distance_bf16(got, want)
+            dist = oracle.ulp_distance_bf16(got, oracle.bf16_bits(oracle.bf16_rne(ref)))
             worst["max_ulp"] = max(worst["max_ulp"], int(dist.max()))
             exact_n += int((dist == 0).sum())
             total_n += dist.size
@@ -548,22 +569,20 @@ def run_copy_ceiling(args):
                       "traffic_bytes": w.bytes_per_pass, "us_per_copy": us, "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS}))
 
 
-def run_norm(args):
+def measure_norm(cfg: int, steps: int, warmup: int, graph: bool) -> dict:
     """The fused per-head RMSNorm + rotation (rope_qk_norm_fwd out of place,
     rope_qk_norm_bwd into a separate dx) on a workload's shapes: each pass
-    timed on its own as a graph of K calls over resident sets of >= 1 GiB
-    (one by one with --no-graph), HIP events around the replays after 0.1 s
-    of warm-up.  Algorithmic bytes: forward read x + write
-    y, backward read x and dy + write dx (the weight-gradient workspace is
-    extra traffic, reported separately)."""
+    timed on its own as a graph of `steps` calls over resident sets of
+    >= 1 GiB (one by one without a graph), HIP events around the replays
+    after 0.1 s of warm-up.  Algorithmic bytes: forward read x + write y,
+    backward read x and dy + write dx (the weight-gradient workspace is extra
+    traffic, reported separately)."""
     import torch
 
     import packed_varlen_rotary_amd as P
     import workloads as W
 
-    if not torch.cuda.is_available():
-        raise SystemExit("bench.py needs a GPU")
-    w = W.make_workload(args.workload)
+    w = W.make_workload(cfg)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     cu = torch.as_tensor(w.cu_seqlens, device=dev)
@@ -597,14 +616,26 @@ def run_norm(args):
         P.rope_qk_norm_bwd(b["dq"], b["dk"], b["q"], b["k"], wq, wk, eps, cu, w.theta, b["xq"], b["xk"],
                            dwq, dwk, ws)
 
-    res = {}
+    res = {"workload": w.name, "io_dtype": w.dtype, "resident_sets": nsets, "workspace_bytes": ws_bytes,
+           "calls_timed": steps}
     for name, fn, nbytes in (("fwd", fwd, 2 * qk_bytes), ("bwd", bwd, 3 * qk_bytes)):
-        us = timed_us(fn, args.steps, args.graph, warmup=args.warmup)
+        us = timed_us(fn, steps, graph, warmup=warmup)
         gbs = nbytes / (us * 1e-6) / 1e9
         res[name] = {"us_per_call": us, "algorithmic_bytes": nbytes, "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS}
         log(f"[bench] norm {name}: {us:.2f} us per call, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak)")
-    print(json.dumps({"metric": "fused per-head QK-RMSNorm + RoPE, achieved HBM GB/s per pass", "workload": w.name,
-                      "io_dtype": w.dtype, "resident_sets": nsets, "workspace_bytes": ws_bytes, "steps": args.steps,
+    del sets, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def run_norm(args):
+    """--norm: measure_norm on --workload, as one JSON line."""
+    import torch
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    res = measure_norm(args.workload, args.steps, args.warmup, args.graph)
+    print(json.dumps({"metric": "fused per-head QK-RMSNorm + RoPE, achieved HBM GB/s per pass", "steps": args.steps,
                       "peak": HBM_PEAK_GBS, **res}))
 
 
@@ -853,6 +884,9 @@ def main():
                     help="the headline workload (default 5: the 524,288-token Llama-3.1-8B-shaped context)")
     ap.add_argument("--table", default="2,3,4",
                     help="other workloads measured in the same run (comma-separated; empty: none)")
+    ap.add_argument("--norm-table", default="3",
+                    help="workloads on which the fused RMSNorm + rotation (forward and backward) is also timed in "
+                         "the same run (comma-separated; empty: none)")
     ap.add_argument("--no-ceiling", dest="ceiling", action="store_false",
                     help="skip the plain-stream ceiling beside each workload")
     ap.add_argument("--no-split", dest="split", action="store_false",
@@ -917,15 +951,22 @@ def main():
 
     w, r = run_gpu(args)
     log(f"[bench] gpu done: {r['ms_per_step']:.4f} ms/step, mean launch {r['launch_ms'] * 1e3:.2f} us, "
-        f"{r['gbs']:.0f} GB/s, parity {r['parity']}")
+        f"{r['gbs']:.0f} GB/s")
     import torch
 
     rows = [r["row"]]
     for cfg in [int(c) for c in args.table.split(",") if c.strip()]:
         if cfg != args.workload:
             rows.append(measure_workload(cfg, torch.device("cuda", 0), args.steps, args.graph, args.ceiling))
+    norm_rows = [measure_norm(int(c), max(args.steps, 20), args.warmup, args.graph)
+                 for c in args.norm_table.split(",") if c.strip()]
+    # the oracle's leg: its outputs against the GPU's on the fresh batch
+    # (parity), and its own speed on the host cores (cpu_baseline)
     cpu = None
+    parity = {"skipped": "--no-cpu-baseline: the oracle leg did not run"}
     if args.workload and not args.no_cpu_baseline:
+        parity = oracle_parity(w, r["parity_sample"])
+        log(f"[bench] parity {parity}")
         cpu = cpu_baseline(w, args.cpu_seconds)
         log(f"[bench] cpu oracle: {cpu['value']:.0f} tokens/s on {cpu['cores']} threads")
 
@@ -970,7 +1011,8 @@ def main():
             "launch": "hip graph of the K steps" if args.graph else "stream launches",
         },
         "workloads": rows,
-        "parity": r["parity"],
+        "norm": norm_rows,
+        "parity": parity,
         "device": r["device"],
     }
     print(json.dumps(line), flush=True)
