@@ -382,10 +382,12 @@ __device__ __forceinline__ void rope_tile(const RopeParams& p, uint32_t tile, in
     //    sequence are left untouched
     bool st[kTPT];
     u32x4 oa[kTPT], ob[kTPT];
-    // Unit tiles: a lane's chunks all sit at the lane's index modulo 2 kG in
-    // their rows, so its half of every pair (first or second) is fixed; the
-    // second-half lane reads the table copy with the sine negated, from its
-    // pairs' entries on (see the rotation below).
+    // Unit tiles: a tile starts on a row boundary and holds whole rows of
+    // 2 kG tasks (its task count is a multiple of 2 kG), so every chunk a lane
+    // holds sits at position tid mod 2 kG of its row, always in the same half.
+    // A lane in the second half reads the table copy with the sine negated,
+    // starting kPPC / 2 entries further on, at the pairs of dwords 2-3 that it
+    // rotates (see the rotation below).
     const bool fst = kG <= 0 || (tid & kG) == 0;
     const uint32_t keep = fst ? 0xFFFFFFFFu : 0u;  // bit mask selecting the first operand of lane_pick
     const double2* tab = kG > 0 && !fst ? s_cs + alt + (kPPC / 2) * kG : s_cs;
