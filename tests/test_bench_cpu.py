@@ -54,3 +54,35 @@ def test_more_than_one_gpu_is_refused_before_any_gpu_work():
     assert out.returncode == 2
     assert out.stdout == ""
     assert "one GPU" in out.stderr
+
+
+def _oracle_sample(w, idx):
+    """A parity sample as the GPU run would hand it over, with the oracle's
+    own outputs in place of the GPU's (inputs: the workload's seeded q, k and
+    fresh gradients at the sampled tokens)."""
+    rng = np.random.default_rng(5)
+    pos = oracle.segment_positions(w.cu_seqlens, w.T)[idx]
+    x, out = {}, {}
+    for n, h, d in (("q", w.Hq, 1), ("k", w.Hkv, 1), ("dq", w.Hq, -1), ("dk", w.Hkv, -1)):
+        xi = oracle.bf16_rne(rng.standard_normal((len(idx), h, w.D)))
+        x[n] = xi
+        out[n] = oracle.bf16_bits(oracle.bf16_rne(oracle.rotate(xi, pos, w.theta, d)))
+    return {"idx": idx, "x": x, "out": out}
+
+
+def test_oracle_parity_counts_and_bounds_ulp_differences():
+    w = W.make_workload(2)
+    idx = np.array([0, 1, 7, 500, w.T - 1])
+    s = _oracle_sample(w, idx)
+    p = bench.oracle_parity(w, s)
+    assert p == {"max_ulp": 0, "max_abs": 0.0, "exact_fraction": 1.0, "tokens_checked": 5, "ok": True}
+    # one element one bf16 ulp off (next bit pattern away from zero): still within
+    # the bound, and counted as not bit-exact
+    s["out"]["k"][2, 1, 3] += 1
+    p = bench.oracle_parity(w, s)
+    n = sum(o.size for o in s["out"].values())
+    assert p["max_ulp"] == 1 and p["ok"] is True and abs(p["exact_fraction"] - (n - 1) / n) < 1e-15
+    # two ulp off: the check fails
+    s["out"]["dq"][4, 0, 0] += 2
+    p = bench.oracle_parity(w, s)
+    assert p["max_ulp"] == 2 and p["ok"] is False
