@@ -91,6 +91,8 @@ __device__ __forceinline__ constexpr int elem_off(int j) {
 constexpr int kBwdWaves16 = 3;
 constexpr int64_t kBwdGroups16 = 4 * 256 * kBwdWaves16;
 constexpr int64_t kBwdGroups32 = 4 * 256 * 4;
+constexpr int64_t kBwdTilesPerRun = 8;   // fewer workgroups than the above when runs would be shorter
+constexpr int64_t kBwdMinGroups = 768;   // ... but at least 3 per compute unit
 
 // One of the two tensors (q, k) of a call.
 struct NormTensor {
@@ -1018,7 +1020,15 @@ int norm_geometry(int64_t T, int64_t Hq, int64_t Hkv, int64_t D, int dtype, bool
   g->table_bytes = g->span * per_token;
   const int64_t total = g->ntiles[0] + g->ntiles[1];
   if (total > INT32_MAX) return ROPE_QK_ERR_SHAPE;
-  const int64_t groups = dtype == ROPE_QK_FP32 ? kBwdGroups32 : kBwdGroups16;
+  // runs of at least ~8 tiles (but no fewer than 768 workgroups, three per
+  // compute unit): with shorter runs each workgroup's own work (weights into
+  // LDS, its weight-gradient sums, the reduction's share of them) outweighs
+  // its tiles (the Qwen2.5-0.5B-shaped backward took 47.7 us with 3072
+  // workgroups of under 3 tiles each, 35.3 us with 1024 of 8)
+  const int64_t most = dtype == ROPE_QK_FP32 ? kBwdGroups32 : kBwdGroups16;
+  int64_t groups = total / kBwdTilesPerRun;
+  if (groups < kBwdMinGroups) groups = kBwdMinGroups;
+  if (groups > most) groups = most;
   g->groups = total < groups ? total : groups;
   return ROPE_QK_OK;
 }

@@ -263,7 +263,7 @@ def test_norm_many_short_sequences(shape):
 
 def test_norm_bwd_long_runs_of_tiles():
     """Enough tiles (12,667) that each backward workgroup takes a run of about
-    four, over thousands of sequences of 0 to 7 tokens: the cursor into
+    eight (1,583 workgroups), over thousands of sequences of 0 to 7 tokens: the cursor into
     cu_seqlens steps across many boundaries inside a run and from tile to
     tile, and one run crosses from q's tiles to k's.  dx bit-exact, dw to the
     oracle's sums."""
