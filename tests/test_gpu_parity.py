@@ -156,6 +156,40 @@ def test_shapes(shape, direction):
     check_against(k, oracle.rope(xk, cu, 1e4, direction), "k")
 
 
+
+def _random_chunk_task_cases(n=24, seed=2026):
+    """Seeded random shapes whose half rows are 1, 2 or 4 chunks (the chunk
+    tasks, where the two lanes of a row's chunk pair split its element
+    pairs): every storage type, 1-20 q heads and 0-5 k heads (token task
+    counts that divide 256 and that do not), 1-699 tokens, and packings with
+    empty segments and tokens outside every sequence at either end."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dt = ("bf16", "fp16", "fp32")[i % 3]
+        D = int(rng.choice([8, 16, 32] if dt == "fp32" else [16, 32, 64]))
+        Hq, Hkv, T = int(rng.integers(1, 21)), int(rng.integers(0, 6)), int(rng.integers(1, 700))
+        lo = int(rng.integers(0, min(T, 3) + 1))
+        hi = T - int(rng.integers(0, min(T - lo, 3) + 1))
+        cu = [lo] + sorted(int(c) for c in rng.integers(lo, hi + 1, size=int(rng.integers(1, 12))))
+        cases.append((T, Hq, Hkv, D, dt, cu, float(rng.choice([1e4, 1e6]))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_chunk_task_cases(), ids=lambda c: f"T{c[0]}_H{c[1]}x{c[2]}_D{c[3]}_{c[4]}")
+@pytest.mark.parametrize("direction", [1, -1])
+def test_chunk_tasks_random_shapes(case, direction):
+    T, Hq, Hkv, D, dt, cu, theta = case
+    q = W.randn((T, Hq, D), dt, seed=T * 13 + Hq, device=DEV)
+    k = W.randn((T, Hkv, D), dt, seed=T * 17 + Hkv + 1, device=DEV)
+    xq, xk = f64(q), f64(k)
+    run(direction, q, k, cu, theta)
+    torch.cuda.synchronize()
+    for name, out, x in (("q", q, xq), ("k", k, xk)):
+        st = check_against(out, oracle.rope(x, cu, theta, direction), name)
+        if dt != "fp32":
+            assert st["exact_fraction"] == 1.0, (name, st)
+
 def test_tokens_outside_sequences_untouched():
     T, cu = 256, [5, 100, 100, 200]
     q = W.randn((T, 4, 64), "bf16", seed=1, device=DEV)
