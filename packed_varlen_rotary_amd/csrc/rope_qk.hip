@@ -27,7 +27,7 @@
 //    chunk's dwords, rotates its half of the pairs whole and sends the
 //    other's outputs back, so each element is unpacked once.
 //  * A workgroup owns one tile of consecutive tasks (256 lanes x 2 pairs or
-//    x 4-8 chunks), which may begin and end inside a token, so every tile but
+//    x 1-8 chunks), which may begin and end inside a token, so every tile but
 //    the last is full whatever the head count.  The grid is two-dimensional
 //    rather than a grid-stride loop: a loop's second copy of the body would
 //    set the register count (and so the occupancy) of every launch.
@@ -56,8 +56,10 @@ namespace {
 constexpr uint32_t kMaxTasksPerToken = 65535;
 constexpr int kPairTasks = 2;                         // chunk pairs per lane (pair tiles)
 constexpr int kInterleaved = -1;                      // tile mode of interleaved pairing
-constexpr int kUnitTasks = 8;                         // chunks per lane (bf16 unit tiles; interleaved short rows)
-constexpr int kLongRowTasks = 4;                      // chunks per lane (fp32 unit tiles; interleaved long rows)
+constexpr int kUnitTasks = 8;      // chunks per lane: 16-bit chunk tasks in small launches, fp32 interleaved short rows
+constexpr int kLongRowTasks = 4;   // chunks per lane: 16-bit chunk tasks in larger launches, fp32 unit tiles, interleaved long rows
+constexpr int kPartRowTasks = 1;   // chunks per lane: larger 16-bit launches of rows rotating under a line of a longer head
+constexpr int64_t kSmallLaunchTasks = int64_t(1) << 21;  // chunk-task launches of at most this many tasks are small
 constexpr int64_t kShortRowChunks = 8;                // interleaved rows of up to this many chunks are short
 
 // Resident workgroups per compute unit for pair tiles, measured on MI355X
@@ -542,15 +544,32 @@ int prepare_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, i
   // task, partner by lane exchange); interleaved: one chunk of whole pairs per task
   const int unit_g = !interleaved && (chunks == 1 || chunks == 2 || chunks == 4) ? static_cast<int>(chunks) : 0;
   const bool chunk_tasks = unit_g != 0 || interleaved;
-  // chunks per lane: 8 amortises the per-tile work best for 16-bit unit tiles
-  // (5% faster than 4 at D = 64) and for interleaved rows of up to 8 chunks;
-  // longer interleaved rows (D = 128 bf16) measured 7% faster with 4 (register
-  // count 128 -> 90, occupancy 4 -> 5), and fp32 unit tiles would spill at 8
-  const int64_t lane_tasks = !chunk_tasks ? kPairTasks
-                             : interleaved ? (chunks > kShortRowChunks ? kLongRowTasks : kUnitTasks)
-                             : (dtype != ROPE_QK_FP32 ? kUnitTasks : kLongRowTasks);
   const int64_t tasks_per_tok = (Hq + Hkv) * (unit_g ? 2 * chunks : chunks);
   if (tasks_per_tok > kMaxTasksPerToken) return ROPE_QK_ERR_SHAPE;
+  // Chunks per lane, measured on MI355X (bf16 and fp16, HIP graphs of
+  // forward launches over resident batches):
+  //  - 16-bit launches of up to 2^21 tasks (64 MiB of traffic, e.g. 16 heads
+  //    of D = 64 over 16,384 tokens, two tiles per compute unit): 8, which
+  //    amortises each tile's work best; 2 and 4 are 8-15% slower;
+  //  - larger 16-bit launches (0.13-1 GB at D = 64): 4, 2-7% faster than 8;
+  //    rotate_half rows that rotate less than one 128-byte line of a longer
+  //    head (rotary_dim < D with r / 2 elements under 64 bytes): 1, 14-26%
+  //    faster than 8 from 2^21 tasks on (the lines' unrotated rest is fetched
+  //    too, so these launches count as large from half the task count);
+  //  - interleaved rows of more than 8 chunks (D = 128 bf16): 4, 7% faster
+  //    than 8 (register count 128 -> 90, occupancy 4 -> 5);
+  //  - fp32: 4 for unit tiles (8 would spill), 8 for short interleaved rows.
+  const bool part_row = unit_g != 0 && unit_g < 4 && r < D;
+  const bool small_launch = T * tasks_per_tok <= (part_row ? kSmallLaunchTasks / 2 : kSmallLaunchTasks);
+  int64_t lane_tasks = kPairTasks;
+  if (chunk_tasks) {
+    if (interleaved)
+      lane_tasks = chunks > kShortRowChunks || (dtype != ROPE_QK_FP32 && !small_launch) ? kLongRowTasks : kUnitTasks;
+    else if (dtype == ROPE_QK_FP32)
+      lane_tasks = kLongRowTasks;
+    else
+      lane_tasks = small_launch ? kUnitTasks : part_row ? kPartRowTasks : kLongRowTasks;
+  }
 
   // a tile touches at most cap_tokens tokens, so its table and positions fit in LDS
   int64_t cap_tokens = kMaxTableBytes / (half * 16);
@@ -605,17 +624,23 @@ int prepare_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, i
   L->span = span;
 
 #define ROPE_FN(DT, G, TPT) reinterpret_cast<const void*>(&rope_qk_kernel<DT, G, TPT>)
-#define ROPE_PICK(DT, UNIT)                                                                    \
-  (interleaved   ? (lane_tasks == kUnitTasks ? ROPE_FN(DT, kInterleaved, kUnitTasks)           \
-                                             : ROPE_FN(DT, kInterleaved, kLongRowTasks))        \
-   : unit_g == 1 ? ROPE_FN(DT, 1, UNIT)                                                         \
-   : unit_g == 2 ? ROPE_FN(DT, 2, UNIT)                                                         \
-   : unit_g == 4 ? ROPE_FN(DT, 4, UNIT)                                                         \
-                 : ROPE_FN(DT, 0, kPairTasks))
-  L->fn = dtype == ROPE_QK_BF16   ? ROPE_PICK(ROPE_QK_BF16, kUnitTasks)
-          : dtype == ROPE_QK_FP16 ? ROPE_PICK(ROPE_QK_FP16, kUnitTasks)
-                                  : ROPE_PICK(ROPE_QK_FP32, kLongRowTasks);
+#define ROPE_UNIT(DT, TPT) \
+  (unit_g == 1 ? ROPE_FN(DT, 1, TPT) : unit_g == 2 ? ROPE_FN(DT, 2, TPT) : ROPE_FN(DT, 4, TPT))
+#define ROPE_PICK(DT, UNIT)                                                                                      \
+  (interleaved ? (lane_tasks == kUnitTasks ? ROPE_FN(DT, kInterleaved, kUnitTasks)                                \
+                                           : ROPE_FN(DT, kInterleaved, kLongRowTasks))                             \
+   : unit_g == 0 ? ROPE_FN(DT, 0, kPairTasks)                                                                     \
+                 : UNIT)
+#define ROPE_PICK16(DT)                                                                  \
+  ROPE_PICK(DT, (lane_tasks == kUnitTasks       ? ROPE_UNIT(DT, kUnitTasks)              \
+                 : lane_tasks == kLongRowTasks  ? ROPE_UNIT(DT, kLongRowTasks)           \
+                                                : ROPE_UNIT(DT, kPartRowTasks)))
+  L->fn = dtype == ROPE_QK_BF16   ? ROPE_PICK16(ROPE_QK_BF16)
+          : dtype == ROPE_QK_FP16 ? ROPE_PICK16(ROPE_QK_FP16)
+                                  : ROPE_PICK(ROPE_QK_FP32, ROPE_UNIT(ROPE_QK_FP32, kLongRowTasks));
+#undef ROPE_PICK16
 #undef ROPE_PICK
+#undef ROPE_UNIT
 #undef ROPE_FN
   return ROPE_QK_OK;
 }

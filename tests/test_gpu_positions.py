@@ -66,7 +66,8 @@ def check_rows(rows, cu, T, pos_offset, what):
 
 ROTATION_SHAPES = [
     # Hq, Hkv, D, dtype code, options (keyword arguments of make_options)
-    (14, 2, 64, P.ROPE_QK_BF16, {}),              # unit tiles, 8 chunks per lane (the Qwen2.5-0.5B shape)
+    (14, 2, 64, P.ROPE_QK_BF16, {}),              # unit tiles (the Qwen2.5-0.5B shape): 8 chunks per lane, 4 past 2^21 tasks
+    (14, 2, 64, P.ROPE_QK_BF16, {"rotary_dim": 32}),  # rotated rows of half a line: 1 chunk per lane past 2^20 tasks
     (32, 8, 128, P.ROPE_QK_BF16, {}),             # pair tiles, tiles starting inside tokens (Qwen3-8B)
     (64, 8, 128, P.ROPE_QK_BF16, {}),             # pair tiles, 576 tasks per token (Qwen3-32B)
     (144, 16, 128, P.ROPE_QK_BF16, {}),           # a token spans several tiles

@@ -114,6 +114,48 @@ def test_partial_rotary_dim(case, direction):
     check_against(k, oracle.rope(xk, cu, 1e4, direction, **o), "k")
 
 
+LARGE_CHUNK_TASKS = [
+    # T, Hq, Hkv, D, dtype, options: chunk-task launches of more than 2^21
+    # tasks (2^20 for rows rotating under a line of a longer head), which
+    # take fewer chunks per lane than smaller ones
+    (20000, 14, 2, 64, "bf16", {}),                     # 4 chunks per lane
+    (20000, 14, 2, 64, "fp16", {}),
+    (40000, 12, 4, 32, "bf16", {}),                     # half rows of 2 chunks, 4 per lane
+    (20000, 14, 2, 64, "bf16", {"interleaved": True}),  # interleaved rows of 8 chunks, 4 per lane
+    (20000, 14, 2, 64, "bf16", {"rotary_dim": 32}),     # rotated rows of half a line: 1 chunk per lane
+    (20000, 14, 2, 64, "fp16", {"rotary_dim": 32}),
+    (20000, 28, 4, 32, "bf16", {"rotary_dim": 16}),     # half rows of 1 chunk, 1 per lane
+    (20000, 14, 2, 128, "bf16", {"rotary_dim": 64}),    # a whole line of a longer head: 4 per lane
+    (16384, 14, 2, 64, "bf16", {}),                     # exactly 2^21 tasks: still 8 per lane
+    (16385, 14, 2, 64, "bf16", {}),                     # one token more: 4 per lane
+    (16384, 14, 2, 64, "bf16", {"rotary_dim": 32}),     # exactly 2^20 tasks of part rows: 8 per lane
+    (16385, 14, 2, 64, "bf16", {"rotary_dim": 32}),     # one token more: 1 per lane
+]
+
+
+@pytest.mark.parametrize("case", LARGE_CHUNK_TASKS,
+                         ids=lambda c: f"T{c[0]}_H{c[1]}x{c[2]}_D{c[3]}_{c[4]}" + "".join(f"_{o}" for o in c[5]))
+@pytest.mark.parametrize("direction", [1, -1])
+def test_large_chunk_task_launches(case, direction):
+    """Every element of launches large enough for the lane counts of large
+    chunk-task launches, against the oracle: ragged segments, tokens outside
+    at both ends, a ragged last tile; partial rotary dims leave the tail alone."""
+    T, Hq, Hkv, D, dt, opts = case
+    rng = np.random.default_rng(T + Hq + D)
+    lengths = rng.integers(1, 3000, size=T // 500)
+    cu = np.concatenate([[0], np.cumsum(lengths)]) + 5
+    cu = cu[cu <= T - 3]
+    q = W.randn((T, Hq, D), dt, seed=T + 1, device=DEV)
+    k = W.randn((T, Hkv, D), dt, seed=T + 2, device=DEV)
+    q0, k0 = q.clone(), k.clone()
+    sq, sk = check_case_tensors(q, k, cu, 5e5, direction, **opts)
+    if dt == "bf16":
+        assert sq["exact_fraction"] == 1.0 and sk["exact_fraction"] == 1.0
+    r = opts.get("rotary_dim")
+    if r:
+        assert torch.equal(q[:, :, r:], q0[:, :, r:]) and torch.equal(k[:, :, r:], k0[:, :, r:])
+
+
 # ---------------------------------------------------------------------------
 # interleaved pairing
 # ---------------------------------------------------------------------------
