@@ -795,6 +795,7 @@ def run_variants(args):
         ("llama3", dict(llama3=llama3), w.dtype),
         ("freq_fp32", dict(freq_fp32=True), w.dtype),
         ("fp16", {}, "fp16"),
+        ("fp32", {}, "fp32"),
         ("interleaved+llama3+freq_fp32+pos_offset", dict(interleaved=True, llama3=llama3, freq_fp32=True,
                                                          pos_offset=77), w.dtype),
     ]
