@@ -481,6 +481,7 @@ def parity_sample(w, cu, dev):
     else:
         rng = np.random.default_rng(1)
         idx = np.unique(np.concatenate([[0, w.T - 1], w.cu_seqlens[:-1], rng.integers(0, w.T, 512)]))
+        idx = idx[(idx >= 0) & (idx < w.T)]  # a sequence may start at T (empty trailing segments)
     idx_d = torch.as_tensor(idx, device=dev)
     x = {n: t[n].index_select(0, idx_d).float().cpu().numpy().astype(np.float64) for n in t}
     P.rope_qk_fwd(t["q"], t["k"], cu, w.theta)
