@@ -634,7 +634,8 @@ int prepare_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, i
 #define ROPE_PICK16(DT)                                                                  \
   ROPE_PICK(DT, (lane_tasks == kUnitTasks       ? ROPE_UNIT(DT, kUnitTasks)              \
                  : lane_tasks == kLongRowTasks  ? ROPE_UNIT(DT, kLongRowTasks)           \
-                                                : ROPE_UNIT(DT, kPartRowTasks)))
+                 : unit_g == 1                  ? ROPE_FN(DT, 1, kPartRowTasks)          \
+                                                : ROPE_FN(DT, 2, kPartRowTasks)))
   L->fn = dtype == ROPE_QK_BF16   ? ROPE_PICK16(ROPE_QK_BF16)
           : dtype == ROPE_QK_FP16 ? ROPE_PICK16(ROPE_QK_FP16)
                                   : ROPE_PICK(ROPE_QK_FP32, ROPE_UNIT(ROPE_QK_FP32, kLongRowTasks));
