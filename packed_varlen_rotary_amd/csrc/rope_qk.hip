@@ -65,10 +65,14 @@ constexpr int64_t kShortRowChunks = 8;                // interleaved rows of up 
 // Resident workgroups per compute unit for pair tiles, measured on MI355X
 // (bf16, D = 128, 0.5-10 GB per launch): with 256 or more tasks per token
 // (e.g. 40 or 72 heads) 3 resident tiles stream 2-5% faster than 4-6, with
-// fewer (e.g. 16 heads) 4 are best.  Unit tiles run uncapped (5 per CU at
-// their register count); any cap costs them 2-17%.
+// fewer (e.g. 16 heads) 4 are best.  fp16, whose rounding test issues about
+// a quarter more vector instructions, is best at 5 (1-9% faster than 3 on
+// the 40- and 72-head shapes, 2% faster than 4 with 16 heads; 6 is no
+// better).  Unit tiles run uncapped (5 per CU at their register count); any
+// cap costs them 2-17%.
 constexpr int kPairCapWide = 3;
 constexpr int kPairCapNarrow = 4;
+constexpr int kPairCapFp16 = 5;
 constexpr int64_t kWideTasksPerToken = 256;
 
 struct RopeParams {
@@ -614,7 +618,9 @@ int prepare_rope(void* q, void* k, const int32_t* cu, int64_t nseq, int64_t T, i
   // (unit tiles: two copies, the second with the sine negated, 16-entry aligned plus 4)
   size_t lds = static_cast<size_t>(unit_g ? 2 * span * half + 20 : span * half) * sizeof(double2);
   if (!chunk_tasks) {
-    const int64_t cap = tasks_per_tok >= kWideTasksPerToken ? kPairCapWide : kPairCapNarrow;
+    const int64_t cap = dtype == ROPE_QK_FP16                ? kPairCapFp16
+                        : tasks_per_tok >= kWideTasksPerToken ? kPairCapWide
+                                                              : kPairCapNarrow;
     const size_t pad = static_cast<size_t>(kLdsPerCu / (cap + 1) + 1024 - kMaxTileTokens * sizeof(int32_t));
     if (lds < pad) lds = pad;
   }
