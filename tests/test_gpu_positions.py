@@ -96,6 +96,34 @@ def test_rotation_tile_positions(shape):
             check_rows(rows, cu, T, pos_offset, f"rotation {shape} T={T} nseq={cu.size - 1} offset={pos_offset}")
 
 
+LANE_COUNTS = [
+    # T, Hq, Hkv, D, dtype code, options, tasks per token, chunks per lane
+    (16384, 14, 2, 64, P.ROPE_QK_BF16, {}, 128, 8),                     # 2^21 tasks: small
+    (16385, 14, 2, 64, P.ROPE_QK_BF16, {}, 128, 4),
+    (16384, 14, 2, 64, P.ROPE_QK_BF16, {"rotary_dim": 32}, 64, 8),      # 2^20 tasks of part rows: small
+    (16385, 14, 2, 64, P.ROPE_QK_BF16, {"rotary_dim": 32}, 64, 1),
+    (16385, 14, 2, 64, P.ROPE_QK_FP16, {"rotary_dim": 32}, 64, 1),
+    (16384, 14, 2, 64, P.ROPE_QK_BF16, {"interleaved": True}, 128, 8),
+    (16385, 14, 2, 64, P.ROPE_QK_BF16, {"interleaved": True}, 128, 4),
+    (20000, 14, 2, 128, P.ROPE_QK_BF16, {"rotary_dim": 64}, 128, 4),    # one whole line of a longer head
+    (20000, 14, 2, 32, P.ROPE_QK_FP32, {}, 128, 4),                     # fp32 chunk tiles: 4 at any size
+]
+
+
+@pytest.mark.parametrize("case", LANE_COUNTS,
+                         ids=lambda c: f"T{c[0]}_D{c[3]}_dt{c[4]}" + "".join(f"_{k}{v}" for k, v in c[5].items()))
+def test_chunk_task_lane_counts(case):
+    """The tile decomposition of chunk-task calls, as the hook runs it: 256
+    lanes times the chunks per lane that the launch's size and row shape
+    select (8 up to 2^21 tasks, 2^20 for rows rotating under a line of a
+    longer head; 4, or 1 for those rows, beyond)."""
+    T, Hq, Hkv, D, dt, opts, tpt, lanes = case
+    cu = torch.as_tensor(np.array([0, T], dtype=np.int32), device=DEV)
+    rows = P.rope_qk_tile_positions(cu, T, Hq, Hkv, D, dt, P.make_options(**opts))
+    assert rows.shape[0] == -(-T * tpt // (256 * lanes)), (case, rows.shape)
+    check_rows(rows, np.array([0, T], dtype=np.int32), T, 0, f"lane counts {case}")
+
+
 NORM_SHAPES = [
     (32, 8, 128, P.ROPE_QK_BF16),
     (14, 2, 64, P.ROPE_QK_BF16),
